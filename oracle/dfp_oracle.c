@@ -1,0 +1,268 @@
+/*
+ * dfp_oracle.c -- plain fp64 CPU oracle for displaced patch attention and the
+ * per-step guidance / sampler / rel-MAE computation.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may link, load or
+ * call this file.  Only the test suite, the smoke check and the benchmark's
+ * CPU-baseline leg use it.  It shares no code, header, table or helper with
+ * the HIP library: every quantity is recomputed here from the definitions on
+ * the pages, in double precision, with no blocking, fusion or reordering
+ * beyond what the definition states.
+ *
+ * Sources (page title, section):
+ *   [DF]  "终极性能对比：DistriFusion vs 传统推理方案", section
+ *         "DistriFusion的革命性突破": first steps synchronous, later steps
+ *         reuse activations of the previous step.
+ *   [XD]  "xDiT: an Inference Engine for Diffusion Transformers (DiTs) with
+ *         Massive Parallelism", section 三.2 PipeFusion (M non-overlapping
+ *         patches) and 三.3 CFG Parallelism (cond/uncond = a batch of 2).
+ *   [HY]  "Accelerating Diffusion via Hybrid Data-Pipeline Parallelism Based
+ *         on Conditional Guidance Scheduling", section 关键设计 2 (rel-MAE of
+ *         the two noise predictions, an L1 ratio with the unconditional term
+ *         below) and 损失函数/训练策略 (flow matching: swap eps for v).
+ *   [AI]  "AIGC 文生图系统如何优化扩散模型推理速度", section 1 (x_T drawn
+ *         from N(0,1)) and section 3 (DDIM with eta; eta = 0 deterministic).
+ *
+ * Readings taken where the pages are silent (each also listed in the design doc):
+ *   - attention is plain softmax(Q K^T * scale) V with no mask or bias;
+ *   - the CFG combine is g = g_u + w (g_c - g_u)  (not printed on [XD]/[HY]);
+ *   - DDIM's undefined sigma_t in x0_hat is sqrt(1 - abar_t);
+ *   - "scaled linear" betas are linear in sqrt(beta);
+ *   - the flow sampler is plain Euler on sigma_i = 1 - i/S.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+/* ------------------------------------------------------------------------ */
+/* The persistent K/V buffer after the fresh patch rows have landed.          */
+/* [DF] later steps attend over the previous step's activations everywhere   */
+/* except the local patch, whose activations are this step's.  [XD] 三.2:    */
+/* a patch is one of M non-overlapping token ranges.                          */
+/* buf: [BH][N][d] stale rows (overwritten in place); fresh: [BH][n][d].     */
+/* ------------------------------------------------------------------------ */
+void oracle_effective_kv(double *buf, const double *fresh, int64_t BH, int64_t N,
+                         int64_t d, int64_t row0, int64_t n)
+{
+    for (int64_t bh = 0; bh < BH; ++bh)
+        for (int64_t i = 0; i < n; ++i)
+            for (int64_t c = 0; c < d; ++c)
+                buf[(bh * N + row0 + i) * d + c] = fresh[(bh * n + i) * d + c];
+}
+
+/* ------------------------------------------------------------------------ */
+/* One query row of attention over N_kv keys, two passes, no online          */
+/* rescaling:  s_j = scale * <q, k_j>;  m = max_j s_j;  p_j = exp(s_j - m);  */
+/* l = sum_j p_j;  o = sum_j p_j v_j / l.                                     */
+/* scratch must hold N_kv doubles.                                            */
+/* ------------------------------------------------------------------------ */
+static void attention_row(const double *q, const double *k, const double *v,
+                          int64_t Nkv, int64_t d, double scale, double *o,
+                          double *s)
+{
+    double m = -INFINITY;
+    for (int64_t j = 0; j < Nkv; ++j) {
+        double dot = 0.0;
+        for (int64_t c = 0; c < d; ++c)
+            dot += q[c] * k[j * d + c];
+        s[j] = scale * dot;
+        if (s[j] > m)
+            m = s[j];
+    }
+    double l = 0.0;
+    for (int64_t j = 0; j < Nkv; ++j) {
+        s[j] = exp(s[j] - m);
+        l += s[j];
+    }
+    for (int64_t c = 0; c < d; ++c)
+        o[c] = 0.0;
+    for (int64_t j = 0; j < Nkv; ++j)
+        for (int64_t c = 0; c < d; ++c)
+            o[c] += s[j] * v[j * d + c];
+    for (int64_t c = 0; c < d; ++c)
+        o[c] /= l;
+}
+
+/* Attention for every query row of every (batch, head).
+ * q: [BH][nq][d], k, v: [BH][Nkv][d] (already the effective buffer),
+ * o: [BH][nq][d].  Returns 0, or -1 if scratch could not be allocated. */
+int oracle_attention(const double *q, const double *k, const double *v,
+                     int64_t BH, int64_t nq, int64_t Nkv, int64_t d,
+                     double scale, double *o)
+{
+    int failed = 0;
+#pragma omp parallel
+    {
+        double *s = (double *)malloc(sizeof(double) * (size_t)(Nkv > 0 ? Nkv : 1));
+        if (!s) {
+#pragma omp atomic write
+            failed = 1;
+        } else {
+#pragma omp for collapse(2) schedule(dynamic, 4)
+            for (int64_t bh = 0; bh < BH; ++bh)
+                for (int64_t i = 0; i < nq; ++i)
+                    attention_row(q + (bh * nq + i) * d, k + bh * Nkv * d,
+                                  v + bh * Nkv * d, Nkv, d, scale,
+                                  o + (bh * nq + i) * d, s);
+            free(s);
+        }
+    }
+    return failed ? -1 : 0;
+}
+
+/* Attention for a chosen subset of (bh, row) pairs, for sampled checks at
+ * sizes where every row would take too long.  rows_bh[r], rows_i[r] name the
+ * r-th row; o: [nrows][d]. */
+int oracle_attention_rows(const double *q, const double *k, const double *v,
+                          int64_t BH, int64_t nq, int64_t Nkv, int64_t d,
+                          double scale, const int64_t *rows_bh,
+                          const int64_t *rows_i, int64_t nrows, double *o)
+{
+    int failed = 0;
+    (void)BH;
+#pragma omp parallel
+    {
+        double *s = (double *)malloc(sizeof(double) * (size_t)(Nkv > 0 ? Nkv : 1));
+        if (!s) {
+#pragma omp atomic write
+            failed = 1;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t r = 0; r < nrows; ++r) {
+                int64_t bh = rows_bh[r], i = rows_i[r];
+                attention_row(q + (bh * nq + i) * d, k + bh * Nkv * d,
+                              v + bh * Nkv * d, Nkv, d, scale, o + r * d, s);
+            }
+            free(s);
+        }
+    }
+    return failed ? -1 : 0;
+}
+
+/* The softmax probability matrix itself, for tiny inputs: p: [BH][nq][Nkv]. */
+void oracle_attention_probs(const double *q, const double *k, int64_t BH,
+                            int64_t nq, int64_t Nkv, int64_t d, double scale,
+                            double *p)
+{
+    for (int64_t bh = 0; bh < BH; ++bh)
+        for (int64_t i = 0; i < nq; ++i) {
+            const double *qi = q + (bh * nq + i) * d;
+            double *row = p + (bh * nq + i) * Nkv;
+            double m = -INFINITY;
+            for (int64_t j = 0; j < Nkv; ++j) {
+                double dot = 0.0;
+                for (int64_t c = 0; c < d; ++c)
+                    dot += qi[c] * k[(bh * Nkv + j) * d + c];
+                row[j] = scale * dot;
+                if (row[j] > m)
+                    m = row[j];
+            }
+            double l = 0.0;
+            for (int64_t j = 0; j < Nkv; ++j) {
+                row[j] = exp(row[j] - m);
+                l += row[j];
+            }
+            for (int64_t j = 0; j < Nkv; ++j)
+                row[j] /= l;
+        }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Noise schedule.  [AI] section 3 asks the schedule for alpha_t and the     */
+/* cumulative alpha-bar_t; the workload names a 1000-step "scaled linear"    */
+/* schedule from 0.00085 to 0.012, read as linear in sqrt(beta):             */
+/*   beta_i = (sqrt(b0) + (sqrt(b1) - sqrt(b0)) * i / (T-1))^2               */
+/*   abar_t = prod_{i<=t} (1 - beta_i).                                      */
+/* ------------------------------------------------------------------------ */
+void oracle_scaled_linear_betas(int64_t T, double beta_start, double beta_end,
+                                double *beta)
+{
+    double a = sqrt(beta_start), b = sqrt(beta_end);
+    for (int64_t i = 0; i < T; ++i) {
+        double r = a + (b - a) * (double)i / (double)(T - 1);
+        beta[i] = r * r;
+    }
+}
+
+void oracle_alphas_cumprod(int64_t T, const double *beta, double *abar)
+{
+    double prod = 1.0;
+    for (int64_t t = 0; t < T; ++t) {
+        prod *= (1.0 - beta[t]);
+        abar[t] = prod;
+    }
+}
+
+/* [AI] section 3: the sampled timesteps are linspace(0, T-1, S) rounded to
+ * integers (numpy's round: halves go to the even neighbour), then walked in
+ * reverse.  ts receives the ascending sequence. */
+void oracle_ddim_timesteps(int64_t T, int64_t S, int64_t *ts)
+{
+    for (int64_t i = 0; i < S; ++i) {
+        double x = (S == 1) ? 0.0 : (double)(T - 1) * (double)i / (double)(S - 1);
+        ts[i] = (int64_t)nearbyint(x); /* default rounding mode: ties to even */
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Classifier-free guidance.  [XD] 三.3 and [HY] 关键设计 1: the guided       */
+/* prediction is formed from a conditional and an unconditional pass over   */
+/* the same x_t.  The combine is read as g = g_u + w (g_c - g_u).            */
+/* ------------------------------------------------------------------------ */
+void oracle_cfg_combine(const double *g_c, const double *g_u, int64_t n,
+                        double w, double *g)
+{
+    for (int64_t i = 0; i < n; ++i)
+        g[i] = g_u[i] + w * (g_c[i] - g_u[i]);
+}
+
+/* [AI] section 3, DDIM with eta = 0, in its own two-stage form:
+ *   x0_hat = (x_t - sigma_t * eps) / sqrt(abar_t),  sigma_t = sqrt(1 - abar_t)
+ *   not last:  x_{t-1} = sqrt(abar_prev) x0_hat
+ *                       + sqrt(1 - abar_prev - sigma_eta^2) eps,  sigma_eta = 0
+ *   last:      x_{t-1} = x0_hat                                               */
+void oracle_ddim_step(double *x, const double *eps, int64_t n, double abar_t,
+                      double abar_prev, int last)
+{
+    double sigma_t = sqrt(1.0 - abar_t);
+    double sqrt_abar_t = sqrt(abar_t);
+    double sigma_eta = 0.0;
+    for (int64_t i = 0; i < n; ++i) {
+        double x0_hat = (x[i] - sigma_t * eps[i]) / sqrt_abar_t;
+        if (last)
+            x[i] = x0_hat;
+        else
+            x[i] = sqrt(abar_prev) * x0_hat +
+                   sqrt(1.0 - abar_prev - sigma_eta * sigma_eta) * eps[i];
+    }
+}
+
+/* [HY] 损失函数/训练策略: flow-matching models predict a velocity v in place
+ * of eps.  Integrator (not on the pages): Euler on sigma,
+ *   x <- x + (sigma_next - sigma) * v,  sigma_i = 1 - i/S, i = 0..S. */
+void oracle_flow_sigmas(int64_t S, double *sigma)
+{
+    for (int64_t i = 0; i <= S; ++i)
+        sigma[i] = 1.0 - (double)i / (double)S;
+}
+
+void oracle_euler_step(double *x, const double *v, int64_t n, double sigma,
+                       double sigma_next)
+{
+    for (int64_t i = 0; i < n; ++i)
+        x[i] = x[i] + (sigma_next - sigma) * v[i];
+}
+
+/* [HY] 关键设计 2: the denoising discrepancy is the relative mean absolute
+ * error of the two predictions; with the unconditional prediction as the
+ * reference it is sum |g_c - g_u| / sum |g_u| over one image.  IEEE division
+ * decides the degenerate cases (0/0 = NaN, x/0 = +Inf). */
+double oracle_relmae(const double *g_c, const double *g_u, int64_t n)
+{
+    double num = 0.0, den = 0.0;
+    for (int64_t i = 0; i < n; ++i) {
+        num += fabs(g_c[i] - g_u[i]);
+        den += fabs(g_u[i]);
+    }
+    return num / den;
+}
