@@ -1,0 +1,302 @@
+#!/usr/bin/env python3
+"""Benchmark of one GPU's share of a patch-parallel diffusion step on MI355X.
+
+One timed "step" is the whole hot path once, at the SDXL-1024-shaped workload
+(64x64 level: 4096 tokens, 10 heads x 64, P=4; 32x32 level: 1024 tokens,
+20 heads x 64, P=4; batch 2 = cond/uncond; latent 1x4x128x128, DDIM-50,
+w=7.5):
+  land fresh K/V (64x64 level) -> patch attention (64x64 level)
+  land fresh K/V (32x32 level) -> patch attention (32x32 level)
+  fused CFG + DDIM update + rel-MAE on the latent.
+All inputs are seeded synthetic arrays resident in HBM before timing starts.
+The timed steps replay one HIP graph of the step (falls back to eager
+launches if capture is refused).  Per-kernel durations for the roofline come
+from HIP events around back-to-back launches on the launch stream.
+
+Prints ONE JSON line.  `--gpus N` with N > 1 is refused: this library is the
+single-GPU share of the work.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("patch-attn TFLOP/s (% bf16 MFMA peak); CFG+sampler step GB/s (% HBM peak)")
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="c2", choices=["c2", "c3", "c4", "c5"],
+                    help="c2 (SDXL-1024) is the reported workload; others for exploration")
+    ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kernel-reps", type=int, default=50)
+    return ap.parse_args()
+
+
+class Level:
+    """Device buffers of one attention level, all resident in HBM."""
+
+    def __init__(self, level, dfp, torch, inputs):
+        x = inputs.attention_inputs(level)
+        self.level = level
+        self.p = 1 if level.P > 1 else 0
+        bf = torch.bfloat16
+
+        def up(a):
+            return torch.from_numpy(np.ascontiguousarray(a)).cuda().to(bf).contiguous()
+
+        self.k_buf, self.v_buf = dfp.alloc_kv_buffer(level.B, level.H, level.N_kv, level.d, bf)
+        dfp.kv_scatter(self.k_buf, self.v_buf, up(x.k_stale), up(x.v_stale), 0)
+        kf, vf = x.fresh_rows(self.p)
+        self.k_new, self.v_new = up(kf), up(vf)
+        self.row0 = level.row0(self.p)
+        self.text = None
+        if level.n_text:
+            kt, vt = x.text_rows()
+            self.text = (up(kt), up(vt))
+        self.q = up(x.q_patch(self.p))
+        self.o = torch.empty_like(self.q)
+        self.scale = 1.0 / level.d ** 0.5
+        self.flops = level.flops()
+        self.fresh_bytes = 2 * 2 * self.k_new.numel() * 2   # K and V, read + write
+        if self.text:
+            self.fresh_bytes += 2 * 2 * self.text[0].numel() * 2
+
+    def scatter(self, dfp):
+        dfp.kv_scatter(self.k_buf, self.v_buf, self.k_new, self.v_new, self.row0)
+        if self.text:
+            dfp.kv_scatter(self.k_buf, self.v_buf, self.text[0], self.text[1], 0)
+
+    def attend(self, dfp):
+        dfp.patch_attention(self.o, self.q, self.k_buf, self.v_buf, self.scale)
+
+
+class Sampler:
+    """Latent, per-step prediction pairs and coefficients, all in HBM."""
+
+    def __init__(self, wl, dfp, torch, inputs):
+        st = inputs.sampler_stream(wl)
+        self.wl = wl
+        self.x = torch.from_numpy(st.x_T).cuda()
+        pairs = [st.next_pair() for _ in range(wl.steps)]
+        self.g_c = [torch.from_numpy(a).cuda() for a, _ in pairs]
+        self.g_u = [torch.from_numpy(b).cuda() for _, b in pairs]
+        self.coeffs = []
+        if wl.sampler == "ddim":
+            abar = dfp.scaled_linear_abar(1000, 0.00085, 0.012)
+            ts = dfp.ddim_timesteps(1000, wl.steps)
+            S = wl.steps
+            for i in range(S):
+                a_prev = 1.0 if i == S - 1 else abar[ts[S - 2 - i]]
+                self.coeffs.append(dfp.ddim_coeffs(abar[ts[S - 1 - i]], a_prev))
+        else:
+            for i in range(wl.steps):
+                self.coeffs.append(dfp.euler_coeffs(1 - i / wl.steps, 1 - (i + 1) / wl.steps))
+        batch = wl.latent[0]
+        self.ws = dfp.cfg_workspace(wl.n_latent, batch)
+        self.r = torch.empty((wl.steps, batch), dtype=torch.float32, device="cuda")
+        self.bytes = 16 * self.x.numel()
+
+    def step(self, dfp, i):
+        k = i % self.wl.steps
+        c_x, c_e = self.coeffs[k]
+        dfp.cfg_step(self.x, self.g_c[k], self.g_u[k], self.wl.w, c_x, c_e, self.r[k], self.ws)
+
+
+def time_kernel(torch, fn, reps):
+    """Average duration (us) of `fn`'s launches: HIP events around each of
+    `reps` back-to-back launches on the current stream."""
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+    fn()
+    torch.cuda.synchronize()
+    for s, e in zip(starts, ends):
+        s.record()
+        fn()
+        e.record()
+    torch.cuda.synchronize()
+    us = [s.elapsed_time(e) * 1e3 for s, e in zip(starts, ends)]
+    return float(np.mean(us)), float(np.median(us)), float(np.min(us))
+
+
+def cpu_baseline(wl, inputs):
+    """The fp64 oracle, as it stands, on a bounded sample of the workload:
+    the first attention level's patch-1 attention for a fixed subset of its
+    query rows (all batch x head pairs), scaled to TFLOP/s."""
+    import oracle
+    lv = wl.levels[0]
+    x = inputs.attention_inputs(lv)
+    p = 1 if lv.P > 1 else 0
+    k_eff = oracle.effective_kv(x.k_stale, x.fresh_rows(p)[0], lv.row0(p))
+    v_eff = oracle.effective_kv(x.v_stale, x.fresh_rows(p)[1], lv.row0(p))
+    BH = lv.B * lv.H
+    # grow the row sample until ~10 s of oracle work (bounded at the whole patch)
+    rows = 16
+    while True:
+        bh = np.repeat(np.arange(BH), rows)
+        ri = np.tile(np.arange(rows), BH)
+        t0 = time.perf_counter()
+        oracle.attention_rows(x.q_patch(p), k_eff, v_eff, 1.0 / lv.d ** 0.5, bh, ri)
+        dt = time.perf_counter() - t0
+        if dt >= 10.0 or rows >= lv.n:
+            break
+        rows = min(lv.n, max(rows * 2, int(rows * 10.0 / max(dt, 1e-3))))
+    flops = 4.0 * bh.size * lv.N_kv * lv.d
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{lv.name} patch {p} attention, {rows} query rows x {BH} (batch,head) "
+                      f"pairs x {lv.N_kv} keys in fp64 ({flops / 1e9:.2f} GFLOP, {dt:.1f} s)"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this benchmark measures one GPU's share of the work; "
+                                   "run it with --gpus 1 (multi-GPU runs are not supported)"}))
+        sys.exit(2)
+
+    import torch
+    from patch_attention_cfg_amd import dfp, inputs
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(3)
+    dfp.lib()
+    wl = inputs.WORKLOADS[args.workload]
+    levels = [Level(lv, dfp, torch, inputs) for lv in wl.levels]
+    sampler = Sampler(wl, dfp, torch, inputs)
+    torch.cuda.synchronize()
+
+    def one_step(i):
+        for L in levels:
+            L.scatter(dfp)
+            L.attend(dfp)
+        sampler.step(dfp, i)
+
+    for i in range(args.warmup):
+        one_step(i)
+    torch.cuda.synchronize()
+
+    launch = "eager"
+    graph = None
+    if not args.no_graph:
+        try:
+            s = torch.cuda.Stream()
+            s.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s):
+                one_step(0)
+            torch.cuda.current_stream().wait_stream(s)
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                one_step(0)
+            torch.cuda.synchronize()
+            for _ in range(3):
+                graph.replay()
+            torch.cuda.synchronize()
+            launch = "hip-graph"
+        except Exception as e:  # capture refused: time eager launches instead
+            print(f"graph capture unavailable ({e}); timing eager launches", file=sys.stderr)
+            graph = None
+
+    # ---- timed region: exactly K steps
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record()
+    for i in range(args.steps):
+        if graph is not None:
+            graph.replay()
+        else:
+            one_step(i)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = max(ev0.elapsed_time(ev1), 1e-9) / args.steps
+    attn_flops = sum(L.flops for L in levels)
+
+    # ---- per-kernel durations (HIP events on the launch stream)
+    reps = args.kernel_reps
+    kern = {}
+    for L in levels:
+        mean, med, mn = time_kernel(torch, lambda L=L: L.attend(dfp), reps)
+        kern[f"attn_{L.level.name}"] = {
+            "us_mean": mean, "us_median": med, "us_min": mn,
+            "tflops": L.flops / (mean * 1e-6) / 1e12,
+            "frac_bf16_peak": L.flops / (mean * 1e-6) / 1e12 / PEAK_BF16_TFLOPS,
+            "flop": L.flops}
+        mean, med, mn = time_kernel(torch, lambda L=L: L.scatter(dfp), reps)
+        kern[f"scatter_{L.level.name}"] = {
+            "us_mean": mean, "us_median": med,
+            "gbps": L.fresh_bytes / (mean * 1e-6) / 1e9, "bytes": L.fresh_bytes}
+    ctr = [0]
+
+    def cfg():
+        sampler.step(dfp, ctr[0])
+        ctr[0] += 1
+    mean, med, mn = time_kernel(torch, cfg, reps)
+    kern["cfg_step"] = {"us_mean": mean, "us_median": med, "us_min": mn,
+                        "gbps": sampler.bytes / (mean * 1e-6) / 1e9,
+                        "frac_hbm_peak": sampler.bytes / (mean * 1e-6) / 1e9 / PEAK_HBM_GBPS,
+                        "bytes": sampler.bytes}
+
+    dom = max(levels, key=lambda L: L.flops)
+    dk = kern[f"attn_{dom.level.name}"]
+    roofline = {"bound": "mfma", "achieved": dk["tflops"], "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": dk["tflops"] / PEAK_BF16_TFLOPS, "traffic": None,
+                "kernel": f"attn_fwd_bf16<{dom.level.d}> ({dom.level.name}, "
+                          f"{dom.flops / 1e9:.2f} GFLOP per launch)"}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, inputs)
+
+    out = {
+        "metric": METRIC,
+        "value": attn_flops / (ms_per_step * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": {"c2": "SDXL-1024-shaped", "c3": "SDXL-2048-shaped",
+                         "c4": "SDXL-3840-shaped", "c5": "DiT/flow-shaped"}[wl.name]
+                        + f" ({wl.name}): one patch per attention level + fused CFG step",
+            "attention": [f"{L.level.name}: B{L.level.B} H{L.level.H} n_q{L.level.n} "
+                          f"N_kv{L.level.N_kv} d{L.level.d} bf16" for L in levels],
+            "latent": list(wl.latent), "sampler": f"{wl.sampler}{wl.steps} fp32", "w": wl.w,
+            "launch": launch},
+        "cfg_step_gbps": kern["cfg_step"]["gbps"],
+        "cfg_step_frac_hbm_peak": kern["cfg_step"]["frac_hbm_peak"],
+        "wall_s_timed": wall,
+        "kernels": kern,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,217 @@
+/*
+ * dfp.h -- displaced patch attention and the fused guided sampler step on
+ * AMD Instinct MI355X (gfx950).  C ABI of libdfp.so.
+ *
+ * The library computes one GPU's share of patch-parallel diffusion
+ * inference:
+ *   - the patch's fresh K/V land in a persistent full-image buffer whose
+ *     other rows still hold the previous denoising step's K/V, and the patch's
+ *     queries attend over that whole buffer;
+ *   - once per step, the conditional and unconditional predictions are
+ *     combined (classifier-free guidance), the latent is advanced by one
+ *     DDIM (eta = 0) or flow-matching Euler step, and the rel-MAE between the
+ *     two predictions is reduced.
+ *
+ * Sources (page title, section):
+ *   [DF] "终极性能对比：DistriFusion vs 传统推理方案" -- "DistriFusion的革命性突破":
+ *        early steps exchange activations synchronously; later steps reuse
+ *        the previous step's activations and hide the exchange.
+ *   [XD] "xDiT: an Inference Engine for Diffusion Transformers (DiTs) with
+ *        Massive Parallelism" -- 三.2 PipeFusion (the image is cut into
+ *        non-overlapping patches), 三.3 CFG Parallelism (cond and uncond
+ *        behave as a batch of two; the two results are gathered before the
+ *        scheduler runs).
+ *   [HY] "Accelerating Diffusion via Hybrid Data-Pipeline Parallelism Based
+ *        on Conditional Guidance Scheduling" -- 关键设计 2 (denoising
+ *        discrepancy rel-MAE between the two predictions) and
+ *        损失函数/训练策略 (flow matching uses the velocity v in place of eps).
+ *   [AI] "AIGC 文生图系统如何优化扩散模型推理速度" -- section 3 (DDIM with
+ *        eta; eta = 0 is deterministic) and section 6 (operator fusion to cut
+ *        data movement).
+ *
+ * Conventions shared by every entry point:
+ *   - Pointers are DEVICE pointers unless the parameter says "host".  The
+ *     caller owns every buffer; the library never allocates device memory.
+ *   - Work is enqueued on `stream` and runs asynchronously; results are
+ *     visible after the caller synchronises that stream.
+ *   - Arguments are validated on the host before anything is enqueued; a bad
+ *     argument returns DFP_ERR_INVALID_ARG (or DFP_ERR_UNSUPPORTED for a
+ *     shape/dtype the kernels do not implement) and touches no memory.
+ *   - A launch error reported by the HIP runtime returns DFP_ERR_HIP.
+ *     Faults inside a kernel surface at the caller's next synchronisation.
+ *   - No entry point throws; none keeps state between calls except where a
+ *     workspace is documented to (see dfp_cfg_step).
+ *   - bf16 tensors hold raw bfloat16 bit patterns (uint16_t).
+ *   - Tensors are dense and row-major in the order their shape is written.
+ *   - Calls that share a workspace must not overlap in time.
+ */
+#ifndef DFP_H
+#define DFP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DFP_OK = 0,
+    DFP_ERR_INVALID_ARG = 1,  /* null pointer, negative or inconsistent size */
+    DFP_ERR_UNSUPPORTED = 2,  /* valid request the kernels do not implement  */
+    DFP_ERR_HIP = 3           /* the HIP runtime rejected a launch           */
+} dfp_status;
+
+typedef enum {
+    DFP_F32 = 0,   /* float32                        */
+    DFP_BF16 = 1   /* bfloat16 bit patterns (uint16) */
+} dfp_dtype;
+
+/* Operation ids for dfp_workspace_bytes. */
+typedef enum {
+    DFP_OP_CFG_STEP = 0,
+    DFP_OP_RELMAE = 1,
+    DFP_OP_PATCH_ATTENTION = 2
+} dfp_op;
+
+/* ------------------------------------------------------------------------
+ * Persistent K/V buffer layout
+ *
+ * K buffer:  k_buf  [B][H][N_buf][d]      (one row per token)
+ * V buffer:  v_buf_t[B][H][d][ldv]        (stored TRANSPOSED, one row per
+ *                                          channel; ldv = dfp_v_ld(N_buf, dt))
+ * ldv rounds N_buf up so every channel row starts on a 16-byte boundary;
+ * columns N_buf..ldv-1 are padding that no kernel reads as data.  The
+ * transposed V is what the attention kernel's P.V matrix product consumes
+ * directly, so the transpose is paid once, when a patch lands, instead of in
+ * every attention tile.
+ * ------------------------------------------------------------------------ */
+
+/* Row stride, in elements, of the transposed V buffer: N_buf rounded up to a
+ * multiple of 8 (bf16) or 4 (f32).  Returns 0 for N_buf <= 0 or a bad dtype. */
+int64_t dfp_v_ld(int64_t N_buf, dfp_dtype dt);
+
+/* (a1) Land a patch's fresh K/V in the persistent buffer.
+ * [DF]: after the warm-up steps a device attends over the previous step's
+ * activations everywhere except its own patch; [XD] 三.2: a patch is one of
+ * the image's non-overlapping token ranges, here rows [row0, row0+n).
+ *
+ *   k_buf   [B][H][N_buf][d]  in/out: rows row0..row0+n-1 of every (b,h)
+ *                             are overwritten with k_new; others untouched.
+ *   v_buf_t [B][H][d][ldv]    in/out: columns row0..row0+n-1 of every
+ *                             channel row are overwritten with v_new
+ *                             transposed; others untouched.
+ *   k_new   [B][H][n][d]      this step's keys of the patch.
+ *   v_new   [B][H][n][d]      this step's values of the patch.
+ * Bit-exact copy, no arithmetic.  Either k pair or v pair may be NULL (both
+ * of a pair) to land only the other.  n == 0 is a no-op (pointers may then
+ * be NULL).
+ * d must be a multiple of 8 (bf16) or 4 (f32).
+ * Errors: INVALID_ARG for row0 < 0, row0 + n > N_buf, non-positive B/H/d/N_buf,
+ * negative n, or a half-null pair; UNSUPPORTED for other d or dtype. */
+dfp_status dfp_kv_scatter(void *k_buf, void *v_buf_t, const void *k_new,
+                          const void *v_new, int B, int H, int N_buf, int d,
+                          int row0, int n, dfp_dtype dt, hipStream_t stream);
+
+/* (a2-a4) One patch's attention over the displaced buffer.
+ * [DF] activation reuse: the buffer holds fresh rows for this patch (and
+ * any always-fresh rows such as a DiT's text tokens) and the previous step's
+ * rows elsewhere; the attention itself is plain softmax attention over all
+ * N_kv buffer rows:
+ *   O[b,h,i,:] = sum_j softmax_j(scale * <Q[b,h,i,:], K[b,h,j,:]>) V[b,h,j,:]
+ * with no mask, bias or dropout.
+ *
+ *   o       [B][H][n_q][d]    output, dtype dt (fp32 accumulation inside).
+ *   q       [B][H][n_q][d]    the patch's queries, dtype dt.
+ *   k_buf   [B][H][N_kv][d]   dtype dt.
+ *   v_buf_t [B][H][d][ldv]    dtype dt, ldv = dfp_v_ld(N_kv, dt).
+ *   scale   softmax scale, normally 1/sqrt(d); must be finite and > 0.
+ *   workspace/ws_bytes  optional device scratch (may be NULL/0).  With at
+ *           least dfp_workspace_bytes(DFP_OP_PATCH_ATTENTION, ...) bytes the
+ *           kernel may split the key range across workgroups when the query
+ *           grid alone is too small to fill the GPU; without it it never
+ *           splits.  The result does not depend on the workspace contents.
+ * d must be 64 or 128.  n_q == 0 is a no-op (pointers may then be NULL).
+ * o must not alias the inputs.
+ * Errors: INVALID_ARG for null pointers, non-positive B/H/N_kv, negative n_q,
+ * a bad scale; UNSUPPORTED for other d or dtype. */
+dfp_status dfp_patch_attention(void *o, const void *q, const void *k_buf,
+                               const void *v_buf_t, int B, int H, int n_q,
+                               int N_kv, int d, float scale, dfp_dtype dt,
+                               void *workspace, size_t ws_bytes,
+                               hipStream_t stream);
+
+/* (a5-a7) Fused guidance + sampler update + rel-MAE, one pass over HBM.
+ * [XD] 三.3 / [HY] 关键设计 1: the step consumes a conditional and an
+ * unconditional prediction of the same latent.  Per element (fp32):
+ *   g  = g_u + w * (g_c - g_u)              classifier-free guidance
+ *   x <- c_x * x + c_e * g                  sampler update, in place
+ * and per image b (batch index), before guidance is applied:
+ *   relmae_out[b] = sum |g_c - g_u| / sum |g_u|        ([HY] 关键设计 2)
+ * The affine form covers DDIM eta = 0 ([AI] section 3; see dfp_ddim_coeffs)
+ * and Euler on sigma (see dfp_euler_coeffs).
+ *
+ *   x          [batch][n_per_image] fp32, updated in place.
+ *   g_c, g_u   [batch][n_per_image] fp32.
+ *   relmae_out [batch] fp32 device memory, or NULL to skip the reduction.
+ *   workspace  device scratch of >= dfp_workspace_bytes(DFP_OP_CFG_STEP,
+ *              n_per_image, batch, ...) bytes, required when relmae_out is
+ *              non-NULL.  Its first 256 bytes hold a completion counter that
+ *              must be zero before the first call (e.g. allocate it zeroed);
+ *              every call leaves it zero again.  The rest holds per-workgroup
+ *              partial sums.  The cross-workgroup sum runs in a fixed order
+ *              in double precision, so results are bitwise reproducible.
+ * Degenerate rel-MAE follows IEEE division (0/0 = NaN, x/0 = +Inf).
+ * Errors: INVALID_ARG for null x/g_c/g_u, n_per_image <= 0, batch <= 0,
+ * a missing or short workspace when relmae_out is non-NULL, non-finite
+ * w/c_x/c_e. */
+dfp_status dfp_cfg_step(float *x, const float *g_c, const float *g_u,
+                        int64_t n_per_image, int batch, float w, double c_x,
+                        double c_e, float *relmae_out, void *workspace,
+                        size_t ws_bytes, hipStream_t stream);
+
+/* (a7) rel-MAE alone ([HY] 关键设计 2):
+ *   out[b] = sum |g_c - g_u| / sum |g_u|  over image b's n_per_image values.
+ * Same reduction, workspace rules and errors as dfp_cfg_step. */
+dfp_status dfp_relmae(const float *g_c, const float *g_u, int64_t n_per_image,
+                      int batch, float *out, void *workspace, size_t ws_bytes,
+                      hipStream_t stream);
+
+/* Device scratch, in bytes, that `op` needs for the given sizes.  Arguments
+ * that do not apply to `op` are ignored.  Returns 0 if the op needs none. */
+size_t dfp_workspace_bytes(int op, int64_t n_per_image, int batch, int B, int H,
+                           int n_q, int N_kv, int d);
+
+/* ------------------------------------------------------------------------
+ * Host helpers (no GPU work).  All outputs are HOST pointers.
+ * ------------------------------------------------------------------------ */
+
+/* [AI] section 3 DDIM, eta = 0, folded to x' = c_x x + c_e g:
+ *   c_x = sqrt(abar_prev / abar_t)
+ *   c_e = sqrt(1 - abar_prev) - sqrt(abar_prev) sqrt(1 - abar_t) / sqrt(abar_t)
+ * Pass abar_prev = 1 on the last step (the step that returns the x0 estimate).
+ * INVALID_ARG unless 0 < abar_t <= 1 and 0 < abar_prev <= 1, or a null output. */
+dfp_status dfp_ddim_coeffs(double abar_t, double abar_prev, double *c_x, double *c_e);
+
+/* Euler on sigma: x' = x + (sigma_next - sigma) v, i.e. c_x = 1,
+ * c_e = sigma_next - sigma.  INVALID_ARG for non-finite input or null output. */
+dfp_status dfp_euler_coeffs(double sigma, double sigma_next, double *c_x, double *c_e);
+
+/* The scaled-linear schedule: beta_i = (sqrt(b0) + (sqrt(b1)-sqrt(b0)) i/(T-1))^2,
+ * abar[t] = prod_{i<=t} (1 - beta_i), t = 0..T-1.  abar: host, T doubles. */
+dfp_status dfp_scaled_linear_abar(int T, double beta_start, double beta_end, double *abar);
+
+/* DDIM timesteps: round-half-even of linspace(0, T-1, S), ascending.
+ * ts: host, S ints.  The sampler walks them in reverse ([AI] section 3). */
+dfp_status dfp_ddim_timesteps(int T, int S, int *ts);
+
+/* Static text for a status code. */
+const char *dfp_status_string(dfp_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DFP_H */

@@ -59,6 +59,7 @@ def _load():
         "oracle_flow_sigmas": (None, [i64, D]),
         "oracle_euler_step": (None, [D, D, i64, dbl, dbl]),
         "oracle_relmae": (dbl, [D, D, i64]),
+        "oracle_num_threads": (cint, []),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
@@ -78,6 +79,11 @@ def _pd(a: np.ndarray):
 
 def _pi(a: np.ndarray):
     return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+
+
+def num_threads() -> int:
+    """Threads the oracle's parallel loops use (OpenMP)."""
+    return int(_load().oracle_num_threads())
 
 
 # --------------------------------------------------------------------------

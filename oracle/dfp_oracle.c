@@ -266,3 +266,16 @@ double oracle_relmae(const double *g_c, const double *g_u, int64_t n)
     }
     return num / den;
 }
+
+/* Number of OpenMP threads a parallel region of this library uses. */
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

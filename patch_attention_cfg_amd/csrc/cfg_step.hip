@@ -1,0 +1,223 @@
+// cfg_step.hip -- one fused, bandwidth-bound pass per denoising step:
+// classifier-free guidance, the affine sampler update of the latent, and the
+// rel-MAE reduction between the two predictions.
+//
+// Sources (page title, section):
+//   "xDiT: an Inference Engine for Diffusion Transformers (DiTs) with Massive
+//   Parallelism", 三.3 CFG Parallelism: the conditional and unconditional
+//   predictions are gathered before the scheduler step.
+//   "Accelerating Diffusion via Hybrid Data-Pipeline Parallelism Based on
+//   Conditional Guidance Scheduling", 关键设计 2: rel-MAE of the two noise
+//   predictions, taken as sum|g_c - g_u| / sum|g_u| over one image; and
+//   损失函数/训练策略: flow-matching models use the velocity instead of eps.
+//   "AIGC 文生图系统如何优化扩散模型推理速度", section 3 (DDIM, eta = 0) and
+//   section 6 (operator fusion cuts data movement): guidance, update and
+//   reduction share one read of g_c and g_u, so the step moves 16 bytes per
+//   latent element (x read + write, g_c and g_u read).
+//
+// Reduction: fp32 per thread and per wavefront, fp64 per workgroup; the last
+// workgroup to finish (integer completion counter) sums the per-workgroup
+// partials in a fixed order in fp64 and writes the ratio.  No float atomics,
+// so the result is bitwise reproducible run to run.
+#include <cmath>
+
+#include "dfp_common.h"
+#include "dfp_internal.h"
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kUnroll = 2;            // float4 items per thread per array in flight
+constexpr int kMaxBlocksPerImage = 2048;
+constexpr size_t kCounterBytes = 256;
+
+struct Grid {
+    int blocks_per_image;
+};
+
+inline Grid plan(int64_t n_per_image) {
+    const int64_t items = (n_per_image + 3) / 4;  // float4 items (or scalar quads)
+    int64_t b = (items + kThreads * kUnroll - 1) / (kThreads * kUnroll);
+    if (b < 1) b = 1;
+    if (b > kMaxBlocksPerImage) b = kMaxBlocksPerImage;
+    return Grid{(int)b};
+}
+
+__device__ __forceinline__ void accum(float &num, float &den, float c, float u) {
+    num += fabsf(c - u);
+    den += fabsf(u);
+}
+
+template <bool UPDATE, bool VEC>
+__global__ __launch_bounds__(kThreads) void cfg_step_kernel(
+    float *__restrict__ x, const float *__restrict__ g_c, const float *__restrict__ g_u,
+    int64_t n, float w, float c_x, float c_e, double *__restrict__ partials,
+    unsigned *__restrict__ counter, float *__restrict__ out, int reduce) {
+    const int img = blockIdx.y;
+    const int blk = blockIdx.x;
+    const int nblk = gridDim.x;
+    const int tid = threadIdx.x;
+    const int64_t base = (int64_t)img * n;
+    float num = 0.f, den = 0.f;
+
+    if (VEC) {
+        const int64_t n4 = n >> 2;
+        float4 *x4 = reinterpret_cast<float4 *>(x + base);
+        const float4 *c4 = reinterpret_cast<const float4 *>(g_c + base);
+        const float4 *u4 = reinterpret_cast<const float4 *>(g_u + base);
+        const int64_t step = (int64_t)nblk * kThreads * kUnroll;
+        for (int64_t i0 = (int64_t)blk * kThreads * kUnroll + tid; i0 < n4; i0 += step) {
+            float4 cv[kUnroll], uv[kUnroll], xv[kUnroll];
+#pragma unroll
+            for (int k = 0; k < kUnroll; ++k) {
+                const int64_t i = i0 + (int64_t)k * kThreads;
+                if (i < n4) {
+                    cv[k] = c4[i];
+                    uv[k] = u4[i];
+                    if (UPDATE) xv[k] = x4[i];
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < kUnroll; ++k) {
+                const int64_t i = i0 + (int64_t)k * kThreads;
+                if (i < n4) {
+                    accum(num, den, cv[k].x, uv[k].x);
+                    accum(num, den, cv[k].y, uv[k].y);
+                    accum(num, den, cv[k].z, uv[k].z);
+                    accum(num, den, cv[k].w, uv[k].w);
+                    if (UPDATE) {
+                        float4 r;
+                        r.x = fmaf(c_x, xv[k].x, c_e * fmaf(w, cv[k].x - uv[k].x, uv[k].x));
+                        r.y = fmaf(c_x, xv[k].y, c_e * fmaf(w, cv[k].y - uv[k].y, uv[k].y));
+                        r.z = fmaf(c_x, xv[k].z, c_e * fmaf(w, cv[k].z - uv[k].z, uv[k].z));
+                        r.w = fmaf(c_x, xv[k].w, c_e * fmaf(w, cv[k].w - uv[k].w, uv[k].w));
+                        x4[i] = r;
+                    }
+                }
+            }
+        }
+    } else {
+        float *xs = x + base;
+        const float *cs = g_c + base;
+        const float *us = g_u + base;
+        const int64_t step = (int64_t)nblk * kThreads;
+        for (int64_t i = (int64_t)blk * kThreads + tid; i < n; i += step) {
+            const float c = cs[i], u = us[i];
+            accum(num, den, c, u);
+            if (UPDATE) xs[i] = fmaf(c_x, xs[i], c_e * fmaf(w, c - u, u));
+        }
+    }
+
+    if (!reduce) return;
+
+    // workgroup partial: wave sums (fp32), then the 4 waves in fp64
+    __shared__ float wnum[kThreads / dfp::kWave], wden[kThreads / dfp::kWave];
+    __shared__ int is_last;
+    num = dfp::wave_sum(num);
+    den = dfp::wave_sum(den);
+    const int wave = tid / dfp::kWave, lane = tid % dfp::kWave;
+    if (lane == 0) {
+        wnum[wave] = num;
+        wden[wave] = den;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        double pn = 0.0, pd = 0.0;
+#pragma unroll
+        for (int k = 0; k < kThreads / dfp::kWave; ++k) {
+            pn += (double)wnum[k];
+            pd += (double)wden[k];
+        }
+        double *p = partials + 2 * ((int64_t)img * nblk + blk);
+        __hip_atomic_store(p, pn, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(p + 1, pd, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const unsigned total = (unsigned)nblk * gridDim.y;
+        const unsigned prev =
+            __hip_atomic_fetch_add(counter, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        is_last = (prev == total - 1);
+    }
+    __syncthreads();
+    if (!is_last) return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+
+    // last workgroup: fixed-order fp64 sums of every image's partials
+    __shared__ double snum[kThreads], sden[kThreads];
+    for (int im = 0; im < (int)gridDim.y; ++im) {
+        double a = 0.0, b = 0.0;
+        const double *p = partials + 2 * (int64_t)im * nblk;
+        for (int k = tid; k < nblk; k += kThreads) {
+            a += __hip_atomic_load(p + 2 * k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            b += __hip_atomic_load(p + 2 * k + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        snum[tid] = a;
+        sden[tid] = b;
+        __syncthreads();
+        for (int s = kThreads / 2; s > 0; s >>= 1) {
+            if (tid < s) {
+                snum[tid] += snum[tid + s];
+                sden[tid] += sden[tid + s];
+            }
+            __syncthreads();
+        }
+        if (tid == 0) out[im] = (float)(snum[0] / sden[0]);
+        __syncthreads();
+    }
+    if (tid == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+size_t workspace_need(int64_t n_per_image, int batch) {
+    const Grid g = plan(n_per_image);
+    return kCounterBytes + (size_t)batch * g.blocks_per_image * 2 * sizeof(double);
+}
+
+template <bool UPDATE>
+dfp_status launch(float *x, const float *g_c, const float *g_u, int64_t n, int batch,
+                  float w, float c_x, float c_e, float *out, void *ws, size_t ws_bytes,
+                  hipStream_t stream) {
+    if (!g_c || !g_u || (UPDATE && !x) || n <= 0 || batch <= 0 || batch > 65535)
+        return DFP_ERR_INVALID_ARG;
+    const int reduce = out != nullptr;
+    if (reduce && (!ws || ws_bytes < workspace_need(n, batch) ||
+                   (reinterpret_cast<uintptr_t>(ws) % 256) != 0))
+        return DFP_ERR_INVALID_ARG;
+    const Grid g = plan(n);
+    const bool vec = (n % 4 == 0) && (reinterpret_cast<uintptr_t>(g_c) % 16 == 0) &&
+                     (reinterpret_cast<uintptr_t>(g_u) % 16 == 0) &&
+                     (!UPDATE || reinterpret_cast<uintptr_t>(x) % 16 == 0);
+    unsigned *counter = reduce ? static_cast<unsigned *>(ws) : nullptr;
+    double *partials =
+        reduce ? reinterpret_cast<double *>(static_cast<char *>(ws) + kCounterBytes) : nullptr;
+    dim3 grid((unsigned)g.blocks_per_image, (unsigned)batch);
+    if (vec)
+        hipLaunchKernelGGL((cfg_step_kernel<UPDATE, true>), grid, dim3(kThreads), 0, stream, x,
+                           g_c, g_u, n, w, c_x, c_e, partials, counter, out, reduce);
+    else
+        hipLaunchKernelGGL((cfg_step_kernel<UPDATE, false>), grid, dim3(kThreads), 0, stream, x,
+                           g_c, g_u, n, w, c_x, c_e, partials, counter, out, reduce);
+    return dfp::launch_status();
+}
+
+}  // namespace
+
+size_t dfp_cfg_workspace_bytes(int64_t n_per_image, int batch) {
+    if (n_per_image <= 0 || batch <= 0) return 0;
+    return workspace_need(n_per_image, batch);
+}
+
+extern "C" dfp_status dfp_cfg_step(float *x, const float *g_c, const float *g_u,
+                                   int64_t n_per_image, int batch, float w, double c_x,
+                                   double c_e, float *relmae_out, void *workspace,
+                                   size_t ws_bytes, hipStream_t stream) {
+    if (!std::isfinite(w) || !std::isfinite(c_x) || !std::isfinite(c_e))
+        return DFP_ERR_INVALID_ARG;
+    return launch<true>(x, g_c, g_u, n_per_image, batch, w, (float)c_x, (float)c_e, relmae_out,
+                        workspace, ws_bytes, stream);
+}
+
+extern "C" dfp_status dfp_relmae(const float *g_c, const float *g_u, int64_t n_per_image,
+                                 int batch, float *out, void *workspace, size_t ws_bytes,
+                                 hipStream_t stream) {
+    if (!out) return DFP_ERR_INVALID_ARG;
+    return launch<false>(nullptr, g_c, g_u, n_per_image, batch, 0.f, 0.f, 0.f, out, workspace,
+                         ws_bytes, stream);
+}

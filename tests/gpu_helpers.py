@@ -1,0 +1,95 @@
+"""Shared plumbing for the GPU parity tests: upload seeded host arrays, land a
+displaced buffer through the library's own scatter, read results back.
+Nothing here computes any part of the method."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+from patch_attention_cfg_amd import dfp
+
+
+def torch_mod():
+    import torch
+    return torch
+
+
+def require_gpu():
+    import pytest
+    torch = torch_mod()
+    if not torch.cuda.is_available():
+        pytest.fail("GPU test run without a visible GPU")
+    dfp.lib()  # raises loudly if libdfp.so is missing
+
+
+def announce(msg: str) -> None:
+    print(f"[gpu-case] {msg}", file=sys.stderr, flush=True)
+
+
+def dtype_of(kind: str):
+    torch = torch_mod()
+    return torch.bfloat16 if kind == "bf16" else torch.float32
+
+
+def up(a: np.ndarray, kind: str):
+    """Host float32 (bf16-exact for bf16) -> device tensor of that dtype."""
+    torch = torch_mod()
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+    return t.to(dtype_of(kind)).contiguous()
+
+
+def down(t) -> np.ndarray:
+    return t.float().cpu().numpy()
+
+
+def v_buffer_to_rows(v_buf_t, N: int) -> np.ndarray:
+    """[B,H,d,ldv] device V buffer -> host [B,H,N,d] (layout only)."""
+    return np.ascontiguousarray(np.swapaxes(down(v_buf_t)[..., :N], -1, -2))
+
+
+def land_buffer(level, x, p: int, kind: str):
+    """Device (k_buf, v_buf_t) holding the previous step's K/V everywhere,
+    this step's K/V for patch p and for the text rows -- all landed with
+    dfp_kv_scatter."""
+    torch = torch_mod()
+    B, H, N, d = level.B, level.H, level.N_kv, level.d
+    k_buf, v_buf = dfp.alloc_kv_buffer(B, H, N, d, dtype_of(kind))
+    dfp.kv_scatter(k_buf, v_buf, up(x.k_stale, kind), up(x.v_stale, kind), 0)
+    kf, vf = x.fresh_rows(p)
+    dfp.kv_scatter(k_buf, v_buf, up(kf, kind), up(vf, kind), level.row0(p))
+    if level.n_text:
+        kt, vt = x.text_rows()
+        dfp.kv_scatter(k_buf, v_buf, up(kt, kind), up(vt, kind), 0)
+    torch.cuda.synchronize()
+    return k_buf, v_buf
+
+
+def run_patch(level, x, p: int, kind: str | None = None):
+    kind = kind or level.dtype
+    torch = torch_mod()
+    k_buf, v_buf = land_buffer(level, x, p, kind)
+    q = up(x.q_patch(p), kind)
+    o = torch.empty_like(q)
+    dfp.patch_attention(o, q, k_buf, v_buf, 1.0 / level.d ** 0.5)
+    torch.cuda.synchronize()
+    return down(o)
+
+
+def sample_rows(n: int, BH: int, per_bh: int, seed: int):
+    """(bh, row) pairs: the first and last rows of every 32/128-row tile edge
+    near both ends, plus seeded random rows, for every (batch, head)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    fixed = {0, 1, 31, 32, 127, 128, n - 1, n - 2, n - 33, n - 129}
+    fixed = sorted(r for r in fixed if 0 <= r < n)
+    bhs, rows = [], []
+    for bh in range(BH):
+        extra = rng.choice(n, size=min(per_bh, n), replace=False)
+        rr = sorted(set(fixed) | set(int(v) for v in extra))
+        bhs += [bh] * len(rr)
+        rows += rr
+    return np.array(bhs, dtype=np.int64), np.array(rows, dtype=np.int64)
+
+
+def rel_l2(a: np.ndarray, b: np.ndarray) -> float:
+    return float(np.linalg.norm((a - b).ravel()) / np.linalg.norm(b.ravel()))

@@ -1,0 +1,172 @@
+"""Host-side checks of libdfp.so (no GPU work): the library loads, exports
+every function include/dfp.h declares, validates arguments before launching
+anything, and its host helpers (schedule, timesteps, folded sampler
+coefficients) agree with the oracle."""
+import ctypes
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from patch_attention_cfg_amd import dfp
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _header_functions():
+    text = open(os.path.join(ROOT, "include", "dfp.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dfp_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(dfp.LIB_PATH):
+        from patch_attention_cfg_amd import build
+        build.build_library()
+    return dfp.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = _header_functions()
+    assert len(names) >= 11
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(dfp.SIGNATURES)
+
+
+def test_status_strings(L):
+    for code in (0, 1, 2, 3):
+        assert dfp.status_string(code).startswith("DFP_")
+    assert "unknown" in dfp.status_string(99)
+
+
+def test_v_ld(L):
+    assert dfp.v_ld(4096, dfp.BF16) == 4096
+    assert dfp.v_ld(13, dfp.BF16) == 16
+    assert dfp.v_ld(13, dfp.F32) == 16
+    assert dfp.v_ld(1, dfp.F32) == 4
+    assert dfp.v_ld(0, dfp.BF16) == 0
+    assert dfp.v_ld(10, 7) == 0
+
+
+# ---------------------------------------------------- validation, no launch
+NULL = None
+S0 = ctypes.c_void_p(0)
+FAKE = ctypes.c_void_p(0x100000)   # never dereferenced: validation fails first
+
+
+@pytest.mark.parametrize("args,expect", [
+    # k pair half null
+    ((FAKE, NULL, NULL, NULL, 2, 2, 64, 64, 0, 8, dfp.BF16), dfp.ERR_INVALID_ARG),
+    # row0 + n > N_buf
+    ((FAKE, FAKE, FAKE, FAKE, 2, 2, 64, 64, 60, 8, dfp.BF16), dfp.ERR_INVALID_ARG),
+    ((FAKE, FAKE, FAKE, FAKE, 2, 2, 64, 64, -1, 8, dfp.BF16), dfp.ERR_INVALID_ARG),
+    ((FAKE, FAKE, FAKE, FAKE, 0, 2, 64, 64, 0, 8, dfp.BF16), dfp.ERR_INVALID_ARG),
+    ((FAKE, FAKE, FAKE, FAKE, 2, 2, 64, 64, 0, -1, dfp.BF16), dfp.ERR_INVALID_ARG),
+    # d not a multiple of 16 bytes
+    ((FAKE, FAKE, FAKE, FAKE, 2, 2, 64, 12, 0, 8, dfp.BF16), dfp.ERR_UNSUPPORTED),
+    ((FAKE, FAKE, FAKE, FAKE, 2, 2, 64, 64, 0, 8, 5), dfp.ERR_UNSUPPORTED),
+    # misaligned pointer
+    ((ctypes.c_void_p(0x100002), FAKE, FAKE, FAKE, 2, 2, 64, 64, 0, 8, dfp.BF16),
+     dfp.ERR_INVALID_ARG),
+    # n == 0 is a no-op
+    ((FAKE, FAKE, FAKE, FAKE, 2, 2, 64, 64, 3, 0, dfp.BF16), dfp.OK),
+    ((FAKE, FAKE, NULL, NULL, 2, 2, 64, 64, 64, 0, dfp.BF16), dfp.OK),
+])
+def test_scatter_validation(L, args, expect):
+    assert L.dfp_kv_scatter(*args, S0) == expect
+
+
+@pytest.mark.parametrize("args,expect", [
+    ((NULL, FAKE, FAKE, FAKE, 2, 2, 16, 64, 64, 0.125, dfp.BF16), dfp.ERR_INVALID_ARG),
+    ((FAKE, FAKE, FAKE, NULL, 2, 2, 16, 64, 64, 0.125, dfp.BF16), dfp.ERR_INVALID_ARG),
+    ((FAKE, FAKE, FAKE, FAKE, 2, 2, 16, 0, 64, 0.125, dfp.BF16), dfp.ERR_INVALID_ARG),
+    ((FAKE, FAKE, FAKE, FAKE, 2, 2, -1, 64, 64, 0.125, dfp.BF16), dfp.ERR_INVALID_ARG),
+    ((FAKE, FAKE, FAKE, FAKE, 2, 2, 16, 64, 64, 0.0, dfp.BF16), dfp.ERR_INVALID_ARG),
+    ((FAKE, FAKE, FAKE, FAKE, 2, 2, 16, 64, 64, float("nan"), dfp.BF16), dfp.ERR_INVALID_ARG),
+    ((FAKE, FAKE, FAKE, FAKE, 2, 2, 16, 64, 64, float("inf"), dfp.BF16), dfp.ERR_INVALID_ARG),
+    ((FAKE, FAKE, FAKE, FAKE, 2, 2, 16, 64, 96, 0.125, dfp.BF16), dfp.ERR_UNSUPPORTED),
+    ((FAKE, FAKE, FAKE, FAKE, 2, 2, 16, 64, 64, 0.125, 4), dfp.ERR_UNSUPPORTED),
+    ((FAKE, FAKE, ctypes.c_void_p(0x100008), FAKE, 2, 2, 16, 64, 64, 0.125, dfp.BF16),
+     dfp.ERR_INVALID_ARG),
+    ((FAKE, FAKE, FAKE, FAKE, 2, 2, 0, 64, 64, 0.125, dfp.BF16), dfp.OK),
+    ((NULL, NULL, NULL, NULL, 2, 2, 0, 64, 64, 0.125, dfp.BF16), dfp.OK),
+])
+def test_attention_validation(L, args, expect):
+    assert L.dfp_patch_attention(*args, NULL, 0, S0) == expect
+
+
+def test_cfg_step_validation(L):
+    ws_need = dfp.workspace_bytes(dfp.OP_CFG_STEP, 4096, 1)
+    assert ws_need > 256
+    cases = [
+        ((NULL, FAKE, FAKE, 4096, 1, 7.5, 1.0, -0.5, NULL, NULL, 0), dfp.ERR_INVALID_ARG),
+        ((FAKE, NULL, FAKE, 4096, 1, 7.5, 1.0, -0.5, NULL, NULL, 0), dfp.ERR_INVALID_ARG),
+        ((FAKE, FAKE, FAKE, 0, 1, 7.5, 1.0, -0.5, NULL, NULL, 0), dfp.ERR_INVALID_ARG),
+        ((FAKE, FAKE, FAKE, 4096, 0, 7.5, 1.0, -0.5, NULL, NULL, 0), dfp.ERR_INVALID_ARG),
+        ((FAKE, FAKE, FAKE, 4096, 1, float("nan"), 1.0, -0.5, NULL, NULL, 0),
+         dfp.ERR_INVALID_ARG),
+        ((FAKE, FAKE, FAKE, 4096, 1, 7.5, float("inf"), -0.5, NULL, NULL, 0),
+         dfp.ERR_INVALID_ARG),
+        # reduction requested without (enough) workspace
+        ((FAKE, FAKE, FAKE, 4096, 1, 7.5, 1.0, -0.5, FAKE, NULL, 0), dfp.ERR_INVALID_ARG),
+        ((FAKE, FAKE, FAKE, 4096, 1, 7.5, 1.0, -0.5, FAKE, FAKE, ws_need - 1),
+         dfp.ERR_INVALID_ARG),
+    ]
+    for args, expect in cases:
+        assert L.dfp_cfg_step(*args, S0) == expect, args
+    assert L.dfp_relmae(FAKE, FAKE, 4096, 1, NULL, FAKE, ws_need, S0) == dfp.ERR_INVALID_ARG
+    assert L.dfp_relmae(FAKE, FAKE, 4096, 1, FAKE, NULL, 0, S0) == dfp.ERR_INVALID_ARG
+
+
+def test_workspace_sizes_grow_with_batch(L):
+    a = dfp.workspace_bytes(dfp.OP_CFG_STEP, 921600, 1)
+    b = dfp.workspace_bytes(dfp.OP_CFG_STEP, 921600, 2)
+    assert b > a > 256
+    assert dfp.workspace_bytes(dfp.OP_RELMAE, 921600, 1) == a
+    assert dfp.workspace_bytes(99) == 0
+
+
+# ------------------------------------------------- host helpers vs oracle
+def test_schedule_matches_oracle(L):
+    ours = dfp.scaled_linear_abar(1000, 0.00085, 0.012)
+    ref = oracle.alphas_cumprod(oracle.scaled_linear_betas(1000, 0.00085, 0.012))
+    np.testing.assert_allclose(ours, ref, rtol=1e-14, atol=0)
+
+
+@pytest.mark.parametrize("S", [1, 10, 28, 50, 100, 999])
+def test_timesteps_match_oracle(L, S):
+    np.testing.assert_array_equal(dfp.ddim_timesteps(1000, S), oracle.ddim_timesteps(1000, S))
+
+
+@pytest.mark.parametrize("steps", [10, 50])
+def test_folded_ddim_coefficients_reproduce_two_stage_step(L, steps):
+    # x' = c_x x + c_e g must equal the oracle's x0-estimate form at every step
+    sch = oracle.DDIMSchedule(steps)
+    r = np.random.Generator(np.random.PCG64(steps))
+    x = r.standard_normal(256)
+    g = r.standard_normal(256)
+    for i in range(steps):
+        at, ap, last = sch.step_args(i)
+        cx, ce = dfp.ddim_coeffs(at, ap)
+        want = oracle.ddim_step(x, g, at, ap, last)
+        np.testing.assert_allclose(cx * x + ce * g, want, rtol=1e-12, atol=1e-12)
+
+
+def test_coefficient_edge_cases(L):
+    cx, ce = dfp.ddim_coeffs(0.5, 0.5)
+    assert abs(cx - 1) < 1e-15 and abs(ce) < 1e-15
+    cx, ce = dfp.euler_coeffs(1.0, 27 / 28)
+    assert cx == 1.0 and abs(ce + 1 / 28) < 1e-16
+    with pytest.raises(dfp.DFPError):
+        dfp.ddim_coeffs(0.0, 0.5)
+    with pytest.raises(dfp.DFPError):
+        dfp.ddim_coeffs(0.5, 1.5)
+    with pytest.raises(dfp.DFPError):
+        dfp.euler_coeffs(math.nan, 0.0)
+    with pytest.raises(dfp.DFPError):
+        dfp.scaled_linear_abar(1, 0.1, 0.2)

@@ -1,0 +1,155 @@
+"""GPU parity of dfp_patch_attention against the fp64 oracle.
+
+Bars: fp32 path max-abs <= 1e-4; bf16 path relative L2 <= 1e-2 and max-abs
+<= 2e-2 (over every checked element).  Small workloads are checked on every
+output element; the SDXL-2048/3840 and DiT workloads on seeded samples of
+rows that include the first and last rows of the tiles at both ends of the
+patch, with every (batch, head).
+"""
+import numpy as np
+import pytest
+
+import oracle
+from patch_attention_cfg_amd import dfp, inputs
+from tests import gpu_helpers as G
+
+pytestmark = pytest.mark.gpu
+
+BF16_REL_L2 = 1e-2
+BF16_MAX_ABS = 2e-2
+F32_MAX_ABS = 1e-4
+
+_cache = {}
+
+
+def _inputs(name):
+    if name not in _cache:
+        _cache.clear()
+        _cache[name] = inputs.attention_inputs(inputs.LEVELS[name])
+    return _cache[name]
+
+
+def _check(got, want, kind, what):
+    err = np.abs(got - want).max()
+    if kind == "f32":
+        assert err <= F32_MAX_ABS, f"{what}: max-abs {err}"
+    else:
+        rl = G.rel_l2(got, want)
+        assert rl <= BF16_REL_L2 and err <= BF16_MAX_ABS, f"{what}: relL2 {rl} max-abs {err}"
+    return err
+
+
+def _oracle_full(level, x, p):
+    kf, vf = x.fresh_rows(p)
+    extra = [(x.text_rows()[0], x.text_rows()[1], 0)] if level.n_text else []
+    return oracle.patch_attention(x.q_patch(p), x.k_stale, x.v_stale, kf, vf, level.row0(p),
+                                  1.0 / level.d ** 0.5, extra)
+
+
+@pytest.mark.parametrize("name,p", [("c1", 0), ("c1", 1), ("c2b", 0), ("c2b", 3), ("c2a", 2)])
+def test_full_patch_every_element(name, p):
+    G.require_gpu()
+    level = inputs.LEVELS[name]
+    G.announce(f"attention {name} patch {p} (all elements)")
+    x = _inputs(name)
+    got = G.run_patch(level, x, p)
+    want = _oracle_full(level, x, p)
+    _check(got, want, level.dtype, f"{name} p{p}")
+
+
+@pytest.mark.parametrize("name,p,per_bh", [("c3", 0, 24), ("c3", 7, 24), ("c4", 3, 12),
+                                           ("c4", 7, 8), ("c5", 0, 24), ("c5", 2, 24)])
+def test_large_patch_sampled_rows(name, p, per_bh):
+    G.require_gpu()
+    level = inputs.LEVELS[name]
+    G.announce(f"attention {name} patch {p} (sampled rows)")
+    x = _inputs(name)
+    got = G.run_patch(level, x, p)
+    k_eff = oracle.effective_kv(x.k_stale, x.fresh_rows(p)[0], level.row0(p))
+    v_eff = oracle.effective_kv(x.v_stale, x.fresh_rows(p)[1], level.row0(p))
+    if level.n_text:
+        k_eff = oracle.effective_kv(k_eff, x.text_rows()[0], 0)
+        v_eff = oracle.effective_kv(v_eff, x.text_rows()[1], 0)
+    BH = level.B * level.H
+    bh, rows = G.sample_rows(level.n, BH, per_bh, seed=7 + p)
+    want = oracle.attention_rows(x.q_patch(p), k_eff, v_eff, 1.0 / level.d ** 0.5, bh, rows)
+    got_rows = got.reshape(BH, level.n, level.d)[bh, rows]
+    _check(got_rows, want, "bf16", f"{name} p{p} sampled")
+    assert np.isfinite(got).all()
+
+
+@pytest.mark.parametrize("kind", ["bf16", "f32"])
+@pytest.mark.parametrize("B,H,nq,N,d", [
+    (1, 1, 1, 1, 64),        # one query, one key
+    (1, 2, 7, 13, 64),       # everything ragged, N not a multiple of 8
+    (2, 1, 130, 200, 64),    # ragged query tile and key tile
+    (1, 3, 33, 65, 128),     # d=128 ragged
+    (2, 2, 256, 64, 128),    # exactly one key tile
+    (1, 1, 64, 1000, 64),    # ragged long key range
+])
+def test_edge_shapes_every_element(kind, B, H, nq, N, d):
+    G.require_gpu()
+    G.announce(f"attention edge {kind} B{B} H{H} nq{nq} N{N} d{d}")
+    torch = G.torch_mod()
+    q, k, v = inputs.random_attention_arrays(B, H, nq, N, d, seed=nq * 7 + N, dtype=kind)
+    k_buf, v_buf = dfp.alloc_kv_buffer(B, H, N, d, G.dtype_of(kind))
+    v_buf.fill_(float("nan"))   # padding columns past N must not leak in
+    dfp.kv_scatter(k_buf, v_buf, G.up(k, kind), G.up(v, kind), 0)
+    qd = G.up(q, kind)
+    # canary elements right after the output must stay untouched
+    numel = B * H * nq * d
+    o_flat = torch.full((numel + 256,), float("nan"), dtype=G.dtype_of(kind), device="cuda")
+    o = o_flat[:numel].view(B, H, nq, d)
+    dfp.patch_attention(o, qd, k_buf, v_buf)
+    torch.cuda.synchronize()
+    got = G.down(o)
+    want = oracle.attention(q, k, v, 1.0 / d ** 0.5)
+    _check(got, want, kind, f"edge {B},{H},{nq},{N},{d}")
+    assert torch.isnan(o_flat[numel:]).all()
+
+
+def test_constant_values_and_single_key_properties():
+    G.require_gpu()
+    G.announce("attention properties (V=1, N_kv=1) at c2a shape")
+    torch = G.torch_mod()
+    level = inputs.LEVELS["c2a"]
+    x = _inputs("c2a")
+    B, H, N, d = level.B, level.H, level.N_kv, level.d
+    k_buf, v_buf = dfp.alloc_kv_buffer(B, H, N, d, torch.bfloat16)
+    ones = np.ones((B, H, N, d), dtype=np.float32)
+    dfp.kv_scatter(k_buf, v_buf, G.up(x.k_fresh, "bf16"), G.up(ones, "bf16"), 0)
+    q = G.up(x.q_patch(1), "bf16")
+    o = torch.empty_like(q)
+    dfp.patch_attention(o, q, k_buf, v_buf)
+    torch.cuda.synchronize()
+    assert np.abs(G.down(o) - 1.0).max() <= BF16_MAX_ABS
+    # one key: the output is that key's value row
+    k1, v1 = dfp.alloc_kv_buffer(B, H, 1, d, torch.bfloat16)
+    vrow = x.v_fresh[:, :, :1]
+    dfp.kv_scatter(k1, v1, G.up(x.k_fresh[:, :, :1], "bf16"), G.up(vrow, "bf16"), 0)
+    dfp.patch_attention(o, q, k1, v1)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(G.down(o), np.broadcast_to(vrow, o.shape), rtol=0, atol=0)
+
+
+def test_stale_equal_fresh_gives_full_attention_rows():
+    # synchronous warm-up case: the patch's rows of full attention
+    G.require_gpu()
+    G.announce("attention stale==fresh c2b")
+    level = inputs.LEVELS["c2b"]
+    x = _inputs("c2b")
+    same = inputs.AttnInputs(level, x.q, x.k_fresh, x.v_fresh, x.k_fresh, x.v_fresh)
+    p = 2
+    got = G.run_patch(level, same, p)
+    full_rows = oracle.attention(x.q_patch(p), x.k_fresh, x.v_fresh, 1.0 / level.d ** 0.5)
+    _check(got, full_rows, "bf16", "stale==fresh")
+
+
+def test_deterministic_bitwise():
+    G.require_gpu()
+    G.announce("attention determinism c2a")
+    level = inputs.LEVELS["c2a"]
+    x = _inputs("c2a")
+    a = G.run_patch(level, x, 0)
+    b = G.run_patch(level, x, 0)
+    np.testing.assert_array_equal(a, b)

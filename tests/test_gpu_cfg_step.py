@@ -1,0 +1,154 @@
+"""GPU parity of the fused guidance + sampler + rel-MAE step (dfp_cfg_step)
+and of dfp_relmae against the fp64 oracle.
+
+Bars: latent step relative L2 <= 1e-5, checked one step at a time (both
+sides start each step from the same fp32 x_t); rel-MAE relative error
+<= 1e-5 at every step.  Every workload runs its full sampler (10 / 50 / 28
+steps)."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from patch_attention_cfg_amd import dfp, inputs
+from tests import gpu_helpers as G
+
+pytestmark = pytest.mark.gpu
+
+STEP_REL_L2 = 1e-5
+RELMAE_REL = 1e-5
+
+
+def _schedule(wl):
+    return oracle.DDIMSchedule(wl.steps) if wl.sampler == "ddim" else oracle.EulerSchedule(wl.steps)
+
+
+def _gpu_coeffs(wl, i):
+    """The GPU path's own coefficients from the library's host helpers."""
+    if wl.sampler == "ddim":
+        abar = dfp.scaled_linear_abar(1000, 0.00085, 0.012)
+        ts = dfp.ddim_timesteps(1000, wl.steps)
+        S = wl.steps
+        t = ts[S - 1 - i]
+        a_prev = 1.0 if i == S - 1 else abar[ts[S - 2 - i]]
+        return dfp.ddim_coeffs(abar[t], a_prev)
+    sig = [1.0 - k / wl.steps for k in range(wl.steps + 1)]
+    return dfp.euler_coeffs(sig[i], sig[i + 1])
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5"])
+def test_sampler_run_step_by_step(name):
+    G.require_gpu()
+    wl = inputs.WORKLOADS[name]
+    G.announce(f"cfg step {name}: {wl.steps} {wl.sampler} steps on {wl.latent}")
+    torch = G.torch_mod()
+    stream = inputs.sampler_stream(wl)
+    sch = _schedule(wl)
+    batch = wl.latent[0]
+    n = wl.n_latent
+    ws = dfp.cfg_workspace(n, batch)
+    r_dev = torch.empty(batch, dtype=torch.float32, device="cuda")
+    x_host = stream.x_T.astype(np.float32)
+    x_ref_traj = x_host.astype(np.float64)
+    worst_step, worst_r = 0.0, 0.0
+    for i in range(wl.steps):
+        g_c, g_u = stream.next_pair()
+        x = torch.from_numpy(x_host).cuda()
+        c_x, c_e = _gpu_coeffs(wl, i)
+        dfp.cfg_step(x, torch.from_numpy(g_c).cuda(), torch.from_numpy(g_u).cuda(), wl.w,
+                     c_x, c_e, r_dev, ws)
+        torch.cuda.synchronize()
+        got = x.cpu().numpy()
+        want, r_want = sch.step(x_host, g_c, g_u, wl.w, i)
+        err = G.rel_l2(got, want)
+        r_got = float(r_dev[0].item())
+        rerr = abs(r_got - r_want) / abs(r_want)
+        worst_step, worst_r = max(worst_step, err), max(worst_r, rerr)
+        assert err <= STEP_REL_L2, f"{name} step {i}: rel L2 {err}"
+        assert rerr <= RELMAE_REL, f"{name} step {i}: rel-MAE {r_got} vs {r_want}"
+        x_ref_traj, _ = sch.step(x_ref_traj, g_c, g_u, wl.w, i)
+        x_host = got
+    assert int(ws[:4].view(torch.int32)[0].item()) == 0   # counter left at zero
+    traj = G.rel_l2(x_host, x_ref_traj)
+    G.announce(f"{name}: worst step relL2 {worst_step:.2e}, worst rel-MAE err {worst_r:.2e}, "
+               f"full-trajectory relL2 {traj:.2e}")
+    assert np.isfinite(x_host).all()
+
+
+def test_relmae_alone_batch_and_determinism():
+    G.require_gpu()
+    G.announce("relmae batch=3, determinism")
+    torch = G.torch_mod()
+    r = np.random.Generator(np.random.PCG64(77))
+    n = 4 * 96 * 96
+    g_c = r.standard_normal((3, n), dtype=np.float32)
+    g_u = r.standard_normal((3, n), dtype=np.float32)
+    g_c[1] = 1.5 * g_u[1]                      # rel-MAE exactly 0.5
+    ws = dfp.cfg_workspace(n, 3)
+    out = torch.empty(3, dtype=torch.float32, device="cuda")
+    dc, du = torch.from_numpy(g_c).cuda(), torch.from_numpy(g_u).cuda()
+    dfp.relmae(dc, du, out, ws)
+    torch.cuda.synchronize()
+    a = out.cpu().numpy().copy()
+    for b in range(3):
+        want = oracle.relmae(g_c[b], g_u[b])
+        assert abs(a[b] - want) / want <= RELMAE_REL
+    assert abs(a[1] - 0.5) < 1e-6
+    dfp.relmae(dc, du, out, ws)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(out.cpu().numpy(), a)
+
+
+@pytest.mark.parametrize("n,offset", [(1001, 0), (4096, 1), (3, 0), (1, 0)])
+def test_scalar_path_ragged_or_misaligned(n, offset):
+    G.require_gpu()
+    G.announce(f"cfg step scalar path n={n} offset={offset}")
+    torch = G.torch_mod()
+    r = np.random.Generator(np.random.PCG64(n + offset))
+    x0 = r.standard_normal(n, dtype=np.float32)
+    g_c = r.standard_normal(n, dtype=np.float32)
+    g_u = r.standard_normal(n, dtype=np.float32)
+
+    def dev(a):
+        t = torch.zeros(n + offset, dtype=torch.float32, device="cuda")
+        t[offset:] = torch.from_numpy(a).cuda()
+        return t[offset:].view(1, n)
+
+    x = dev(x0)
+    out = torch.empty(1, dtype=torch.float32, device="cuda")
+    ws = dfp.cfg_workspace(n, 1)
+    c_x, c_e = dfp.ddim_coeffs(0.3, 0.6)
+    dfp.cfg_step(x, dev(g_c), dev(g_u), 7.5, c_x, c_e, out, ws)
+    torch.cuda.synchronize()
+    want = oracle.ddim_step(x0, oracle.cfg_combine(g_c, g_u, 7.5), 0.3, 0.6, False)
+    assert G.rel_l2(x.cpu().numpy().ravel(), want) <= STEP_REL_L2
+    rw = oracle.relmae(g_c, g_u)
+    assert abs(out.item() - rw) / rw <= RELMAE_REL
+
+
+def test_no_reduction_and_degenerate_ratios():
+    G.require_gpu()
+    G.announce("cfg step without rel-MAE; degenerate rel-MAE")
+    torch = G.torch_mod()
+    n = 4 * 32 * 32
+    r = np.random.Generator(np.random.PCG64(3))
+    x0 = r.standard_normal((1, n), dtype=np.float32)
+    g = r.standard_normal((1, n), dtype=np.float32)
+    x = torch.from_numpy(x0).cuda()
+    dg = torch.from_numpy(g).cuda()
+    c_x, c_e = dfp.euler_coeffs(1.0, 0.5)
+    dfp.cfg_step(x, dg, dg, 3.5, c_x, c_e, None, None)
+    torch.cuda.synchronize()
+    want = oracle.euler_step(x0, g, 1.0, 0.5)
+    assert G.rel_l2(x.cpu().numpy(), want) <= STEP_REL_L2
+    ws = dfp.cfg_workspace(n, 2)
+    out = torch.empty(2, dtype=torch.float32, device="cuda")
+    zeros = torch.zeros((2, n), dtype=torch.float32, device="cuda")
+    ones = torch.ones((2, n), dtype=torch.float32, device="cuda")
+    dfp.relmae(zeros, zeros, out, ws)
+    torch.cuda.synchronize()
+    assert math.isnan(out[0].item()) and math.isnan(out[1].item())
+    dfp.relmae(ones, zeros, out, ws)
+    torch.cuda.synchronize()
+    assert math.isinf(out[0].item()) and out[0].item() > 0
