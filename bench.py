@@ -70,6 +70,7 @@ class Level:
             self.text = (up(kt), up(vt))
         self.q = up(x.q_patch(self.p))
         self.o = torch.empty_like(self.q)
+        self.ws = dfp.attention_workspace(level.B, level.H, level.n, level.N_kv, level.d)
         self.scale = 1.0 / level.d ** 0.5
         self.flops = level.flops()
         self.fresh_bytes = 2 * 2 * self.k_new.numel() * 2   # K and V, read + write
@@ -82,7 +83,7 @@ class Level:
             dfp.kv_scatter(self.k_buf, self.v_buf, self.text[0], self.text[1], 0)
 
     def attend(self, dfp):
-        dfp.patch_attention(self.o, self.q, self.k_buf, self.v_buf, self.scale)
+        dfp.patch_attention(self.o, self.q, self.k_buf, self.v_buf, self.scale, self.ws)
 
 
 class Sampler:
@@ -119,11 +120,14 @@ class Sampler:
 
 def time_kernel(torch, fn, reps):
     """Average duration (us) of `fn`'s launches: HIP events around each of
-    `reps` back-to-back launches on the current stream."""
+    `reps` back-to-back launches on the current stream.  A GPU spin queued
+    first lets every launch and event reach the queue before any of them
+    runs, so host launch latency does not land between the events."""
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
     fn()
     torch.cuda.synchronize()
+    torch.cuda._sleep(int(2e6 + reps * 1e5))
     for s, e in zip(starts, ends):
         s.record()
         fn()

@@ -128,11 +128,15 @@ dfp_status dfp_kv_scatter(void *k_buf, void *v_buf_t, const void *k_new,
  *   k_buf   [B][H][N_kv][d]   dtype dt.
  *   v_buf_t [B][H][d][ldv]    dtype dt, ldv = dfp_v_ld(N_kv, dt).
  *   scale   softmax scale, normally 1/sqrt(d); must be finite and > 0.
- *   workspace/ws_bytes  optional device scratch (may be NULL/0).  With at
- *           least dfp_workspace_bytes(DFP_OP_PATCH_ATTENTION, ...) bytes the
- *           kernel may split the key range across workgroups when the query
- *           grid alone is too small to fill the GPU; without it it never
- *           splits.  The result does not depend on the workspace contents.
+ *   workspace/ws_bytes  optional device scratch (may be NULL/0), 256-byte
+ *           aligned.  With at least dfp_workspace_bytes(DFP_OP_PATCH_ATTENTION,
+ *           ...) bytes the kernel may split the key range across workgroups
+ *           when the query grid alone is too small to fill the GPU; without
+ *           it, it never splits.  The workspace starts with per-query-tile
+ *           arrival counters that must be zero before the first call (e.g.
+ *           allocate it zeroed); every call leaves them zero again.  The
+ *           split partials are merged in a fixed order, so results are
+ *           bitwise reproducible for a given shape.
  * d must be 64 or 128.  n_q == 0 is a no-op (pointers may then be NULL).
  * o must not alias the inputs.
  * Errors: INVALID_ARG for null pointers, non-positive B/H/N_kv, negative n_q,

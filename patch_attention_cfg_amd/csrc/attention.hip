@@ -128,16 +128,10 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 }  // namespace
 
-size_t dfp_attn_workspace_bytes(int B, int H, int n_q, int N_kv, int d) {
-    (void)B; (void)H; (void)n_q; (void)N_kv; (void)d;
-    return 0;  // the current kernels never split the key range
-}
-
 extern "C" dfp_status dfp_patch_attention(void *o, const void *q, const void *k_buf,
                                           const void *v_buf_t, int B, int H, int n_q, int N_kv,
                                           int d, float scale, dfp_dtype dt, void *workspace,
                                           size_t ws_bytes, hipStream_t stream) {
-    (void)workspace; (void)ws_bytes;
     if (B <= 0 || H <= 0 || N_kv <= 0 || n_q < 0) return DFP_ERR_INVALID_ARG;
     if (!(scale > 0.f) || !std::isfinite(scale)) return DFP_ERR_INVALID_ARG;
     if (dt != DFP_BF16 && dt != DFP_F32) return DFP_ERR_UNSUPPORTED;
@@ -149,6 +143,7 @@ extern "C" dfp_status dfp_patch_attention(void *o, const void *q, const void *k_
     const int64_t BH = (int64_t)B * H;
     if (BH > 0x7FFFFFFF) return DFP_ERR_UNSUPPORTED;
     if (dt == DFP_BF16)
-        return dfp_attn_bf16_launch(o, q, k_buf, v_buf_t, (int)BH, n_q, N_kv, d, scale, stream);
+        return dfp_attn_bf16_launch(o, q, k_buf, v_buf_t, (int)BH, n_q, N_kv, d, scale, workspace,
+                                    ws_bytes, stream);
     return attn_f32_launch(o, q, k_buf, v_buf_t, (int)BH, n_q, N_kv, d, scale, stream);
 }

@@ -8,26 +8,51 @@
 // holds this step's K/V for the patch's own rows and the previous step's
 // K/V for every other row, so the patch's output is plain softmax attention
 // over all N_kv buffer rows.  The kernel streams the buffer tile by tile
-// with an online (running max / running sum) softmax, so its memory is
-// O(tile) whatever N_kv is, and the result equals two-pass softmax up to
-// rounding.
+// with an online softmax, so its memory is O(tile) whatever N_kv is, and
+// the result equals two-pass softmax up to rounding.
 //
-// Layout of the work (per workgroup: 4 wavefronts x 32 query rows):
+// Work layout (one workgroup = NW wavefronts x 32 query rows, over one
+// contiguous range of 64-key tiles; NW = 4 for d=64, 8 for d=128):
 //   * Each wavefront keeps its 32 queries in registers as the B operand of
 //     S^T = K Q^T (32 keys x 32 queries per MFMA block).  Computing S^T
-//     rather than S leaves every score of one query in one lane pair
-//     (lane l and l^32), so the row max needs one cross-lane exchange and
-//     the probabilities are already in the B-operand layout of
-//     O^T = V^T P^T -- no LDS round trip and no transpose for P.
-//   * K tiles sit in LDS row-major [key][d]; V is stored transposed in HBM
-//     ([d][token], see dfp.h) so V^T tiles land in LDS as [d][key] and feed
-//     the A operand of O^T = V^T P^T with plain 8-byte reads.
-//   * LDS rows are padded (K: +16 B, V^T: +8 B) so the 32 rows one MFMA
-//     operand read touches fall in distinct banks.
-//   * Two LDS stages: the next tile's global loads are issued before the
-//     current tile's math and stored after it (one barrier per tile).
-//   * exp(x) is evaluated as exp2 with log2(e) * scale folded into one FMA.
+//     leaves every score of one query in one lane pair (l, l^32), so the
+//     row max needs one cross-lane swap and the probabilities already sit
+//     in the B-operand layout of O^T = V^T P^T: no LDS round trip and no
+//     transpose for P.
+//   * K and V^T tiles move from HBM straight into LDS with
+//     global_load_lds_dwordx4 (no VGPR staging).  V is stored transposed in
+//     HBM ([d][token]) so V^T tiles feed the A operand of O^T = V^T P^T with
+//     plain 8-byte LDS reads.  LDS rows carry one 16-byte pad slot, so the
+//     32 rows an operand read touches hit distinct banks; lanes whose
+//     16-byte slot is a pad fetch an in-row chunk that is never read.
+//   * Three LDS stages per operand: tile t+3's K and tile t+1's V are in
+//     flight while step t computes, one barrier per step.
+//   * Each step is one basic block holding three independent streams:
+//     tile t+1's Q.K^T MFMAs, tile t-1's P.V MFMAs and tile t's softmax
+//     VALU work, interleaved in a fixed order (alternating accumulators,
+//     LDS operands read two MFMAs ahead).
+//   * Q is multiplied by scale * log2(e) once, as it enters registers, and
+//     each Q.K^T accumulator starts at -m (the reference max), so the MFMA
+//     emits scores in log2 units already relative to the reference.  The
+//     softmax VALU work per score is then one exp2, half a bf16 pack and
+//     half a dot2 -- the row sum is taken on the bf16-rounded
+//     probabilities the P.V product uses.
+//   * The reference max is the first tile's row max and stays fixed while
+//     the scores stay below it + 12 (log2 units).  Every probability is
+//     bounded by the tile's row-sum share, so a share of at most 2^12
+//     proves that; a larger one sends the wavefront down a rare path that
+//     raises the reference to the tile max and rescales O and the running
+//     sum.  Numerator and denominator share the reference, so the result
+//     is exactly the softmax whichever reference is used.
+//   * Split-KV for small grids: the key range is cut into `splits` ranges
+//     handled by different workgroups; each writes an fp32 partial
+//     (unnormalised O, running max, running sum) to the workspace, and the
+//     last workgroup of a query tile to finish (integer counter) merges the
+//     partials in split order, so the result is bitwise reproducible.
+//   * Workgroups are mapped to XCDs so that each XCD streams a contiguous
+//     range of (batch, head) buffers, keeping their K/V in that XCD's L2.
 #include <cmath>
+#include <cstdlib>
 
 #include "dfp_common.h"
 #include "dfp_internal.h"
@@ -36,97 +61,54 @@ namespace {
 
 using dfp::bf16x8_t;
 using dfp::f32x16_t;
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
-constexpr int kWaves = 4;
-constexpr int kQPW = 32;                  // query rows per wavefront
-constexpr int kBlockM = kWaves * kQPW;    // query rows per workgroup
-constexpr int kBlockN = 64;               // keys per tile
-constexpr int kThreads = kWaves * dfp::kWave;
+constexpr float kMaxTileSum = 4096.0f;   // a tile's row-sum share above this raises the max
+constexpr int kNumXcd = 8;
+
+struct Params {
+    const uint16_t *Q;
+    const uint16_t *K;
+    const uint16_t *Vt;
+    uint16_t *O;
+    float *part_o;       // [BH*q_tiles][splits][BLOCK_M][D] unnormalised partial O
+    float *part_ml;      // [BH*q_tiles][splits][BLOCK_M][2] running max / sum
+    unsigned *counters;  // [BH*q_tiles] arrival counters (zero between calls)
+    int64_t ldv;
+    int n_q;
+    int N_kv;
+    float c_log2;
+    int q_tiles;
+    int splits;
+    int tiles_per_split;
+    int total_wg;
+};
 
 template <int D>
-struct Smem {
-    static constexpr int K_LD = D + 8;            // bf16 per K row in LDS
-    static constexpr int V_LD = kBlockN + 4;      // bf16 per V^T row in LDS
-    static constexpr int K_TILE = kBlockN * K_LD;
+struct Cfg {
+    static constexpr int NW = D == 64 ? 4 : 8;   // wavefronts per workgroup
+    static constexpr int WG_PER_CU = D == 64 ? 2 : 1;   // resident workgroups per CU
+    static constexpr int THREADS = NW * dfp::kWave;
+    static constexpr int BLOCK_M = NW * 32;      // query rows per workgroup
+    static constexpr int BN = 64;                // keys per tile
+    static constexpr int K_SLOTS = D / 8 + 1;    // 16-byte slots per K row in LDS (one pad)
+    static constexpr int V_SLOTS = BN / 8 + 1;   // 16-byte slots per V^T row in LDS (one pad)
+    static constexpr int K_LD = K_SLOTS * 8;     // bf16 per K row in LDS
+    static constexpr int V_LD = V_SLOTS * 8;     // bf16 per V^T row in LDS
+    static constexpr int K_TILE = BN * K_LD;
     static constexpr int V_TILE = D * V_LD;
-    static constexpr int STAGE = K_TILE + V_TILE;
-    static constexpr int K_CHUNKS = kBlockN * D / 8 / kThreads;  // 16-byte chunks per thread
-    static constexpr int V_CHUNKS = D * kBlockN / 8 / kThreads;
+    static constexpr int K_DMA = BN * K_SLOTS / 64;   // 64-lane DMA instructions per K tile
+    static constexpr int V_DMA = D * V_SLOTS / 64;    // ... per V^T tile
+    static constexpr int K_DMA_W = (K_DMA + NW - 1) / NW;  // per wavefront (upper bound)
+    static constexpr int V_DMA_W = (V_DMA + NW - 1) / NW;
+    static constexpr int STAGES = 3;
+    static constexpr int SB = BN / 32;           // 32-key score blocks per tile
+    static constexpr int DB = D / 32;            // 32-channel output blocks
+    static constexpr int KC = D / 16;            // K=16 slices of the Q.K^T product
+    static_assert(BN * K_SLOTS % 64 == 0 && D * V_SLOTS % 64 == 0, "whole DMA instructions");
 };
 
 __device__ __forceinline__ uint4 zero4() { return make_uint4(0u, 0u, 0u, 0u); }
-
-// Zero the bf16 lanes of a 16-byte chunk whose key index is >= N_kv.
-__device__ __forceinline__ uint4 mask_keys(uint4 v, int key0, int N_kv) {
-    uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const int k_lo = key0 + 2 * e, k_hi = k_lo + 1;
-        uint32_t lo = k_lo < N_kv ? (w[e] & 0xFFFFu) : 0u;
-        uint32_t hi = k_hi < N_kv ? (w[e] & 0xFFFF0000u) : 0u;
-        w[e] = lo | hi;
-    }
-    return make_uint4(w[0], w[1], w[2], w[3]);
-}
-
-template <int D>
-struct TileLoader {
-    uint4 k[Smem<D>::K_CHUNKS];
-    uint4 v[Smem<D>::V_CHUNKS];
-
-    // Global -> registers for the tile starting at key j0.
-    __device__ __forceinline__ void load(const uint16_t *__restrict__ Kh,
-                                         const uint16_t *__restrict__ Vh, int j0, int N_kv,
-                                         int64_t ldv, int tid) {
-        constexpr int KCPR = D / 8;  // K chunks per key row
-#pragma unroll
-        for (int c = 0; c < Smem<D>::K_CHUNKS; ++c) {
-            const int idx = tid + c * kThreads;
-            const int row = idx / KCPR, col = idx % KCPR;
-            const int key = j0 + row;
-            k[c] = key < N_kv
-                       ? *reinterpret_cast<const uint4 *>(Kh + (int64_t)key * D + col * 8)
-                       : zero4();
-        }
-        constexpr int VCPR = kBlockN / 8;  // V^T chunks per channel row
-#pragma unroll
-        for (int c = 0; c < Smem<D>::V_CHUNKS; ++c) {
-            const int idx = tid + c * kThreads;
-            const int row = idx / VCPR, col = idx % VCPR;
-            const int key0 = j0 + col * 8;
-            if (key0 + 8 <= N_kv)
-                v[c] = *reinterpret_cast<const uint4 *>(Vh + (int64_t)row * ldv + key0);
-            else if (key0 < N_kv)  // ldv pads rows to 8 keys: the read stays in the row
-                v[c] = mask_keys(*reinterpret_cast<const uint4 *>(Vh + (int64_t)row * ldv + key0),
-                                 key0, N_kv);
-            else
-                v[c] = zero4();
-        }
-    }
-
-    // Registers -> LDS stage.
-    __device__ __forceinline__ void store(uint16_t *stage, int tid) const {
-        constexpr int KCPR = D / 8;
-        uint16_t *Ks = stage;
-        uint16_t *Vs = stage + Smem<D>::K_TILE;
-#pragma unroll
-        for (int c = 0; c < Smem<D>::K_CHUNKS; ++c) {
-            const int idx = tid + c * kThreads;
-            const int row = idx / KCPR, col = idx % KCPR;
-            *reinterpret_cast<uint4 *>(Ks + row * Smem<D>::K_LD + col * 8) = k[c];
-        }
-        constexpr int VCPR = kBlockN / 8;
-#pragma unroll
-        for (int c = 0; c < Smem<D>::V_CHUNKS; ++c) {
-            const int idx = tid + c * kThreads;
-            const int row = idx / VCPR, col = idx % VCPR;
-            // V^T rows are 8-byte aligned in LDS (V_LD*2 = 136 B): two 8-byte stores
-            uint2 *dst = reinterpret_cast<uint2 *>(Vs + row * Smem<D>::V_LD + col * 8);
-            dst[0] = make_uint2(v[c].x, v[c].y);
-            dst[1] = make_uint2(v[c].z, v[c].w);
-        }
-    }
-};
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) {
     bf16x8_t r;
@@ -134,12 +116,390 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) {
     return r;
 }
 
+// XCD-aware logical workgroup index: the hardware deals workgroup i to XCD
+// i % 8, so give XCD x the contiguous logical range of its share.
+__device__ __forceinline__ int logical_wg(int i, int total) {
+    const int x = i % kNumXcd, j = i / kNumXcd;
+    const int base = total / kNumXcd, rem = total % kNumXcd;
+    return x * base + (x < rem ? x : rem) + j;
+}
+
+// Max / sum of x over the lane pair (l, l^32): v_permlane32_swap of x with
+// itself yields x of lanes 0-31 in the first result and x of lanes 32-63 in
+// the second, in both halves of the wave.
+__device__ __forceinline__ float pair_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                     false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float pair_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                     false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+typedef int int32x4_t __attribute__((ext_vector_type(4)));
+
+// A raw buffer resource (V#) covering `bytes` bytes from `base`; accesses at
+// or past the end read as zero instead of faulting.  Built from uniform
+// values, so it lives in scalar registers.
+__device__ __forceinline__ int32x4_t buffer_rsrc(const void *base, uint32_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    int32x4_t r;
+    r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xFFFFu));   // stride 0
+    r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+    r[3] = 0x00020000;   // gfx9-family raw buffer: dword data, no swizzle
+    return r;
+}
+
+// One 64-lane HBM -> LDS copy instruction (buffer_load_dwordx4 ... lds):
+// lane l reads the 16 bytes at byte offset `voff` of the buffer and writes
+// them to LDS byte address lds + 16 l.  It is issued from inline assembly
+// so that the compiler, which cannot tell which LDS stage a copy lands in,
+// does not wait for copies in flight before every LDS read; the kernel
+// instead waits for them explicitly (vmcnt) right before the barrier that
+// publishes a stage.  M0 carries the LDS address; nothing else in this
+// kernel uses M0 (checked on the built code object).
+__device__ __forceinline__ void lds_dma16(int32x4_t rsrc, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(
+                     __builtin_amdgcn_readfirstlane(lds)),
+                 "v"(voff), "s"(rsrc)
+                 : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+    return __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>(p));
+}
+
+// Wait until every copy this wavefront issued has landed in LDS.
+__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Direct HBM -> LDS copies of one K tile (rows [j0, j0+64)) and one V^T tile
+// (columns [j0, j0+64)).  Copy instruction i of a tile writes LDS slots
+// [64 i, 64 i + 64): slot s = 64 i + lane is row s / SLOTS, 16-byte chunk
+// s % SLOTS of the padded tile; a pad chunk fetches the row's chunk 0 (never
+// read).  Each wavefront issues instructions w, w + NW, ...  The buffer
+// resource starts at the tile, so every lane's byte offset is fixed for the
+// kernel.  K rows past N_kv fall outside the resource and read as zero
+// (their scores are masked anyway); V^T reads past a row's end land in the
+// next row or read as zero, and keys >= N_kv are zeroed in LDS afterwards.
 template <int D>
-__global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16(
-    const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
-    const uint16_t *__restrict__ Vt, uint16_t *__restrict__ O, int n_q, int N_kv, int64_t ldv,
-    float c_log2, int q_tiles) {
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * Smem<D>::STAGE];
+struct TileDma {
+    using C = Cfg<D>;
+    uint32_t k_off[C::K_DMA_W];   // byte offset of this lane's K chunk within a tile
+    uint32_t v_off[C::V_DMA_W];   // byte offset of this lane's V^T chunk (key 0 of the tile)
+    int wave;
+
+    __device__ __forceinline__ void init(int wv, int lane, int64_t ldv) {
+        wave = __builtin_amdgcn_readfirstlane(wv);
+#pragma unroll
+        for (int k = 0; k < C::K_DMA_W; ++k) {
+            const int s = (wave + k * C::NW) * 64 + lane;
+            const int row = s / C::K_SLOTS;
+            int col = s % C::K_SLOTS;
+            if (col == C::K_SLOTS - 1) col = 0;
+            k_off[k] = (uint32_t)(row * D * 2 + col * 16);
+        }
+#pragma unroll
+        for (int k = 0; k < C::V_DMA_W; ++k) {
+            const int s = (wave + k * C::NW) * 64 + lane;
+            const int row = s / C::V_SLOTS;
+            int col = s % C::V_SLOTS;
+            if (col == C::V_SLOTS - 1) col = 0;
+            v_off[k] = (uint32_t)(row * ldv * 2 + col * 16);
+        }
+    }
+
+    __device__ __forceinline__ void load_k(const uint16_t *Kh, int j0, int N_kv,
+                                           const uint16_t *Ks) const {
+        const int32x4_t rs = buffer_rsrc(Kh + (int64_t)j0 * D, (uint32_t)(N_kv - j0) * D * 2);
+        const uint32_t lds = lds_addr(Ks);
+#pragma unroll
+        for (int k = 0; k < C::K_DMA_W; ++k) {
+            const int i = wave + k * C::NW;
+            if (C::K_DMA % C::NW != 0 && i >= C::K_DMA) break;   // wave-uniform
+            lds_dma16(rs, k_off[k], lds + i * 1024);
+        }
+    }
+
+    __device__ __forceinline__ void load_v(const uint16_t *Vh, int j0, int64_t ldv,
+                                           const uint16_t *Vs) const {
+        const int32x4_t rs = buffer_rsrc(Vh + j0, (uint32_t)((int64_t)D * ldv - j0) * 2);
+        const uint32_t lds = lds_addr(Vs);
+#pragma unroll
+        for (int k = 0; k < C::V_DMA_W; ++k) {
+            const int i = wave + k * C::NW;
+            if (C::V_DMA % C::NW != 0 && i >= C::V_DMA) break;   // wave-uniform
+            lds_dma16(rs, v_off[k], lds + i * 1024);
+        }
+    }
+};
+
+// Zero V^T columns of keys >= N_kv in a landed tile (ragged last tile).
+template <int D>
+__device__ __forceinline__ void zero_tail_v(uint16_t *Vs, int j0, int N_kv, int tid) {
+    using C = Cfg<D>;
+    const int first = N_kv - j0;   // first masked key within the tile (1..63)
+    for (int e = tid; e < D * C::BN; e += C::THREADS) {
+        const int row = e / C::BN, kk = e % C::BN;
+        if (kk >= first) Vs[row * C::V_LD + kk] = 0;
+    }
+}
+
+// S^T = K Q^T for one tile: s[sb][i] is the score of key
+// sb*32 + (i/4)*8 + g*4 + i%4 (tile-relative) against query ql.
+template <int D>
+__device__ __forceinline__ void qk_tile(f32x16_t (&s)[Cfg<D>::SB], const uint16_t *Ks,
+                                        const bf16x8_t (&qreg)[Cfg<D>::KC], int ql, int g) {
+    using C = Cfg<D>;
+#pragma unroll
+    for (int kc = 0; kc < C::KC; ++kc)
+#pragma unroll
+        for (int sb = 0; sb < C::SB; ++sb) {
+            const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(
+                Ks + (sb * 32 + ql) * C::K_LD + kc * 16 + g * 8);
+            if (kc == 0) {
+                const f32x16_t zero = {};
+                s[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[0], zero, 0, 0, 0);
+            } else {
+                s[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[kc], s[sb], 0, 0, 0);
+            }
+        }
+}
+
+// O^T += V^T P^T over one tile's 16-key slices.  MFMA k index g*8 + j of
+// slice kc2 is key kc2*16 + (j/4)*8 + g*4 + j%4 on both operands.
+template <int D>
+__device__ __forceinline__ void pv_tile(f32x16_t (&oacc)[Cfg<D>::DB],
+                                        const bf16x8_t (&pm)[Cfg<D>::SB][2], const uint16_t *Vs,
+                                        int ql, int g) {
+    using C = Cfg<D>;
+#pragma unroll
+    for (int kc2 = 0; kc2 < C::BN / 16; ++kc2) {
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) {
+            const uint16_t *vrow = Vs + (db * 32 + ql) * C::V_LD + kc2 * 16 + g * 4;
+            const uint2 lo = *reinterpret_cast<const uint2 *>(vrow);
+            const uint2 hi = *reinterpret_cast<const uint2 *>(vrow + 8);
+            const bf16x8_t a = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pm[kc2 >> 1][kc2 & 1], oacc[db],
+                                                                0, 0, 0);
+        }
+    }
+}
+
+// The fixed order of one step's MFMAs: pairs of Q.K^T MFMAs alternate with
+// pairs of P.V MFMAs, so consecutive MFMAs never share an accumulator.
+template <int D>
+struct Steps {
+    using C = Cfg<D>;
+    static constexpr int NQ = C::SB * C::KC;             // Q.K^T MFMAs per tile
+    static constexpr int NV = (C::BN / 16) * C::DB;      // P.V MFMAs per tile
+    static constexpr int N = NQ + NV;
+    static_assert(NQ == NV, "steps alternate pairs of Q.K^T and P.V MFMAs");
+    static constexpr bool is_qk(int i) { return (i & 3) < 2; }
+    static constexpr int idx(int i) { return (i >> 2) * 2 + (i & 1); }
+    static constexpr int CHUNKS = C::SB * 8;             // pairs of probabilities
+    static constexpr int CHUNK_EVERY = N / CHUNKS;       // MFMAs per softmax chunk
+};
+
+// ko = ql*K_LD + g*8 and vo = ql*V_LD + g*4 are the lane's element offsets
+// inside a K / V^T stage; everything else in the address is a constant.
+template <int D>
+__device__ __forceinline__ bf16x8_t step_operand(int i, const uint16_t *Kn, const uint16_t *Vp,
+                                                 int ko, int vo) {
+    using C = Cfg<D>;
+    using S = Steps<D>;
+    if (S::is_qk(i)) {
+        const int q = S::idx(i), kc = q / C::SB, sb = q % C::SB;
+        return *reinterpret_cast<const bf16x8_t *>(Kn + ko + sb * 32 * C::K_LD + kc * 16);
+    }
+    const int v = S::idx(i), kc2 = v / C::DB, db = v % C::DB;
+    const uint16_t *vrow = Vp + vo + db * 32 * C::V_LD + kc2 * 16;
+    const uint2 lo = *reinterpret_cast<const uint2 *>(vrow);
+    const uint2 hi = *reinterpret_cast<const uint2 *>(vrow + 8);
+    return as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+}
+
+// One step's basic block: s_next = K(t+1) Q^T - m (from Kn; Q is pre-scaled
+// by log2(e) * scale and the accumulator starts at -m, so the scores come
+// out in log2 units relative to the reference max), O^T += V(t-1)^T
+// P(t-1)^T (from Vp, p_prev), and the softmax of tile t: p = 2^s rounded
+// to bf16, with this tile's row-sum share (dot2 with ones) on the rounded
+// values accumulated in l_tile.
+// sched_barrier pins the interleaved order; the empty asm keeps the
+// probabilities computed here rather than sunk into the next step.
+template <int D>
+__device__ __forceinline__ void region(f32x16_t (&s_next)[Cfg<D>::SB],
+                                       f32x16_t (&oacc)[Cfg<D>::DB],
+                                       bf16x8_t (&p_cur)[Cfg<D>::SB][2], float &l_tile,
+                                       const f32x16_t (&s_cur)[Cfg<D>::SB],
+                                       const bf16x8_t (&p_prev)[Cfg<D>::SB][2],
+                                       const uint16_t *Kn, const uint16_t *Vp,
+                                       const bf16x8_t (&qreg)[Cfg<D>::KC], const f32x16_t &negm,
+                                       int ko, int vo) {
+    using C = Cfg<D>;
+    using S = Steps<D>;
+    const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+    // opaque per step: keeps the compiler from hoisting one address
+    // register per stage out of the unrolled loop
+    asm volatile("" : "+v"(ko), "+v"(vo));
+    bf16x8_t ring[3];
+    ring[0] = step_operand<D>(0, Kn, Vp, ko, vo);
+    ring[1] = step_operand<D>(1, Kn, Vp, ko, vo);
+#pragma unroll
+    for (int i = 0; i < S::N; ++i) {
+        if (i + 2 < S::N) ring[(i + 2) % 3] = step_operand<D>(i + 2, Kn, Vp, ko, vo);
+        const bf16x8_t a = ring[i % 3];
+        if (S::is_qk(i)) {
+            const int q = S::idx(i), kc = q / C::SB, sb = q % C::SB;
+            s_next[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[kc],
+                                                                  kc == 0 ? negm : s_next[sb],
+                                                                  0, 0, 0);
+        } else {
+            const int v = S::idx(i), kc2 = v / C::DB, db = v % C::DB;
+            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, p_prev[kc2 >> 1][kc2 & 1],
+                                                                oacc[db], 0, 0, 0);
+        }
+        if (i % S::CHUNK_EVERY == S::CHUNK_EVERY - 1) {
+            const int k = i / S::CHUNK_EVERY;      // chunk: two consecutive scores
+            const int sb = k / 8, h = (k % 8) / 4, j = (k % 4) * 2;
+            bf16x2_t pr;
+            pr[0] = (__bf16)__builtin_amdgcn_exp2f(s_cur[sb][h * 8 + j]);
+            pr[1] = (__bf16)__builtin_amdgcn_exp2f(s_cur[sb][h * 8 + j + 1]);
+            l_tile = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_tile, false);
+            p_cur[sb][h][j] = pr[0];
+            p_cur[sb][h][j + 1] = pr[1];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int sb = 0; sb < C::SB; ++sb)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) asm volatile("" ::"v"(p_cur[sb][h]));
+}
+
+template <int D>
+struct State {
+    f32x16_t oacc[Cfg<D>::DB];
+    f32x16_t negm;   // -m_run in every element: the Q.K^T accumulator's start
+    float m_run;     // reference max, log2 units (scores * log2(e) * scale)
+    float l_run;     // this lane's share of the running sum
+};
+
+// Rare path: some probability of tile t exceeded kMaxTileSum (the scores
+// outgrew the reference).  Raise the reference to the tile max, rescale O
+// and l to it, recompute the tile's probabilities, and shift the next
+// tile's scores (computed against the old reference) by the same amount.
+template <int D>
+__device__ __forceinline__ void raise_reference(
+    State<D> &st, f32x16_t (&s_cur)[Cfg<D>::SB], f32x16_t (&s_next)[Cfg<D>::SB],
+    bf16x8_t (&p_cur)[Cfg<D>::SB][2], float &l_tile) {
+    using C = Cfg<D>;
+    float mx = s_cur[0][0];
+#pragma unroll
+    for (int sb = 0; sb < C::SB; ++sb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s_cur[sb][i]);
+    mx = pair_max(mx);
+    const float delta = mx > 0.f ? mx : 0.f;
+    const float alpha = __builtin_amdgcn_exp2f(-delta);
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) st.oacc[db][i] *= alpha;
+    st.l_run *= alpha;
+    const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+    l_tile = 0.f;
+#pragma unroll
+    for (int sb = 0; sb < C::SB; ++sb)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int j = 0; j < 8; j += 2) {
+                bf16x2_t pr;
+                pr[0] = (__bf16)__builtin_amdgcn_exp2f(s_cur[sb][h * 8 + j] - delta);
+                pr[1] = (__bf16)__builtin_amdgcn_exp2f(s_cur[sb][h * 8 + j + 1] - delta);
+                l_tile = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_tile, false);
+                p_cur[sb][h][j] = pr[0];
+                p_cur[sb][h][j + 1] = pr[1];
+            }
+#pragma unroll
+    for (int sb = 0; sb < C::SB; ++sb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s_next[sb][i] -= delta;
+    st.m_run += delta;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) st.negm[i] = -st.m_run;
+}
+
+template <int D>
+struct Smem {
+    uint16_t k[Cfg<D>::STAGES][Cfg<D>::K_TILE];
+    uint16_t v[Cfg<D>::STAGES][Cfg<D>::V_TILE];
+};
+
+struct Ctx {
+    const uint16_t *Kh;
+    const uint16_t *Vh;
+    int64_t ldv;
+    int N_kv, t_begin, t_end;
+    int tid, wave, ql, g;
+};
+
+// One pipeline step for tile t, r = t - t_begin.  On entry K(t+1) is in
+// stage (r+1)%3, V(t-1) in stage (r+2)%3, and K(t+2), V(t) are in flight to
+// stages (r+2)%3 and r%3.  The step computes, waits for its in-flight
+// tiles, publishes them with a barrier, then starts K(t+3) and V(t+1) into
+// the stages freed by tiles t and t-2.
+template <int D, bool RAGGED>
+__device__ __forceinline__ void tile_step(int t, const Ctx &x, State<D> &st, Smem<D> &sm,
+                                          const TileDma<D> &dma, f32x16_t (&s_cur)[Cfg<D>::SB],
+                                          f32x16_t (&s_next)[Cfg<D>::SB],
+                                          const bf16x8_t (&p_prev)[Cfg<D>::SB][2],
+                                          bf16x8_t (&p_cur)[Cfg<D>::SB][2],
+                                          const bf16x8_t (&qreg)[Cfg<D>::KC]) {
+    using C = Cfg<D>;
+    constexpr int BN = C::BN;
+    const int r = t - x.t_begin;
+    const int s0 = r % 3, s1 = (r + 1) % 3, s2 = (r + 2) % 3;
+    const int j0 = t * BN;
+    if (RAGGED && j0 + BN > x.N_kv) {  // ragged last tile: drop keys past the buffer
+#pragma unroll
+        for (int sb = 0; sb < C::SB; ++sb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int key = j0 + sb * 32 + (i >> 2) * 8 + x.g * 4 + (i & 3);
+                if (key >= x.N_kv) s_cur[sb][i] = -INFINITY;
+            }
+    }
+
+    float l_tile = 0.f;
+    region<D>(s_next, st.oacc, p_cur, l_tile, s_cur, p_prev, sm.k[s1], sm.v[s2], qreg, st.negm,
+              x.ql * C::K_LD + x.g * 8, x.ql * C::V_LD + x.g * 4);
+    // each probability is at most the tile's row-sum share, so a share
+    // within kMaxTileSum proves none outgrew the reference
+    if (__any(!(l_tile <= kMaxTileSum))) raise_reference<D>(st, s_cur, s_next, p_cur, l_tile);
+    st.l_run += l_tile;
+
+    wait_dma();                       // this wave's K(t+2), V(t) copies have landed
+    __syncthreads();
+    if (RAGGED && j0 + BN > x.N_kv) {   // V(t) is the ragged last tile
+        zero_tail_v<D>(sm.v[s0], j0, x.N_kv, x.tid);
+        __syncthreads();
+    }
+    if (t + 3 < x.t_end) dma.load_k(x.Kh, j0 + 3 * BN, x.N_kv, sm.k[s0]);
+    if (t + 1 < x.t_end) dma.load_v(x.Vh, j0 + BN, x.ldv, sm.v[s1]);
+}
+
+template <int D>
+__global__ __launch_bounds__(Cfg<D>::THREADS, Cfg<D>::WG_PER_CU) void attn_fwd_bf16(Params p) {
+    using C = Cfg<D>;
+    constexpr int BN = C::BN;
+    __shared__ __attribute__((aligned(16))) Smem<D> sm;
+    __shared__ int s_last;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -147,153 +507,301 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16(
     const int ql = lane & 31;   // query column of this lane in every MFMA block
     const int g = lane >> 5;    // which half of the K=16 slice this lane feeds
 
-    const int bh = blockIdx.x / q_tiles;
-    const int qt = blockIdx.x - bh * q_tiles;
-    const uint16_t *Qh = Q + (int64_t)bh * n_q * D;
-    const uint16_t *Kh = K + (int64_t)bh * N_kv * D;
-    const uint16_t *Vh = Vt + (int64_t)bh * D * ldv;
-    const int q_row = qt * kBlockM + wave * kQPW + ql;
+    const int L = logical_wg(blockIdx.x, p.total_wg);
+    const int split = L % p.splits;
+    const int qtile_id = L / p.splits;          // bh * q_tiles + qt
+    const int bh = qtile_id / p.q_tiles;
+    const int qt = qtile_id - bh * p.q_tiles;
+
+    const int n_q = p.n_q, N_kv = p.N_kv;
+    const uint16_t *Qh = p.Q + (int64_t)bh * n_q * D;
+    const int q_row = qt * C::BLOCK_M + wave * 32 + ql;
     const bool q_valid = q_row < n_q;
 
-    // Q^T as the B operand: lane (ql, g) holds d = kc*16 + g*8 .. +7 of its query.
-    bf16x8_t qreg[D / 16];
-#pragma unroll
-    for (int kc = 0; kc < D / 16; ++kc)
-        qreg[kc] = as_bf16x8(q_valid ? *reinterpret_cast<const uint4 *>(
-                                           Qh + (int64_t)q_row * D + kc * 16 + g * 8)
-                                     : zero4());
+    Ctx x;
+    x.Kh = p.K + (int64_t)bh * N_kv * D;
+    x.Vh = p.Vt + (int64_t)bh * D * p.ldv;
+    x.ldv = p.ldv;
+    x.N_kv = N_kv;
+    const int ntiles = (N_kv + BN - 1) / BN;
+    x.t_begin = split * p.tiles_per_split;
+    x.t_end = min(ntiles, x.t_begin + p.tiles_per_split);
+    x.tid = tid;
+    x.wave = wave;
+    x.ql = ql;
+    x.g = g;
 
-    f32x16_t oacc[D / 32];
+    // Q^T as the B operand: lane (ql, g) holds d = kc*16 + g*8 .. +7 of its
+    // query, pre-multiplied by scale * log2(e) (rounded to bf16) so the
+    // scores come out of the MFMA in log2 units.
+    bf16x8_t qreg[C::KC];
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+    for (int kc = 0; kc < C::KC; ++kc) {
+        const bf16x8_t raw = as_bf16x8(q_valid ? *reinterpret_cast<const uint4 *>(
+                                                     Qh + (int64_t)q_row * D + kc * 16 + g * 8)
+                                               : zero4());
 #pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
-    float m_run = -INFINITY;  // running max, in log2 units (scores * c_log2)
-    float l_run = 0.f;        // this lane's share of the running sum
+        for (int j = 0; j < 8; ++j) qreg[kc][j] = (__bf16)((float)raw[j] * p.c_log2);
+    }
 
-    const int ntiles = (N_kv + kBlockN - 1) / kBlockN;
-    TileLoader<D> ld;
-    ld.load(Kh, Vh, 0, N_kv, ldv, tid);
-    ld.store(smem, tid);
+    State<D> st;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) st.oacc[db][i] = 0.f;
+    st.l_run = 0.f;
+
+    // Prologue: K(t0), K(t0+1) landed; V "tile t0-1" (stage 2) zeroed, since
+    // the first step's P.V uses zero probabilities against it; S(t0); then
+    // K(t0+2) and V(t0) in flight.
+    TileDma<D> dma;
+    dma.init(wave, lane, p.ldv);
+    const int t0 = x.t_begin;
+    dma.load_k(x.Kh, t0 * BN, N_kv, sm.k[0]);
+    if (t0 + 1 < x.t_end) dma.load_k(x.Kh, (t0 + 1) * BN, N_kv, sm.k[1]);
+    for (int e = tid; e < C::V_TILE / 8; e += C::THREADS)
+        reinterpret_cast<uint4 *>(sm.v[2])[e] = zero4();
+    wait_dma();
     __syncthreads();
 
-    for (int t = 0; t < ntiles; ++t) {
-        const int j0 = t * kBlockN;
-        const uint16_t *Ks = smem + (t & 1) * Smem<D>::STAGE;
-        const uint16_t *Vs = Ks + Smem<D>::K_TILE;
-        const bool more = t + 1 < ntiles;
-        if (more) ld.load(Kh, Vh, j0 + kBlockN, N_kv, ldv, tid);
-
-        // S^T = K Q^T for two 32-key blocks.  s[mb][i] is the score of key
-        // j0 + mb*32 + (i/4)*8 + g*4 + i%4 against query ql.
-        f32x16_t s[2];
+    f32x16_t sA[C::SB], sB[C::SB];
+    bf16x8_t pA[C::SB][2], pB[C::SB][2];
+    qk_tile<D>(sA, sm.k[0], qreg, ql, g);
+    // The reference max is the first tile's max over valid keys; it stays
+    // fixed until a later tile outgrows it (raise_reference).
+    {
+        const int nvalid = N_kv - t0 * BN;
+        float mx = -INFINITY;
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) s[mb][i] = 0.f;
-#pragma unroll
-            for (int kc = 0; kc < D / 16; ++kc) {
-                const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(
-                    Ks + (mb * 32 + ql) * Smem<D>::K_LD + kc * 16 + g * 8);
-                s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[kc], s[mb], 0, 0, 0);
-            }
-        }
-
-        if (j0 + kBlockN > N_kv) {  // ragged last tile: drop keys past the buffer
-#pragma unroll
-            for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int key = j0 + mb * 32 + (i >> 2) * 8 + g * 4 + (i & 3);
-                    if (key >= N_kv) s[mb][i] = -INFINITY;
-                }
-        }
-
-        // online softmax: tile max across the lane pair, rescale, exponentiate
-        float mx = s[0][0];
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[mb][i]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float m_new = fmaxf(m_run, mx * c_log2);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        m_run = m_new;
-        float lsum = 0.f;
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
+        for (int sb = 0; sb < C::SB; ++sb)
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const float p = __builtin_amdgcn_exp2f(fmaf(s[mb][i], c_log2, -m_new));
-                s[mb][i] = p;
-                lsum += p;
+                const int key = sb * 32 + (i >> 2) * 8 + g * 4 + (i & 3);
+                if (key >= nvalid) sA[sb][i] = -INFINITY;
+                mx = fmaxf(mx, sA[sb][i]);
             }
-        l_run = fmaf(l_run, alpha, lsum);
+        st.m_run = pair_max(mx);
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db)
+        for (int sb = 0; sb < C::SB; ++sb)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+            for (int i = 0; i < 16; ++i) sA[sb][i] -= st.m_run;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) st.negm[i] = -st.m_run;
+    }
+#pragma unroll
+    for (int sb = 0; sb < C::SB; ++sb)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) pB[sb][h][j] = (__bf16)0.0f;
+    if (t0 + 2 < x.t_end) dma.load_k(x.Kh, (t0 + 2) * BN, N_kv, sm.k[2]);
+    dma.load_v(x.Vh, t0 * BN, p.ldv, sm.v[0]);
 
-        // O^T += V^T P^T over four 16-key slices.  MFMA k index g*8 + j of
-        // slice kc2 is key kc2*16 + (j/4)*8 + g*4 + j%4 on both operands.
-#pragma unroll
-        for (int kc2 = 0; kc2 < kBlockN / 16; ++kc2) {
-            const int mb = kc2 >> 1, half = kc2 & 1;
-            bf16x8_t pb;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) pb[j] = (__bf16)s[mb][half * 8 + j];
-#pragma unroll
-            for (int db = 0; db < D / 32; ++db) {
-                const uint16_t *vrow = Vs + (db * 32 + ql) * Smem<D>::V_LD + kc2 * 16 + g * 4;
-                const uint2 lo = *reinterpret_cast<const uint2 *>(vrow);
-                const uint2 hi = *reinterpret_cast<const uint2 *>(vrow + 8);
-                const bf16x8_t a = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
-                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, oacc[db], 0, 0, 0);
-            }
-        }
-
-        if (more) ld.store(smem + ((t + 1) & 1) * Smem<D>::STAGE, tid);
-        __syncthreads();
+    // Two register sets alternate roles from step to step, so the loop runs
+    // two steps per trip and never copies scores or probabilities.  Only
+    // the last tile can be ragged: the final one or two steps take the path
+    // that masks it.
+    int t = t0;
+    for (; t + 2 < x.t_end; t += 2) {
+        tile_step<D, false>(t, x, st, sm, dma, sA, sB, pB, pA, qreg);
+        tile_step<D, false>(t + 1, x, st, sm, dma, sB, sA, pA, pB, qreg);
+    }
+    if (t + 1 < x.t_end) {
+        tile_step<D, true>(t, x, st, sm, dma, sA, sB, pB, pA, qreg);
+        tile_step<D, true>(t + 1, x, st, sm, dma, sB, sA, pA, pB, qreg);
+        pv_tile<D>(st.oacc, pB, sm.v[(t + 1 - t0) % 3], ql, g);
+    } else {
+        tile_step<D, true>(t, x, st, sm, dma, sA, sB, pB, pA, qreg);
+        pv_tile<D>(st.oacc, pA, sm.v[(t - t0) % 3], ql, g);
     }
 
-    // normalise and store: oacc[db][i] is channel db*32 + (i/4)*8 + g*4 + i%4
-    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-    const float inv = 1.0f / l_tot;
-    if (q_valid) {
-        uint16_t *orow = O + ((int64_t)bh * n_q + q_row) * D;
+    const float l_tot = pair_sum(st.l_run);
+
+    // st.oacc[db][i] is channel db*32 + (i/4)*8 + g*4 + i%4 of query ql
+    if (p.splits == 1) {
+        if (!q_valid) return;
+        const float inv = 1.0f / l_tot;
+        uint16_t *orow = p.O + ((int64_t)bh * n_q + q_row) * D;
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db)
+        for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
+            for (int rr = 0; rr < 4; ++rr) {
                 __bf16 vals[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) vals[e] = (__bf16)(oacc[db][r * 4 + e] * inv);
+                for (int e = 0; e < 4; ++e) vals[e] = (__bf16)(st.oacc[db][rr * 4 + e] * inv);
                 uint2 pk;
                 __builtin_memcpy(&pk, vals, 8);
-                *reinterpret_cast<uint2 *>(orow + db * 32 + r * 8 + g * 4) = pk;
+                *reinterpret_cast<uint2 *>(orow + db * 32 + rr * 8 + g * 4) = pk;
             }
+        return;
     }
+
+    // split-KV: publish this range's partial, the last arrival merges
+    const int row = wave * 32 + ql;
+    const int64_t slot = (int64_t)qtile_id * p.splits + split;
+    float *po = p.part_o + slot * C::BLOCK_M * D + (int64_t)row * D;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr)
+            *reinterpret_cast<float4 *>(po + db * 32 + rr * 8 + g * 4) =
+                make_float4(st.oacc[db][rr * 4], st.oacc[db][rr * 4 + 1], st.oacc[db][rr * 4 + 2],
+                            st.oacc[db][rr * 4 + 3]);
+    if (g == 0) {
+        float *pml = p.part_ml + (slot * C::BLOCK_M + row) * 2;
+        pml[0] = st.m_run;
+        pml[1] = l_tot;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __syncthreads();
+    if (tid == 0) {
+        const unsigned prev = __hip_atomic_fetch_add(p.counters + qtile_id, 1u, __ATOMIC_ACQ_REL,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+        s_last = (prev == (unsigned)p.splits - 1);
+    }
+    __syncthreads();
+    if (!s_last) return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+
+    // merge: O = sum_s 2^(m_s - m*) O_s / sum_s 2^(m_s - m*) l_s, split order
+    const int64_t base = (int64_t)qtile_id * p.splits;
+    for (int e = tid; e < C::BLOCK_M * D / 4; e += C::THREADS) {
+        const int rr = (e * 4) / D, d0 = (e * 4) % D;
+        const int qr = qt * C::BLOCK_M + rr;
+        if (qr >= n_q) continue;
+        float mstar = -INFINITY;
+        for (int s = 0; s < p.splits; ++s)
+            mstar = fmaxf(mstar, __hip_atomic_load(p.part_ml + ((base + s) * C::BLOCK_M + rr) * 2,
+                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+        float den = 0.f;
+        for (int s = 0; s < p.splits; ++s) {
+            const float *ml = p.part_ml + ((base + s) * C::BLOCK_M + rr) * 2;
+            const float ms = __hip_atomic_load(ml, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const float ls = __hip_atomic_load(ml + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const float wgt = __builtin_amdgcn_exp2f(ms - mstar);
+            const float *src = p.part_o + ((base + s) * C::BLOCK_M + rr) * D + d0;
+#pragma unroll
+            for (int e4 = 0; e4 < 4; ++e4)
+                acc[e4] = fmaf(wgt,
+                               __hip_atomic_load(src + e4, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT),
+                               acc[e4]);
+            den = fmaf(wgt, ls, den);
+        }
+        const float inv = 1.0f / den;
+        __bf16 vals[4] = {(__bf16)(acc[0] * inv), (__bf16)(acc[1] * inv), (__bf16)(acc[2] * inv),
+                          (__bf16)(acc[3] * inv)};
+        uint2 pk;
+        __builtin_memcpy(&pk, vals, 8);
+        *reinterpret_cast<uint2 *>(p.O + ((int64_t)bh * n_q + qr) * D + d0) = pk;
+    }
+    if (tid == 0)
+        __hip_atomic_store(p.counters + qtile_id, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ---------------------------------------------------------------- planning
+constexpr int kCus = 256;
+constexpr int kMaxSplits = 8;
+
+struct Plan {
+    int block_m, q_tiles, ntiles, splits, tiles_per_split;
+};
+
+// Pick the key-range split that minimises an estimate of the makespan:
+// rounds of resident workgroups x tiles per workgroup, plus the cost of
+// writing and merging fp32 partials.  One workgroup is resident per CU
+// (the LDS ring and VGPR budget are sized for that).
+Plan make_plan(int BH, int n_q, int N_kv, int d, bool can_split) {
+    Plan pl;
+    pl.block_m = d == 64 ? Cfg<64>::BLOCK_M : Cfg<128>::BLOCK_M;
+    const int bn = 64;
+    pl.q_tiles = (n_q + pl.block_m - 1) / pl.block_m;
+    pl.ntiles = (N_kv + bn - 1) / bn;
+    pl.splits = 1;
+    pl.tiles_per_split = pl.ntiles;
+    if (!can_split) return pl;
+    const double base = (double)BH * pl.q_tiles;
+    const double tile_flop = 4.0 * pl.block_m * bn * d;
+    const double cu_rate = 1.8e15 / kCus;  // sustained MFMA rate per CU
+    const double part_bw = 4.0e12;         // partial write + merge read
+    double best = 1e300;
+    const char *env = std::getenv("DFP_ATTN_SPLITS");
+    const int forced = env ? std::atoi(env) : 0;
+    for (int s = 1; s <= kMaxSplits && s <= pl.ntiles; ++s) {
+        const int tps = (pl.ntiles + s - 1) / s;
+        const int s_eff = (pl.ntiles + tps - 1) / tps;
+        if (s_eff != s) continue;
+        const double wgs = base * s;
+        double t = std::ceil(wgs / kCus) * tps * tile_flop / cu_rate;
+        if (s > 1) t += wgs * pl.block_m * d * 8.0 / part_bw;
+        if (forced > 0 ? s == forced : t < best * 0.98) {
+            best = t;
+            pl.splits = s;
+            pl.tiles_per_split = tps;
+        }
+        if (forced > 0 && s == forced) break;
+    }
+    return pl;
+}
+
+size_t counters_bytes(int BH, int q_tiles) {
+    return ((size_t)BH * q_tiles * sizeof(unsigned) + 255) / 256 * 256;
+}
+
+size_t need_bytes(int BH, int d, const Plan &pl) {
+    if (pl.splits <= 1) return 0;
+    const size_t slots = (size_t)BH * pl.q_tiles * pl.splits;
+    return counters_bytes(BH, pl.q_tiles) + slots * pl.block_m * d * sizeof(float) +
+           slots * pl.block_m * 2 * sizeof(float);
 }
 
 }  // namespace
 
+size_t dfp_attn_workspace_bytes(int B, int H, int n_q, int N_kv, int d) {
+    if (B <= 0 || H <= 0 || n_q <= 0 || N_kv <= 0 || (d != 64 && d != 128)) return 0;
+    const int BH = B * H;
+    return need_bytes(BH, d, make_plan(BH, n_q, N_kv, d, true));
+}
+
 dfp_status dfp_attn_bf16_launch(void *o, const void *q, const void *k, const void *vt, int BH,
-                                int n_q, int N_kv, int d, float scale, hipStream_t stream) {
-    const int q_tiles = (n_q + kBlockM - 1) / kBlockM;
-    const int64_t blocks = (int64_t)q_tiles * BH;
+                                int n_q, int N_kv, int d, float scale, void *ws, size_t ws_bytes,
+                                hipStream_t stream) {
+    Plan pl = make_plan(BH, n_q, N_kv, d, true);
+    if (pl.splits > 1 && (!ws || ws_bytes < need_bytes(BH, d, pl) ||
+                          (reinterpret_cast<uintptr_t>(ws) & 255u) != 0))
+        pl = make_plan(BH, n_q, N_kv, d, false);
+    const int64_t blocks = (int64_t)pl.q_tiles * BH * pl.splits;
     if (blocks > 0x7FFFFFFF) return DFP_ERR_UNSUPPORTED;
-    const int64_t ldv = dfp_v_ld(N_kv, DFP_BF16);
-    const float c_log2 = scale * 1.4426950408889634f;
+
+    Params p{};
+    p.Q = static_cast<const uint16_t *>(q);
+    p.K = static_cast<const uint16_t *>(k);
+    p.Vt = static_cast<const uint16_t *>(vt);
+    p.O = static_cast<uint16_t *>(o);
+    p.ldv = dfp_v_ld(N_kv, DFP_BF16);
+    p.n_q = n_q;
+    p.N_kv = N_kv;
+    p.c_log2 = scale * 1.4426950408889634f;
+    p.q_tiles = pl.q_tiles;
+    p.splits = pl.splits;
+    p.tiles_per_split = pl.tiles_per_split;
+    p.total_wg = (int)blocks;
+    if (pl.splits > 1) {
+        char *w = static_cast<char *>(ws);
+        p.counters = reinterpret_cast<unsigned *>(w);
+        w += counters_bytes(BH, pl.q_tiles);
+        const size_t slots = (size_t)BH * pl.q_tiles * pl.splits;
+        p.part_o = reinterpret_cast<float *>(w);
+        w += slots * pl.block_m * d * sizeof(float);
+        p.part_ml = reinterpret_cast<float *>(w);
+    }
     if (d == 64)
-        hipLaunchKernelGGL(attn_fwd_bf16<64>, dim3((unsigned)blocks), dim3(kThreads), 0, stream,
-                           static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
-                           static_cast<const uint16_t *>(vt), static_cast<uint16_t *>(o), n_q,
-                           N_kv, ldv, c_log2, q_tiles);
+        hipLaunchKernelGGL(attn_fwd_bf16<64>, dim3((unsigned)blocks), dim3(Cfg<64>::THREADS), 0,
+                           stream, p);
     else if (d == 128)
-        hipLaunchKernelGGL(attn_fwd_bf16<128>, dim3((unsigned)blocks), dim3(kThreads), 0, stream,
-                           static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
-                           static_cast<const uint16_t *>(vt), static_cast<uint16_t *>(o), n_q,
-                           N_kv, ldv, c_log2, q_tiles);
+        hipLaunchKernelGGL(attn_fwd_bf16<128>, dim3((unsigned)blocks), dim3(Cfg<128>::THREADS), 0,
+                           stream, p);
     else
         return DFP_ERR_UNSUPPORTED;
     return dfp::launch_status();

@@ -13,4 +13,5 @@ size_t dfp_attn_workspace_bytes(int B, int H, int n_q, int N_kv, int d);
 // bf16 MFMA attention launcher (attention_bf16.hip); arguments already
 // validated by dfp_patch_attention.
 dfp_status dfp_attn_bf16_launch(void *o, const void *q, const void *k, const void *vt, int BH,
-                                int n_q, int N_kv, int d, float scale, hipStream_t stream);
+                                int n_q, int N_kv, int d, float scale, void *ws, size_t ws_bytes,
+                                hipStream_t stream);

@@ -188,6 +188,16 @@ def patch_attention(o, q, k_buf, v_buf_t, scale: float | None = None, workspace=
     _check(st, "dfp_patch_attention")
 
 
+def attention_workspace(B: int, H: int, n_q: int, N_kv: int, d: int, device="cuda"):
+    """A zero-filled workspace that lets dfp_patch_attention split the key
+    range (None when the chosen plan does not split)."""
+    torch = _torch()
+    nbytes = workspace_bytes(OP_PATCH_ATTENTION, 0, 0, B, H, n_q, N_kv, d)
+    if nbytes == 0:
+        return None
+    return torch.zeros(nbytes, dtype=torch.uint8, device=device)
+
+
 def cfg_workspace(n_per_image: int, batch: int, device="cuda"):
     """A zero-filled workspace for dfp_cfg_step / dfp_relmae."""
     torch = _torch()

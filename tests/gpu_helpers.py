@@ -65,15 +65,28 @@ def land_buffer(level, x, p: int, kind: str):
     return k_buf, v_buf
 
 
-def run_patch(level, x, p: int, kind: str | None = None):
+def run_patch(level, x, p: int, kind: str | None = None, split_ok: bool = True):
+    """Patch p's attention on the GPU.  With split_ok the call gets a
+    workspace, so the library may split the key range (its default plan)."""
     kind = kind or level.dtype
     torch = torch_mod()
     k_buf, v_buf = land_buffer(level, x, p, kind)
     q = up(x.q_patch(p), kind)
     o = torch.empty_like(q)
-    dfp.patch_attention(o, q, k_buf, v_buf, 1.0 / level.d ** 0.5)
+    ws = (dfp.attention_workspace(level.B, level.H, level.n, level.N_kv, level.d)
+          if split_ok else None)
+    dfp.patch_attention(o, q, k_buf, v_buf, 1.0 / level.d ** 0.5, ws)
     torch.cuda.synchronize()
+    if ws is not None:
+        assert_counters_zero(ws, level.B * level.H, level.n)
     return down(o)
+
+
+def assert_counters_zero(ws, BH: int, n_q: int) -> None:
+    """The attention workspace starts with one uint32 arrival counter per
+    128-row query tile; every call must leave them at zero."""
+    n = BH * ((n_q + 127) // 128) * 4
+    assert int(ws[:n].sum().item()) == 0
 
 
 def sample_rows(n: int, BH: int, per_bh: int, seed: int):

@@ -108,6 +108,34 @@ def test_edge_shapes_every_element(kind, B, H, nq, N, d):
     assert torch.isnan(o_flat[numel:]).all()
 
 
+@pytest.mark.parametrize("splits", [2, 3, 8])
+@pytest.mark.parametrize("B,H,nq,N,d", [
+    (1, 2, 7, 1000, 64),      # ragged keys and queries, 8 key tiles
+    (2, 1, 130, 700, 128),    # d=128, 11 key tiles, two query tiles
+    (1, 2, 256, 4096, 64),    # even split
+])
+def test_forced_split_kv_every_element(monkeypatch, splits, B, H, nq, N, d):
+    G.require_gpu()
+    G.announce(f"attention split-KV x{splits} B{B} H{H} nq{nq} N{N} d{d}")
+    monkeypatch.setenv("DFP_ATTN_SPLITS", str(splits))
+    torch = G.torch_mod()
+    q, k, v = inputs.random_attention_arrays(B, H, nq, N, d, seed=splits * 1000 + N)
+    k_buf, v_buf = dfp.alloc_kv_buffer(B, H, N, d, torch.bfloat16)
+    dfp.kv_scatter(k_buf, v_buf, G.up(k, "bf16"), G.up(v, "bf16"), 0)
+    ws = dfp.attention_workspace(B, H, nq, N, d)
+    qd = G.up(q, "bf16")
+    o = torch.empty_like(qd)
+    dfp.patch_attention(o, qd, k_buf, v_buf, None, ws)
+    torch.cuda.synchronize()
+    first = G.down(o)
+    if ws is not None:
+        G.assert_counters_zero(ws, B * H, nq)
+    _check(first, oracle.attention(q, k, v, 1.0 / d ** 0.5), "bf16", f"split{splits}")
+    dfp.patch_attention(o, qd, k_buf, v_buf, None, ws)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(G.down(o), first)
+
+
 def test_constant_values_and_single_key_properties():
     G.require_gpu()
     G.announce("attention properties (V=1, N_kv=1) at c2a shape")
