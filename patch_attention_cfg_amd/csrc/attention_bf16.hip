@@ -31,12 +31,12 @@
 //     tile t+1's Q.K^T MFMAs, tile t-1's P.V MFMAs and tile t's softmax
 //     VALU work, interleaved in a fixed order (alternating accumulators,
 //     LDS operands read two MFMAs ahead).
-//   * Q is multiplied by scale * log2(e) once, as it enters registers, and
-//     each Q.K^T accumulator starts at -m (the reference max), so the MFMA
-//     emits scores in log2 units already relative to the reference.  The
-//     softmax VALU work per score is then one exp2, half a bf16 pack and
-//     half a dot2 -- the row sum is taken on the bf16-rounded
-//     probabilities the P.V product uses.
+//   * Softmax VALU work per score: one FMA (log2(e) * scale and the
+//     reference folded in), one exp2, half a bf16 pack and half a dot2 --
+//     the row sum is taken on the bf16-rounded probabilities the P.V
+//     product uses.  Q enters the MFMA unscaled: folding the scale into a
+//     bf16 copy of Q would add a rounding whose score error grows with
+//     the score's size.
 //   * The reference max is the first tile's row max and stays fixed while
 //     the scores stay below it + 12 (log2 units).  Every probability is
 //     bounded by the tile's row-sum share, so a share of at most 2^12
@@ -323,12 +323,10 @@ __device__ __forceinline__ bf16x8_t step_operand(int i, const uint16_t *Kn, cons
     return as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
 }
 
-// One step's basic block: s_next = K(t+1) Q^T - m (from Kn; Q is pre-scaled
-// by log2(e) * scale and the accumulator starts at -m, so the scores come
-// out in log2 units relative to the reference max), O^T += V(t-1)^T
-// P(t-1)^T (from Vp, p_prev), and the softmax of tile t: p = 2^s rounded
-// to bf16, with this tile's row-sum share (dot2 with ones) on the rounded
-// values accumulated in l_tile.
+// One step's basic block: s_next = K(t+1) Q^T (from Kn), O^T += V(t-1)^T
+// P(t-1)^T (from Vp, p_prev), and the softmax of tile t:
+// p = 2^(s * c - m) rounded to bf16, with this tile's row-sum share (dot2
+// with ones) on the rounded values accumulated in l_tile.
 // sched_barrier pins the interleaved order; the empty asm keeps the
 // probabilities computed here rather than sunk into the next step.
 template <int D>
@@ -338,11 +336,12 @@ __device__ __forceinline__ void region(f32x16_t (&s_next)[Cfg<D>::SB],
                                        const f32x16_t (&s_cur)[Cfg<D>::SB],
                                        const bf16x8_t (&p_prev)[Cfg<D>::SB][2],
                                        const uint16_t *Kn, const uint16_t *Vp,
-                                       const bf16x8_t (&qreg)[Cfg<D>::KC], const f32x16_t &negm,
+                                       const bf16x8_t (&qreg)[Cfg<D>::KC], float c, float m_run,
                                        int ko, int vo) {
     using C = Cfg<D>;
     using S = Steps<D>;
     const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+    const f32x16_t zero = {};
     // opaque per step: keeps the compiler from hoisting one address
     // register per stage out of the unrolled loop
     asm volatile("" : "+v"(ko), "+v"(vo));
@@ -356,7 +355,7 @@ __device__ __forceinline__ void region(f32x16_t (&s_next)[Cfg<D>::SB],
         if (S::is_qk(i)) {
             const int q = S::idx(i), kc = q / C::SB, sb = q % C::SB;
             s_next[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[kc],
-                                                                  kc == 0 ? negm : s_next[sb],
+                                                                  kc == 0 ? zero : s_next[sb],
                                                                   0, 0, 0);
         } else {
             const int v = S::idx(i), kc2 = v / C::DB, db = v % C::DB;
@@ -367,8 +366,8 @@ __device__ __forceinline__ void region(f32x16_t (&s_next)[Cfg<D>::SB],
             const int k = i / S::CHUNK_EVERY;      // chunk: two consecutive scores
             const int sb = k / 8, h = (k % 8) / 4, j = (k % 4) * 2;
             bf16x2_t pr;
-            pr[0] = (__bf16)__builtin_amdgcn_exp2f(s_cur[sb][h * 8 + j]);
-            pr[1] = (__bf16)__builtin_amdgcn_exp2f(s_cur[sb][h * 8 + j + 1]);
+            pr[0] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s_cur[sb][h * 8 + j], c, -m_run));
+            pr[1] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s_cur[sb][h * 8 + j + 1], c, -m_run));
             l_tile = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_tile, false);
             p_cur[sb][h][j] = pr[0];
             p_cur[sb][h][j + 1] = pr[1];
@@ -384,27 +383,27 @@ __device__ __forceinline__ void region(f32x16_t (&s_next)[Cfg<D>::SB],
 template <int D>
 struct State {
     f32x16_t oacc[Cfg<D>::DB];
-    f32x16_t negm;   // -m_run in every element: the Q.K^T accumulator's start
-    float m_run;     // reference max, log2 units (scores * log2(e) * scale)
-    float l_run;     // this lane's share of the running sum
+    float m_run;   // reference max, log2 units (scores * log2(e) * scale)
+    float l_run;   // this lane's share of the running sum
 };
 
 // Rare path: some probability of tile t exceeded kMaxTileSum (the scores
-// outgrew the reference).  Raise the reference to the tile max, rescale O
-// and l to it, recompute the tile's probabilities, and shift the next
-// tile's scores (computed against the old reference) by the same amount.
+// outgrew the reference).  Raise the reference to the tile max (never
+// lower it), rescale O and l to it and recompute the tile's
+// probabilities.
 template <int D>
 __device__ __forceinline__ void raise_reference(
-    State<D> &st, f32x16_t (&s_cur)[Cfg<D>::SB], f32x16_t (&s_next)[Cfg<D>::SB],
-    bf16x8_t (&p_cur)[Cfg<D>::SB][2], float &l_tile) {
+    State<D> &st, const f32x16_t (&s_cur)[Cfg<D>::SB], bf16x8_t (&p_cur)[Cfg<D>::SB][2],
+    float &l_tile, float c) {
     using C = Cfg<D>;
-    float mx = s_cur[0][0];
+    float mx = -INFINITY;
 #pragma unroll
     for (int sb = 0; sb < C::SB; ++sb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s_cur[sb][i]);
-    mx = pair_max(mx);
+    mx = pair_max(mx) * c - st.m_run;   // tile max relative to the reference
     const float delta = mx > 0.f ? mx : 0.f;
+    st.m_run += delta;
     const float alpha = __builtin_amdgcn_exp2f(-delta);
 #pragma unroll
     for (int db = 0; db < C::DB; ++db)
@@ -420,19 +419,12 @@ __device__ __forceinline__ void raise_reference(
 #pragma unroll
             for (int j = 0; j < 8; j += 2) {
                 bf16x2_t pr;
-                pr[0] = (__bf16)__builtin_amdgcn_exp2f(s_cur[sb][h * 8 + j] - delta);
-                pr[1] = (__bf16)__builtin_amdgcn_exp2f(s_cur[sb][h * 8 + j + 1] - delta);
+                pr[0] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s_cur[sb][h * 8 + j], c, -st.m_run));
+                pr[1] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s_cur[sb][h * 8 + j + 1], c, -st.m_run));
                 l_tile = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_tile, false);
                 p_cur[sb][h][j] = pr[0];
                 p_cur[sb][h][j + 1] = pr[1];
             }
-#pragma unroll
-    for (int sb = 0; sb < C::SB; ++sb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) s_next[sb][i] -= delta;
-    st.m_run += delta;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) st.negm[i] = -st.m_run;
 }
 
 template <int D>
@@ -446,6 +438,7 @@ struct Ctx {
     const uint16_t *Vh;
     int64_t ldv;
     int N_kv, t_begin, t_end;
+    float c;   // log2(e) * scale
     int tid, wave, ql, g;
 };
 
@@ -477,11 +470,11 @@ __device__ __forceinline__ void tile_step(int t, const Ctx &x, State<D> &st, Sme
     }
 
     float l_tile = 0.f;
-    region<D>(s_next, st.oacc, p_cur, l_tile, s_cur, p_prev, sm.k[s1], sm.v[s2], qreg, st.negm,
-              x.ql * C::K_LD + x.g * 8, x.ql * C::V_LD + x.g * 4);
+    region<D>(s_next, st.oacc, p_cur, l_tile, s_cur, p_prev, sm.k[s1], sm.v[s2], qreg, x.c,
+              st.m_run, x.ql * C::K_LD + x.g * 8, x.ql * C::V_LD + x.g * 4);
     // each probability is at most the tile's row-sum share, so a share
     // within kMaxTileSum proves none outgrew the reference
-    if (__any(!(l_tile <= kMaxTileSum))) raise_reference<D>(st, s_cur, s_next, p_cur, l_tile);
+    if (__any(!(l_tile <= kMaxTileSum))) raise_reference<D>(st, s_cur, p_cur, l_tile, x.c);
     st.l_run += l_tile;
 
     wait_dma();                       // this wave's K(t+2), V(t) copies have landed
@@ -530,19 +523,17 @@ __global__ __launch_bounds__(Cfg<D>::THREADS, Cfg<D>::WG_PER_CU) void attn_fwd_b
     x.wave = wave;
     x.ql = ql;
     x.g = g;
+    x.c = p.c_log2;
 
     // Q^T as the B operand: lane (ql, g) holds d = kc*16 + g*8 .. +7 of its
-    // query, pre-multiplied by scale * log2(e) (rounded to bf16) so the
-    // scores come out of the MFMA in log2 units.
+    // query.  Q enters the product unscaled (exact); scale * log2(e) is
+    // applied to the fp32 scores.
     bf16x8_t qreg[C::KC];
 #pragma unroll
-    for (int kc = 0; kc < C::KC; ++kc) {
-        const bf16x8_t raw = as_bf16x8(q_valid ? *reinterpret_cast<const uint4 *>(
-                                                     Qh + (int64_t)q_row * D + kc * 16 + g * 8)
-                                               : zero4());
-#pragma unroll
-        for (int j = 0; j < 8; ++j) qreg[kc][j] = (__bf16)((float)raw[j] * p.c_log2);
-    }
+    for (int kc = 0; kc < C::KC; ++kc)
+        qreg[kc] = as_bf16x8(q_valid ? *reinterpret_cast<const uint4 *>(
+                                           Qh + (int64_t)q_row * D + kc * 16 + g * 8)
+                                     : zero4());
 
     State<D> st;
 #pragma unroll
@@ -580,13 +571,7 @@ __global__ __launch_bounds__(Cfg<D>::THREADS, Cfg<D>::WG_PER_CU) void attn_fwd_b
                 if (key >= nvalid) sA[sb][i] = -INFINITY;
                 mx = fmaxf(mx, sA[sb][i]);
             }
-        st.m_run = pair_max(mx);
-#pragma unroll
-        for (int sb = 0; sb < C::SB; ++sb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) sA[sb][i] -= st.m_run;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) st.negm[i] = -st.m_run;
+        st.m_run = pair_max(mx) * p.c_log2;
     }
 #pragma unroll
     for (int sb = 0; sb < C::SB; ++sb)

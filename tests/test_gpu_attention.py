@@ -181,3 +181,33 @@ def test_deterministic_bitwise():
     a = G.run_patch(level, x, 0)
     b = G.run_patch(level, x, 0)
     np.testing.assert_array_equal(a, b)
+
+
+@pytest.mark.parametrize("splits", [1, 3])
+@pytest.mark.parametrize("B,H,nq,N,d,growth", [
+    (1, 2, 130, 2000, 64, 6.0),     # later tiles outrun the first tile's max many times
+    (2, 1, 257, 1500, 128, 6.0),
+    (1, 2, 64, 700, 64, 40.0),      # one huge jump: probabilities of early keys underflow
+    (1, 1, 96, 900, 64, -0.9),      # shrinking scores: the first tile keeps the max
+])
+def test_scores_that_outgrow_the_first_tile(monkeypatch, splits, B, H, nq, N, d, growth):
+    """Keys scaled by a ramp along the sequence make later tiles' scores far
+    exceed the first tile's, which the kernel's reference max must follow
+    (and a falling ramp must leave it alone)."""
+    G.require_gpu()
+    G.announce(f"attention growing scores x{growth} splits{splits} B{B} H{H} nq{nq} N{N} d{d}")
+    monkeypatch.setenv("DFP_ATTN_SPLITS", str(splits))
+    torch = G.torch_mod()
+    q, k, v = inputs.random_attention_arrays(B, H, nq, N, d, seed=int(abs(growth) * 10) + N)
+    ramp = (1.0 + growth * np.arange(N, dtype=np.float32) / N)[None, None, :, None]
+    k = inputs.round_bf16(k * ramp)
+    k_buf, v_buf = dfp.alloc_kv_buffer(B, H, N, d, torch.bfloat16)
+    dfp.kv_scatter(k_buf, v_buf, G.up(k, "bf16"), G.up(v, "bf16"), 0)
+    ws = dfp.attention_workspace(B, H, nq, N, d)
+    qd = G.up(q, "bf16")
+    o = torch.empty_like(qd)
+    dfp.patch_attention(o, qd, k_buf, v_buf, None, ws)
+    torch.cuda.synchronize()
+    got = G.down(o)
+    assert np.isfinite(got).all()
+    _check(got, oracle.attention(q, k, v, 1.0 / d ** 0.5), "bf16", f"growth {growth}")
