@@ -20,11 +20,15 @@
 //     in the B-operand layout of O^T = V^T P^T: no LDS round trip and no
 //     transpose for P.
 //   * K and V^T tiles move from HBM straight into LDS with
-//     global_load_lds_dwordx4 (no VGPR staging).  V is stored transposed in
-//     HBM ([d][token]) so V^T tiles feed the A operand of O^T = V^T P^T with
-//     plain 8-byte LDS reads.  LDS rows carry one 16-byte pad slot, so the
-//     32 rows an operand read touches hit distinct banks; lanes whose
-//     16-byte slot is a pad fetch an in-row chunk that is never read.
+//     buffer_load_dwordx4 ... lds (no VGPR staging).  V is stored
+//     transposed in HBM ([d][token]) so V^T tiles feed the A operand of
+//     O^T = V^T P^T directly.  The lanes of the Q.K^T A operand load K rows
+//     in a permuted order (key_row) that leaves each lane's probabilities
+//     on 8 consecutive keys, so every MFMA operand is one 16-byte LDS read.
+//     LDS rows carry one 16-byte pad slot (a 144-byte pitch at 64 keys or
+//     64 channels), so each 16-lane group of a 16-byte read covers all 64
+//     banks once; lanes whose DMA slot is a pad fetch an in-row chunk that
+//     is never read.
 //   * Three LDS stages per operand: tile t+3's K and tile t+1's V are in
 //     flight while step t computes, one barrier per step.
 //   * Each step is one basic block holding three independent streams:
@@ -91,22 +95,34 @@ struct Cfg {
     static constexpr int THREADS = NW * dfp::kWave;
     static constexpr int BLOCK_M = NW * 32;      // query rows per workgroup
     static constexpr int BN = 64;                // keys per tile
-    static constexpr int K_SLOTS = D / 8 + 1;    // 16-byte slots per K row in LDS (one pad)
-    static constexpr int V_SLOTS = BN / 8 + 1;   // 16-byte slots per V^T row in LDS (one pad)
-    static constexpr int K_LD = K_SLOTS * 8;     // bf16 per K row in LDS
-    static constexpr int V_LD = V_SLOTS * 8;     // bf16 per V^T row in LDS
-    static constexpr int K_TILE = BN * K_LD;
-    static constexpr int V_TILE = D * V_LD;
-    static constexpr int K_DMA = BN * K_SLOTS / 64;   // 64-lane DMA instructions per K tile
-    static constexpr int V_DMA = D * V_SLOTS / 64;    // ... per V^T tile
-    static constexpr int K_DMA_W = (K_DMA + NW - 1) / NW;  // per wavefront (upper bound)
-    static constexpr int V_DMA_W = (V_DMA + NW - 1) / NW;
-    static constexpr int STAGES = 3;
+    static constexpr int K_ROW = D * 2;          // bytes per K row in LDS (no padding)
+    static constexpr int V_ROW = BN * 2;         // bytes per V^T row in LDS
+    static constexpr int K_SLOTS = K_ROW / 16;   // 16-byte slots per row
+    static constexpr int V_SLOTS = V_ROW / 16;
+    static constexpr int K_TILE = BN * K_ROW;    // bytes per stage
+    static constexpr int V_TILE = D * V_ROW;
+    static constexpr int K_DMA = K_TILE / 1024;  // 64-lane x 16-byte copies per tile
+    static constexpr int V_DMA = V_TILE / 1024;
+    static constexpr int DMA_W = (K_DMA + V_DMA) / NW;   // copies per wavefront per step
+    static constexpr int K_DMA_W = K_DMA / NW;           // ... of which K
+    static constexpr int STAGES = 4;
     static constexpr int SB = BN / 32;           // 32-key score blocks per tile
     static constexpr int DB = D / 32;            // 32-channel output blocks
     static constexpr int KC = D / 16;            // K=16 slices of the Q.K^T product
-    static_assert(BN * K_SLOTS % 64 == 0 && D * V_SLOTS % 64 == 0, "whole DMA instructions");
+    static constexpr int KC2 = BN / 16;          // K=16 slices of the P.V product
+    static_assert(K_DMA % NW == 0 && V_DMA % NW == 0, "every wavefront issues as many copies");
+    static_assert(DMA_W == 4, "the end-of-step wait keeps exactly this step's copies in flight");
 };
+
+// LDS swizzle: 16-byte slot s of row r is stored at slot s ^ swz(r).  A
+// 16-byte read of one slot by 16 consecutive lanes on 16 consecutive rows
+// (the MFMA operand pattern) then touches every one of the 64 banks once:
+// with 128-byte rows two rows share a 256-byte bank sweep and swz spreads
+// the pairs; with 256-byte rows swz alone must separate 16 rows.
+template <int ROW_BYTES>
+__device__ __forceinline__ int swz(int r) {
+    return ROW_BYTES == 128 ? (r >> 1) & 7 : r & 15;
+}
 
 __device__ __forceinline__ uint4 zero4() { return make_uint4(0u, 0u, 0u, 0u); }
 
@@ -142,7 +158,8 @@ __device__ __forceinline__ float pair_sum(float x) {
 typedef int int32x4_t __attribute__((ext_vector_type(4)));
 
 // A raw buffer resource (V#) covering `bytes` bytes from `base`; accesses at
-// or past the end read as zero instead of faulting.  Built from uniform
+// or past the end read as zero instead of faulting, and a zero size makes
+// every access read zero without touching memory.  Built from uniform
 // values, so it lives in scalar registers.
 __device__ __forceinline__ int32x4_t buffer_rsrc(const void *base, uint32_t bytes) {
     const uint64_t a = reinterpret_cast<uint64_t>(base);
@@ -174,120 +191,167 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
 }
 
 // Wait until every copy this wavefront issued has landed in LDS.
-__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void wait_dma_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Wait until at most the 4 copies issued last are still in flight (this
+// step's own; every earlier copy has landed).
+__device__ __forceinline__ void wait_dma_keep4() {
+    asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+}
 
 // Direct HBM -> LDS copies of one K tile (rows [j0, j0+64)) and one V^T tile
 // (columns [j0, j0+64)).  Copy instruction i of a tile writes LDS slots
-// [64 i, 64 i + 64): slot s = 64 i + lane is row s / SLOTS, 16-byte chunk
-// s % SLOTS of the padded tile; a pad chunk fetches the row's chunk 0 (never
-// read).  Each wavefront issues instructions w, w + NW, ...  The buffer
-// resource starts at the tile, so every lane's byte offset is fixed for the
-// kernel.  K rows past N_kv fall outside the resource and read as zero
-// (their scores are masked anyway); V^T reads past a row's end land in the
-// next row or read as zero, and keys >= N_kv are zeroed in LDS afterwards.
+// [64 i, 64 i + 64): slot z = 64 i + lane is row z / SLOTS, stored slot
+// z % SLOTS, which holds 16-byte chunk (z % SLOTS) ^ swz(row) of that row.
+// Wavefront w issues instructions w, w + NW, ... of the K tile, then of the
+// V^T tile (DMA_W in all).  Every lane's byte offset from the tile start is
+// fixed for the kernel; the buffer resource starts at the tile.  K rows
+// past N_kv fall outside the resource and read as zero (their scores are
+// masked anyway); V^T reads past a row's end land in the next row or read
+// as zero, and keys >= N_kv are zeroed in LDS afterwards.
 template <int D>
 struct TileDma {
     using C = Cfg<D>;
-    uint32_t k_off[C::K_DMA_W];   // byte offset of this lane's K chunk within a tile
-    uint32_t v_off[C::V_DMA_W];   // byte offset of this lane's V^T chunk (key 0 of the tile)
+    uint32_t off[C::DMA_W];   // byte offset of this lane's chunk within a tile
     int wave;
 
     __device__ __forceinline__ void init(int wv, int lane, int64_t ldv) {
         wave = __builtin_amdgcn_readfirstlane(wv);
 #pragma unroll
-        for (int k = 0; k < C::K_DMA_W; ++k) {
-            const int s = (wave + k * C::NW) * 64 + lane;
-            const int row = s / C::K_SLOTS;
-            int col = s % C::K_SLOTS;
-            if (col == C::K_SLOTS - 1) col = 0;
-            k_off[k] = (uint32_t)(row * D * 2 + col * 16);
-        }
-#pragma unroll
-        for (int k = 0; k < C::V_DMA_W; ++k) {
-            const int s = (wave + k * C::NW) * 64 + lane;
-            const int row = s / C::V_SLOTS;
-            int col = s % C::V_SLOTS;
-            if (col == C::V_SLOTS - 1) col = 0;
-            v_off[k] = (uint32_t)(row * ldv * 2 + col * 16);
+        for (int e = 0; e < C::DMA_W; ++e) {
+            if (e < C::K_DMA_W) {
+                const int z = (wave + e * C::NW) * 64 + lane;
+                const int row = z / C::K_SLOTS, slot = (z % C::K_SLOTS) ^ swz<C::K_ROW>(row);
+                off[e] = (uint32_t)(row * C::K_ROW + slot * 16);
+            } else {
+                const int z = (wave + (e - C::K_DMA_W) * C::NW) * 64 + lane;
+                const int row = z / C::V_SLOTS, slot = (z % C::V_SLOTS) ^ swz<C::V_ROW>(row);
+                off[e] = (uint32_t)(row * ldv * 2 + slot * 16);
+            }
         }
     }
 
-    __device__ __forceinline__ void load_k(const uint16_t *Kh, int j0, int N_kv,
-                                           const uint16_t *Ks) const {
-        const int32x4_t rs = buffer_rsrc(Kh + (int64_t)j0 * D, (uint32_t)(N_kv - j0) * D * 2);
-        const uint32_t lds = lds_addr(Ks);
-#pragma unroll
-        for (int k = 0; k < C::K_DMA_W; ++k) {
-            const int i = wave + k * C::NW;
-            if (C::K_DMA % C::NW != 0 && i >= C::K_DMA) break;   // wave-uniform
-            lds_dma16(rs, k_off[k], lds + i * 1024);
-        }
-    }
-
-    __device__ __forceinline__ void load_v(const uint16_t *Vh, int j0, int64_t ldv,
-                                           const uint16_t *Vs) const {
-        const int32x4_t rs = buffer_rsrc(Vh + j0, (uint32_t)((int64_t)D * ldv - j0) * 2);
-        const uint32_t lds = lds_addr(Vs);
-#pragma unroll
-        for (int k = 0; k < C::V_DMA_W; ++k) {
-            const int i = wave + k * C::NW;
-            if (C::V_DMA % C::NW != 0 && i >= C::V_DMA) break;   // wave-uniform
-            lds_dma16(rs, v_off[k], lds + i * 1024);
-        }
+    // LDS byte address written by copy e of this wavefront.
+    __device__ __forceinline__ uint32_t lds_of(int e, uint32_t k_stage, uint32_t v_stage) const {
+        return e < C::K_DMA_W ? k_stage + (uint32_t)(wave + e * C::NW) * 1024u
+                              : v_stage + (uint32_t)(wave + (e - C::K_DMA_W) * C::NW) * 1024u;
     }
 };
 
+// Per-step copy job: the buffer resources and LDS stages of the K tile and
+// the V^T tile one step's copies fill.  A tile outside the workgroup's key
+// range gets an empty resource (its copies read zeros, touch no memory).
+struct CopyJob {
+    int32x4_t rk, rv;
+    uint32_t lk, lv;
+};
+
+template <int D>
+__device__ __forceinline__ CopyJob copy_job(const uint16_t *Kh, const uint16_t *Vh, int64_t ldv,
+                                            int N_kv, int t_end, int tk, int tv, uint32_t lk,
+                                            uint32_t lv) {
+    using C = Cfg<D>;
+    const int jk = tk * C::BN, jv = tv * C::BN;
+    CopyJob j;
+    j.rk = buffer_rsrc(Kh + (int64_t)jk * D, tk < t_end ? (uint32_t)(N_kv - jk) * D * 2 : 0u);
+    j.rv = buffer_rsrc(Vh + jv, tv < t_end ? (uint32_t)((int64_t)D * ldv - jv) * 2 : 0u);
+    j.lk = lk;
+    j.lv = lv;
+    return j;
+}
+
+template <int D>
+__device__ __forceinline__ void issue_copy(const TileDma<D> &dma, const CopyJob &j, int e) {
+    lds_dma16(e < Cfg<D>::K_DMA_W ? j.rk : j.rv, dma.off[e], dma.lds_of(e, j.lk, j.lv));
+}
+
 // Zero V^T columns of keys >= N_kv in a landed tile (ragged last tile).
 template <int D>
-__device__ __forceinline__ void zero_tail_v(uint16_t *Vs, int j0, int N_kv, int tid) {
+__device__ __forceinline__ void zero_tail_v(char *Vs, int j0, int N_kv, int tid) {
     using C = Cfg<D>;
     const int first = N_kv - j0;   // first masked key within the tile (1..63)
     for (int e = tid; e < D * C::BN; e += C::THREADS) {
         const int row = e / C::BN, kk = e % C::BN;
-        if (kk >= first) Vs[row * C::V_LD + kk] = 0;
+        if (kk >= first) {
+            const int slot = (kk / 8) ^ swz<C::V_ROW>(row);
+            *reinterpret_cast<uint16_t *>(Vs + row * C::V_ROW + slot * 16 + (kk % 8) * 2) = 0;
+        }
     }
+}
+
+// Key order inside a 32-key score block.  The MFMA leaves accumulator
+// element i of lane (ql, g) in block row (i/4)*8 + g*4 + i%4; the A-operand
+// lane for block row r loads K row key_row(r), which swaps bits 2 and 3 of
+// r.  Element i then holds key (i/8)*16 + g*8 + ((i/4)%2)*4 + i%4, so each
+// half (i < 8, i >= 8) of a lane's scores covers 8 consecutive keys: the
+// matching V^T operand of P.V is one 16-byte LDS read.
+__device__ __forceinline__ int key_row(int r) {
+    return (r & ~12) | ((r >> 1) & 4) | ((r << 1) & 8);
+}
+__device__ __forceinline__ int score_key(int i, int g) {
+    return (i >> 3) * 16 + g * 8 + ((i >> 2) & 1) * 4 + (i & 3);
+}
+
+// Per-lane LDS byte offsets of the MFMA operands inside a stage: K slice kc
+// of key row key_row(ql) (+ sb*32 rows, a constant), V^T slice kc2 of
+// channel ql (+ db*32 rows).  The swizzle depends only on the row modulo 32,
+// so one offset per slice serves every block.
+template <int D>
+struct OperandOffsets {
+    using C = Cfg<D>;
+    uint32_t k[C::KC];
+    uint32_t v[C::KC2];
+    __device__ __forceinline__ void init(int ql, int g) {
+        const int kr = key_row(ql);
+#pragma unroll
+        for (int kc = 0; kc < C::KC; ++kc)
+            k[kc] = (uint32_t)(kr * C::K_ROW + (((kc * 2 + g) ^ swz<C::K_ROW>(kr)) * 16));
+#pragma unroll
+        for (int kc2 = 0; kc2 < C::KC2; ++kc2)
+            v[kc2] = (uint32_t)(ql * C::V_ROW + (((kc2 * 2 + g) ^ swz<C::V_ROW>(ql)) * 16));
+    }
+};
+
+template <int D>
+__device__ __forceinline__ bf16x8_t k_operand(const char *Ks, const OperandOffsets<D> &oo, int kc,
+                                              int sb) {
+    return *reinterpret_cast<const bf16x8_t *>(Ks + oo.k[kc] + sb * 32 * Cfg<D>::K_ROW);
+}
+
+template <int D>
+__device__ __forceinline__ bf16x8_t v_operand(const char *Vs, const OperandOffsets<D> &oo, int kc2,
+                                              int db) {
+    return *reinterpret_cast<const bf16x8_t *>(Vs + oo.v[kc2] + db * 32 * Cfg<D>::V_ROW);
 }
 
 // S^T = K Q^T for one tile: s[sb][i] is the score of key
-// sb*32 + (i/4)*8 + g*4 + i%4 (tile-relative) against query ql.
+// sb*32 + score_key(i, g) (tile-relative) against query ql.
 template <int D>
-__device__ __forceinline__ void qk_tile(f32x16_t (&s)[Cfg<D>::SB], const uint16_t *Ks,
-                                        const bf16x8_t (&qreg)[Cfg<D>::KC], int ql, int g) {
+__device__ __forceinline__ void qk_tile(f32x16_t (&s)[Cfg<D>::SB], const char *Ks,
+                                        const bf16x8_t (&qreg)[Cfg<D>::KC],
+                                        const OperandOffsets<D> &oo) {
     using C = Cfg<D>;
+    const f32x16_t zero = {};
 #pragma unroll
     for (int kc = 0; kc < C::KC; ++kc)
 #pragma unroll
-        for (int sb = 0; sb < C::SB; ++sb) {
-            const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(
-                Ks + (sb * 32 + ql) * C::K_LD + kc * 16 + g * 8);
-            if (kc == 0) {
-                const f32x16_t zero = {};
-                s[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[0], zero, 0, 0, 0);
-            } else {
-                s[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[kc], s[sb], 0, 0, 0);
-            }
-        }
+        for (int sb = 0; sb < C::SB; ++sb)
+            s[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_operand<D>(Ks, oo, kc, sb), qreg[kc],
+                                                            kc == 0 ? zero : s[sb], 0, 0, 0);
 }
 
 // O^T += V^T P^T over one tile's 16-key slices.  MFMA k index g*8 + j of
-// slice kc2 is key kc2*16 + (j/4)*8 + g*4 + j%4 on both operands.
+// slice kc2 is key kc2*16 + g*8 + j on both operands.
 template <int D>
 __device__ __forceinline__ void pv_tile(f32x16_t (&oacc)[Cfg<D>::DB],
-                                        const bf16x8_t (&pm)[Cfg<D>::SB][2], const uint16_t *Vs,
-                                        int ql, int g) {
+                                        const bf16x8_t (&pm)[Cfg<D>::SB][2], const char *Vs,
+                                        const OperandOffsets<D> &oo) {
     using C = Cfg<D>;
 #pragma unroll
-    for (int kc2 = 0; kc2 < C::BN / 16; ++kc2) {
+    for (int kc2 = 0; kc2 < C::KC2; ++kc2)
 #pragma unroll
-        for (int db = 0; db < C::DB; ++db) {
-            const uint16_t *vrow = Vs + (db * 32 + ql) * C::V_LD + kc2 * 16 + g * 4;
-            const uint2 lo = *reinterpret_cast<const uint2 *>(vrow);
-            const uint2 hi = *reinterpret_cast<const uint2 *>(vrow + 8);
-            const bf16x8_t a = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
-            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pm[kc2 >> 1][kc2 & 1], oacc[db],
-                                                                0, 0, 0);
-        }
-    }
+        for (int db = 0; db < C::DB; ++db)
+            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                v_operand<D>(Vs, oo, kc2, db), pm[kc2 >> 1][kc2 & 1], oacc[db], 0, 0, 0);
 }
 
 // The fixed order of one step's MFMAs: pairs of Q.K^T MFMAs alternate with
@@ -296,61 +360,61 @@ template <int D>
 struct Steps {
     using C = Cfg<D>;
     static constexpr int NQ = C::SB * C::KC;             // Q.K^T MFMAs per tile
-    static constexpr int NV = (C::BN / 16) * C::DB;      // P.V MFMAs per tile
+    static constexpr int NV = C::KC2 * C::DB;            // P.V MFMAs per tile
     static constexpr int N = NQ + NV;
     static_assert(NQ == NV, "steps alternate pairs of Q.K^T and P.V MFMAs");
+    static_assert(N >= 4, "a step's first two operands are Q.K^T operands");
     static constexpr bool is_qk(int i) { return (i & 3) < 2; }
     static constexpr int idx(int i) { return (i >> 2) * 2 + (i & 1); }
     static constexpr int CHUNKS = C::SB * 8;             // pairs of probabilities
     static constexpr int CHUNK_EVERY = N / CHUNKS;       // MFMAs per softmax chunk
+    // copy e of the step is issued after MFMA copy_at(e), spread evenly
+    static constexpr int copy_at(int e) { return e * (N / C::DMA_W) + 1; }
 };
 
-// ko = ql*K_LD + g*8 and vo = ql*V_LD + g*4 are the lane's element offsets
-// inside a K / V^T stage; everything else in the address is a constant.
 template <int D>
-__device__ __forceinline__ bf16x8_t step_operand(int i, const uint16_t *Kn, const uint16_t *Vp,
-                                                 int ko, int vo) {
+__device__ __forceinline__ bf16x8_t step_operand(int i, const char *Kn, const char *Vp,
+                                                 const OperandOffsets<D> &oo) {
     using C = Cfg<D>;
     using S = Steps<D>;
     if (S::is_qk(i)) {
-        const int q = S::idx(i), kc = q / C::SB, sb = q % C::SB;
-        return *reinterpret_cast<const bf16x8_t *>(Kn + ko + sb * 32 * C::K_LD + kc * 16);
+        const int q = S::idx(i);
+        return k_operand<D>(Kn, oo, q / C::SB, q % C::SB);
     }
-    const int v = S::idx(i), kc2 = v / C::DB, db = v % C::DB;
-    const uint16_t *vrow = Vp + vo + db * 32 * C::V_LD + kc2 * 16;
-    const uint2 lo = *reinterpret_cast<const uint2 *>(vrow);
-    const uint2 hi = *reinterpret_cast<const uint2 *>(vrow + 8);
-    return as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+    const int v = S::idx(i);
+    return v_operand<D>(Vp, oo, v / C::DB, v % C::DB);
 }
 
 // One step's basic block: s_next = K(t+1) Q^T (from Kn), O^T += V(t-1)^T
 // P(t-1)^T (from Vp, p_prev), and the softmax of tile t:
 // p = 2^(s * c - m) rounded to bf16, with this tile's row-sum share (dot2
-// with ones) on the rounded values accumulated in l_tile.
-// sched_barrier pins the interleaved order; the empty asm keeps the
-// probabilities computed here rather than sunk into the next step.
+// with ones) on the rounded values accumulated in l_tile.  The step's
+// DMA_W copies are issued between its MFMAs, so the copy engine is fed
+// evenly instead of in a burst.  Operands are read two MFMAs ahead; `carry`
+// brings in this step's first two (read by the previous step) and takes
+// out the next step's first two, read from Kn_next (K(t+2), already
+// published) so they are in flight across the step boundary.
 template <int D>
 __device__ __forceinline__ void region(f32x16_t (&s_next)[Cfg<D>::SB],
                                        f32x16_t (&oacc)[Cfg<D>::DB],
                                        bf16x8_t (&p_cur)[Cfg<D>::SB][2], float &l_tile,
                                        const f32x16_t (&s_cur)[Cfg<D>::SB],
                                        const bf16x8_t (&p_prev)[Cfg<D>::SB][2],
-                                       const uint16_t *Kn, const uint16_t *Vp,
-                                       const bf16x8_t (&qreg)[Cfg<D>::KC], float c, float m_run,
-                                       int ko, int vo) {
+                                       const char *Kn, const char *Vp, const char *Kn_next,
+                                       bf16x8_t (&carry)[2], const bf16x8_t (&qreg)[Cfg<D>::KC],
+                                       float c, float m_run, const OperandOffsets<D> &oo,
+                                       const TileDma<D> &dma, const CopyJob &job) {
     using C = Cfg<D>;
     using S = Steps<D>;
     const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
     const f32x16_t zero = {};
-    // opaque per step: keeps the compiler from hoisting one address
-    // register per stage out of the unrolled loop
-    asm volatile("" : "+v"(ko), "+v"(vo));
     bf16x8_t ring[3];
-    ring[0] = step_operand<D>(0, Kn, Vp, ko, vo);
-    ring[1] = step_operand<D>(1, Kn, Vp, ko, vo);
+    ring[0] = carry[0];
+    ring[1] = carry[1];
 #pragma unroll
     for (int i = 0; i < S::N; ++i) {
-        if (i + 2 < S::N) ring[(i + 2) % 3] = step_operand<D>(i + 2, Kn, Vp, ko, vo);
+        ring[(i + 2) % 3] = i + 2 < S::N ? step_operand<D>(i + 2, Kn, Vp, oo)
+                                         : step_operand<D>(i + 2 - S::N, Kn_next, Vp, oo);
         const bf16x8_t a = ring[i % 3];
         if (S::is_qk(i)) {
             const int q = S::idx(i), kc = q / C::SB, sb = q % C::SB;
@@ -362,6 +426,9 @@ __device__ __forceinline__ void region(f32x16_t (&s_next)[Cfg<D>::SB],
             oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, p_prev[kc2 >> 1][kc2 & 1],
                                                                 oacc[db], 0, 0, 0);
         }
+#pragma unroll
+        for (int e = 0; e < C::DMA_W; ++e)
+            if (i == S::copy_at(e)) issue_copy<D>(dma, job, e);
         if (i % S::CHUNK_EVERY == S::CHUNK_EVERY - 1) {
             const int k = i / S::CHUNK_EVERY;      // chunk: two consecutive scores
             const int sb = k / 8, h = (k % 8) / 4, j = (k % 4) * 2;
@@ -374,6 +441,8 @@ __device__ __forceinline__ void region(f32x16_t (&s_next)[Cfg<D>::SB],
         }
         __builtin_amdgcn_sched_barrier(0);
     }
+    carry[0] = ring[S::N % 3];
+    carry[1] = ring[(S::N + 1) % 3];
 #pragma unroll
     for (int sb = 0; sb < C::SB; ++sb)
 #pragma unroll
@@ -429,8 +498,8 @@ __device__ __forceinline__ void raise_reference(
 
 template <int D>
 struct Smem {
-    uint16_t k[Cfg<D>::STAGES][Cfg<D>::K_TILE];
-    uint16_t v[Cfg<D>::STAGES][Cfg<D>::V_TILE];
+    char k[Cfg<D>::STAGES][Cfg<D>::K_TILE];
+    char v[Cfg<D>::STAGES][Cfg<D>::V_TILE];
 };
 
 struct Ctx {
@@ -439,52 +508,58 @@ struct Ctx {
     int64_t ldv;
     int N_kv, t_begin, t_end;
     float c;   // log2(e) * scale
-    int tid, wave, ql, g;
+    int tid, ql, g;
 };
 
-// One pipeline step for tile t, r = t - t_begin.  On entry K(t+1) is in
-// stage (r+1)%3, V(t-1) in stage (r+2)%3, and K(t+2), V(t) are in flight to
-// stages (r+2)%3 and r%3.  The step computes, waits for its in-flight
-// tiles, publishes them with a barrier, then starts K(t+3) and V(t+1) into
-// the stages freed by tiles t and t-2.
+// One pipeline step for tile t, r = t - t_begin.  Tile t' of K and of V^T
+// lives in stage (t' - t_begin) % 4 (V "tile t_begin - 1", all zeros, in
+// stage 3).  On entry K(t+1), K(t+2), V(t-1) and V(t) are published (landed,
+// behind a barrier) and K(t+3), V(t+1) are in flight.  The step computes
+// (reading K(t+1), V(t-1), and K(t+2) for the next step's first operands)
+// while its copies of K(t+4) and V(t+2) go into the stages of K(t) and
+// V(t-2), freed by the previous barrier; it then waits until only its own
+// copies are in flight and publishes K(t+3), V(t+1) with a barrier.  A tile
+// is thus published one step before it is read and copied two steps ahead.
 template <int D, bool RAGGED>
 __device__ __forceinline__ void tile_step(int t, const Ctx &x, State<D> &st, Smem<D> &sm,
-                                          const TileDma<D> &dma, f32x16_t (&s_cur)[Cfg<D>::SB],
+                                          const TileDma<D> &dma, const OperandOffsets<D> &oo,
+                                          f32x16_t (&s_cur)[Cfg<D>::SB],
                                           f32x16_t (&s_next)[Cfg<D>::SB],
                                           const bf16x8_t (&p_prev)[Cfg<D>::SB][2],
                                           bf16x8_t (&p_cur)[Cfg<D>::SB][2],
+                                          bf16x8_t (&carry)[2],
                                           const bf16x8_t (&qreg)[Cfg<D>::KC]) {
     using C = Cfg<D>;
     constexpr int BN = C::BN;
     const int r = t - x.t_begin;
-    const int s0 = r % 3, s1 = (r + 1) % 3, s2 = (r + 2) % 3;
+    const int sk1 = (r + 1) & 3, sk2 = (r + 2) & 3, sv_prev = (r + 3) & 3;
     const int j0 = t * BN;
     if (RAGGED && j0 + BN > x.N_kv) {  // ragged last tile: drop keys past the buffer
 #pragma unroll
         for (int sb = 0; sb < C::SB; ++sb)
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const int key = j0 + sb * 32 + (i >> 2) * 8 + x.g * 4 + (i & 3);
+                const int key = j0 + sb * 32 + score_key(i, x.g);
                 if (key >= x.N_kv) s_cur[sb][i] = -INFINITY;
             }
     }
+    const CopyJob job = copy_job<D>(x.Kh, x.Vh, x.ldv, x.N_kv, x.t_end, t + 4, t + 2,
+                                    lds_addr(sm.k[r & 3]), lds_addr(sm.v[(r + 2) & 3]));
 
     float l_tile = 0.f;
-    region<D>(s_next, st.oacc, p_cur, l_tile, s_cur, p_prev, sm.k[s1], sm.v[s2], qreg, x.c,
-              st.m_run, x.ql * C::K_LD + x.g * 8, x.ql * C::V_LD + x.g * 4);
+    region<D>(s_next, st.oacc, p_cur, l_tile, s_cur, p_prev, sm.k[sk1], sm.v[sv_prev], sm.k[sk2],
+              carry, qreg, x.c, st.m_run, oo, dma, job);
     // each probability is at most the tile's row-sum share, so a share
     // within kMaxTileSum proves none outgrew the reference
     if (__any(!(l_tile <= kMaxTileSum))) raise_reference<D>(st, s_cur, p_cur, l_tile, x.c);
     st.l_run += l_tile;
 
-    wait_dma();                       // this wave's K(t+2), V(t) copies have landed
+    wait_dma_keep4();                 // K(t+3), V(t+1) have landed
     __syncthreads();
-    if (RAGGED && j0 + BN > x.N_kv) {   // V(t) is the ragged last tile
-        zero_tail_v<D>(sm.v[s0], j0, x.N_kv, x.tid);
+    if (RAGGED && j0 + 2 * BN > x.N_kv && t + 1 < x.t_end) {   // V(t+1) is the ragged last tile
+        zero_tail_v<D>(sm.v[(r + 1) & 3], j0 + BN, x.N_kv, x.tid);
         __syncthreads();
     }
-    if (t + 3 < x.t_end) dma.load_k(x.Kh, j0 + 3 * BN, x.N_kv, sm.k[s0]);
-    if (t + 1 < x.t_end) dma.load_v(x.Vh, j0 + BN, x.ldv, sm.v[s1]);
 }
 
 template <int D>
@@ -519,11 +594,10 @@ __global__ __launch_bounds__(Cfg<D>::THREADS, Cfg<D>::WG_PER_CU) void attn_fwd_b
     const int ntiles = (N_kv + BN - 1) / BN;
     x.t_begin = split * p.tiles_per_split;
     x.t_end = min(ntiles, x.t_begin + p.tiles_per_split);
+    x.c = p.c_log2;
     x.tid = tid;
-    x.wave = wave;
     x.ql = ql;
     x.g = g;
-    x.c = p.c_log2;
 
     // Q^T as the B operand: lane (ql, g) holds d = kc*16 + g*8 .. +7 of its
     // query.  Q enters the product unscaled (exact); scale * log2(e) is
@@ -542,22 +616,38 @@ __global__ __launch_bounds__(Cfg<D>::THREADS, Cfg<D>::WG_PER_CU) void attn_fwd_b
         for (int i = 0; i < 16; ++i) st.oacc[db][i] = 0.f;
     st.l_run = 0.f;
 
-    // Prologue: K(t0), K(t0+1) landed; V "tile t0-1" (stage 2) zeroed, since
-    // the first step's P.V uses zero probabilities against it; S(t0); then
-    // K(t0+2) and V(t0) in flight.
+    // Prologue: K(t0..t0+2) and V(t0) landed, V "tile t0-1" (stage 3)
+    // zeroed, since the first step's P.V uses zero probabilities against
+    // it; S(t0) and the reference max; the first step's first operands;
+    // K(t0+3) and V(t0+1) in flight (the loop's entry state).
     TileDma<D> dma;
     dma.init(wave, lane, p.ldv);
+    OperandOffsets<D> oo;
+    oo.init(ql, g);
     const int t0 = x.t_begin;
-    dma.load_k(x.Kh, t0 * BN, N_kv, sm.k[0]);
-    if (t0 + 1 < x.t_end) dma.load_k(x.Kh, (t0 + 1) * BN, N_kv, sm.k[1]);
-    for (int e = tid; e < C::V_TILE / 8; e += C::THREADS)
-        reinterpret_cast<uint4 *>(sm.v[2])[e] = zero4();
-    wait_dma();
+    {
+        const CopyJob j0 = copy_job<D>(x.Kh, x.Vh, x.ldv, N_kv, x.t_end, t0, t0,
+                                       lds_addr(sm.k[0]), lds_addr(sm.v[0]));
+        const CopyJob j1 = copy_job<D>(x.Kh, x.Vh, x.ldv, N_kv, x.t_end, t0 + 1, t0 + 1,
+                                       lds_addr(sm.k[1]), lds_addr(sm.v[1]));
+        const CopyJob j2 = copy_job<D>(x.Kh, x.Vh, x.ldv, N_kv, x.t_end, t0 + 2, t0 + 2,
+                                       lds_addr(sm.k[2]), lds_addr(sm.v[2]));
+#pragma unroll
+        for (int e = 0; e < C::DMA_W; ++e) issue_copy<D>(dma, j0, e);   // K(t0), V(t0)
+#pragma unroll
+        for (int e = 0; e < C::K_DMA_W; ++e) issue_copy<D>(dma, j1, e);   // K(t0+1)
+#pragma unroll
+        for (int e = 0; e < C::K_DMA_W; ++e) issue_copy<D>(dma, j2, e);   // K(t0+2)
+    }
+    for (int e = tid; e < C::V_TILE / 16; e += C::THREADS)
+        reinterpret_cast<uint4 *>(sm.v[3])[e] = zero4();
+    wait_dma_all();
     __syncthreads();
+    if (t0 * BN + BN > N_kv) zero_tail_v<D>(sm.v[0], t0 * BN, N_kv, tid);   // lone ragged tile
 
     f32x16_t sA[C::SB], sB[C::SB];
     bf16x8_t pA[C::SB][2], pB[C::SB][2];
-    qk_tile<D>(sA, sm.k[0], qreg, ql, g);
+    qk_tile<D>(sA, sm.k[0], qreg, oo);
     // The reference max is the first tile's max over valid keys; it stays
     // fixed until a later tile outgrows it (raise_reference).
     {
@@ -567,7 +657,7 @@ __global__ __launch_bounds__(Cfg<D>::THREADS, Cfg<D>::WG_PER_CU) void attn_fwd_b
         for (int sb = 0; sb < C::SB; ++sb)
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const int key = sb * 32 + (i >> 2) * 8 + g * 4 + (i & 3);
+                const int key = sb * 32 + score_key(i, g);
                 if (key >= nvalid) sA[sb][i] = -INFINITY;
                 mx = fmaxf(mx, sA[sb][i]);
             }
@@ -579,8 +669,15 @@ __global__ __launch_bounds__(Cfg<D>::THREADS, Cfg<D>::WG_PER_CU) void attn_fwd_b
         for (int h = 0; h < 2; ++h)
 #pragma unroll
             for (int j = 0; j < 8; ++j) pB[sb][h][j] = (__bf16)0.0f;
-    if (t0 + 2 < x.t_end) dma.load_k(x.Kh, (t0 + 2) * BN, N_kv, sm.k[2]);
-    dma.load_v(x.Vh, t0 * BN, p.ldv, sm.v[0]);
+    bf16x8_t carry[2] = {step_operand<D>(0, sm.k[1], sm.v[0], oo),
+                         step_operand<D>(1, sm.k[1], sm.v[0], oo)};
+    {
+        const CopyJob j3 = copy_job<D>(x.Kh, x.Vh, x.ldv, N_kv, x.t_end, t0 + 3, t0 + 1,
+                                       lds_addr(sm.k[3]), lds_addr(sm.v[1]));
+#pragma unroll
+        for (int e = 0; e < C::DMA_W; ++e) issue_copy<D>(dma, j3, e);   // K(t0+3), V(t0+1)
+    }
+    __syncthreads();   // stage 0 of K is free; V(t0)'s zeroed tail is visible
 
     // Two register sets alternate roles from step to step, so the loop runs
     // two steps per trip and never copies scores or probabilities.  Only
@@ -588,17 +685,18 @@ __global__ __launch_bounds__(Cfg<D>::THREADS, Cfg<D>::WG_PER_CU) void attn_fwd_b
     // that masks it.
     int t = t0;
     for (; t + 2 < x.t_end; t += 2) {
-        tile_step<D, false>(t, x, st, sm, dma, sA, sB, pB, pA, qreg);
-        tile_step<D, false>(t + 1, x, st, sm, dma, sB, sA, pA, pB, qreg);
+        tile_step<D, false>(t, x, st, sm, dma, oo, sA, sB, pB, pA, carry, qreg);
+        tile_step<D, false>(t + 1, x, st, sm, dma, oo, sB, sA, pA, pB, carry, qreg);
     }
     if (t + 1 < x.t_end) {
-        tile_step<D, true>(t, x, st, sm, dma, sA, sB, pB, pA, qreg);
-        tile_step<D, true>(t + 1, x, st, sm, dma, sB, sA, pA, pB, qreg);
-        pv_tile<D>(st.oacc, pB, sm.v[(t + 1 - t0) % 3], ql, g);
+        tile_step<D, true>(t, x, st, sm, dma, oo, sA, sB, pB, pA, carry, qreg);
+        tile_step<D, true>(t + 1, x, st, sm, dma, oo, sB, sA, pA, pB, carry, qreg);
+        pv_tile<D>(st.oacc, pB, sm.v[(t + 1 - t0) & 3], oo);
     } else {
-        tile_step<D, true>(t, x, st, sm, dma, sA, sB, pB, pA, qreg);
-        pv_tile<D>(st.oacc, pA, sm.v[(t - t0) % 3], ql, g);
+        tile_step<D, true>(t, x, st, sm, dma, oo, sA, sB, pB, pA, carry, qreg);
+        pv_tile<D>(st.oacc, pA, sm.v[(t - t0) & 3], oo);
     }
+    wait_dma_all();   // no copy may outlive the workgroup's LDS
 
     const float l_tot = pair_sum(st.l_run);
 
