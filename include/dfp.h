@@ -140,7 +140,8 @@ dfp_status dfp_kv_scatter(void *k_buf, void *v_buf_t, const void *k_new,
  * d must be 64 or 128.  n_q == 0 is a no-op (pointers may then be NULL).
  * o must not alias the inputs.
  * Errors: INVALID_ARG for null pointers, non-positive B/H/N_kv, negative n_q,
- * a bad scale; UNSUPPORTED for other d or dtype. */
+ * a bad scale, pointers not 16-byte aligned; UNSUPPORTED for other d or
+ * dtype, or (bf16) when one (b,h) slice of k_buf or v_buf_t reaches 2 GiB. */
 dfp_status dfp_patch_attention(void *o, const void *q, const void *k_buf,
                                const void *v_buf_t, int B, int H, int n_q,
                                int N_kv, int d, float scale, dfp_dtype dt,

@@ -65,9 +65,12 @@ namespace {
 
 using dfp::bf16x8_t;
 using dfp::f32x16_t;
+using dfp::f32x4_t;
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 constexpr float kMaxTileSum = 4096.0f;   // a tile's row-sum share above this raises the max
+constexpr int kMaxSplits = 8;            // key-range splits per query tile, at most
+constexpr int kCoherent = 16;            // buffer cache policy sc1: device-coherent access
 constexpr int kNumXcd = 8;
 
 struct Params {
@@ -719,82 +722,119 @@ __global__ __launch_bounds__(Cfg<D>::THREADS, Cfg<D>::WG_PER_CU) void attn_fwd_b
         return;
     }
 
-    // split-KV: publish this range's partial, the last arrival merges
+    // split-KV: publish this range's partial, the last arrival merges.
+    // Partials travel through coherent 16-byte stores and loads (cache
+    // policy sc1: they bypass the non-coherent part of the cache hierarchy
+    // for device scope), see dfp::publish.
     const int row = wave * 32 + ql;
     const int64_t slot = (int64_t)qtile_id * p.splits + split;
-    float *po = p.part_o + slot * C::BLOCK_M * D + (int64_t)row * D;
+    {
+        const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+            p.part_o + slot * C::BLOCK_M * D, 0, C::BLOCK_M * D * 4, 0x00020000);
 #pragma unroll
-    for (int db = 0; db < C::DB; ++db)
+        for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr)
-            *reinterpret_cast<float4 *>(po + db * 32 + rr * 8 + g * 4) =
-                make_float4(st.oacc[db][rr * 4], st.oacc[db][rr * 4 + 1], st.oacc[db][rr * 4 + 2],
-                            st.oacc[db][rr * 4 + 3]);
+            for (int rr = 0; rr < 4; ++rr) {
+                const f32x4_t v = {st.oacc[db][rr * 4], st.oacc[db][rr * 4 + 1],
+                                   st.oacc[db][rr * 4 + 2], st.oacc[db][rr * 4 + 3]};
+                __builtin_amdgcn_raw_buffer_store_b128(
+                    __builtin_bit_cast(int32x4_t, v), ro,
+                    (row * D + db * 32 + rr * 8 + g * 4) * 4, 0, kCoherent);
+            }
+    }
     if (g == 0) {
         float *pml = p.part_ml + (slot * C::BLOCK_M + row) * 2;
-        pml[0] = st.m_run;
-        pml[1] = l_tot;
+        dfp::publish(pml, st.m_run);
+        dfp::publish(pml + 1, l_tot);
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    dfp::published_wait();
     __syncthreads();
-    if (tid == 0) {
-        const unsigned prev = __hip_atomic_fetch_add(p.counters + qtile_id, 1u, __ATOMIC_ACQ_REL,
-                                                     __HIP_MEMORY_SCOPE_AGENT);
-        s_last = (prev == (unsigned)p.splits - 1);
-    }
+    if (tid == 0) s_last = (dfp::arrive(p.counters + qtile_id) == (unsigned)p.splits - 1);
     __syncthreads();
     if (!s_last) return;
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 
-    // merge: O = sum_s 2^(m_s - m*) O_s / sum_s 2^(m_s - m*) l_s, split order
+    // merge: O = sum_s w_s O_s with w_s = 2^(m_s - m*) / sum_s' 2^(m_s' - m*) l_s',
+    // in split order.  Row weights first (into LDS, reusing the K ring),
+    // then every thread streams its 16-byte groups, one batch of loads per
+    // split in flight together.
     const int64_t base = (int64_t)qtile_id * p.splits;
-    for (int e = tid; e < C::BLOCK_M * D / 4; e += C::THREADS) {
-        const int rr = (e * 4) / D, d0 = (e * 4) % D;
+    float *wts = reinterpret_cast<float *>(sm.k[0]);   // [BLOCK_M][kMaxSplits]
+    static_assert(C::BLOCK_M * kMaxSplits * 4 <= C::K_TILE, "row weights fit one K stage");
+    if (tid < C::BLOCK_M) {
+        float ms[kMaxSplits], ls[kMaxSplits];
+#pragma unroll
+        for (int s = 0; s < kMaxSplits; ++s) {
+            if (s < p.splits) {
+                const float *ml = p.part_ml + ((base + s) * C::BLOCK_M + tid) * 2;
+                ms[s] = dfp::fetch_published(ml);
+                ls[s] = dfp::fetch_published(ml + 1);
+            }
+        }
+        float mstar = -INFINITY;
+#pragma unroll
+        for (int s = 0; s < kMaxSplits; ++s)
+            if (s < p.splits) mstar = fmaxf(mstar, ms[s]);
+        float den = 0.f;
+#pragma unroll
+        for (int s = 0; s < kMaxSplits; ++s)
+            if (s < p.splits) {
+                ms[s] = __builtin_amdgcn_exp2f(ms[s] - mstar);
+                den = fmaf(ms[s], ls[s], den);
+            }
+        const float inv = 1.0f / den;
+#pragma unroll
+        for (int s = 0; s < kMaxSplits; ++s)
+            if (s < p.splits) wts[tid * kMaxSplits + s] = ms[s] * inv;
+    }
+    __syncthreads();
+    constexpr int G = C::BLOCK_M * D / 4 / C::THREADS;   // 16-byte groups per thread
+    static_assert(G * C::THREADS * 4 == C::BLOCK_M * D, "groups tile the query tile");
+    f32x4_t acc[G];
+#pragma unroll
+    for (int k = 0; k < G; ++k) acc[k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < p.splits; ++s) {
+        const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+            p.part_o + (base + s) * C::BLOCK_M * D, 0, C::BLOCK_M * D * 4, 0x00020000);
+        f32x4_t v[G];
+#pragma unroll
+        for (int k = 0; k < G; ++k)
+            v[k] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                   ro, (tid + k * C::THREADS) * 16, 0, kCoherent));
+#pragma unroll
+        for (int k = 0; k < G; ++k) {
+            const int rr = (tid + k * C::THREADS) * 4 / D;
+            acc[k] += wts[rr * kMaxSplits + s] * v[k];
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < G; ++k) {
+        const int e = tid + k * C::THREADS;
+        const int rr = e * 4 / D, d0 = e * 4 % D;
         const int qr = qt * C::BLOCK_M + rr;
         if (qr >= n_q) continue;
-        float mstar = -INFINITY;
-        for (int s = 0; s < p.splits; ++s)
-            mstar = fmaxf(mstar, __hip_atomic_load(p.part_ml + ((base + s) * C::BLOCK_M + rr) * 2,
-                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-        float acc[4] = {0.f, 0.f, 0.f, 0.f};
-        float den = 0.f;
-        for (int s = 0; s < p.splits; ++s) {
-            const float *ml = p.part_ml + ((base + s) * C::BLOCK_M + rr) * 2;
-            const float ms = __hip_atomic_load(ml, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            const float ls = __hip_atomic_load(ml + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            const float wgt = __builtin_amdgcn_exp2f(ms - mstar);
-            const float *src = p.part_o + ((base + s) * C::BLOCK_M + rr) * D + d0;
-#pragma unroll
-            for (int e4 = 0; e4 < 4; ++e4)
-                acc[e4] = fmaf(wgt,
-                               __hip_atomic_load(src + e4, __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_AGENT),
-                               acc[e4]);
-            den = fmaf(wgt, ls, den);
-        }
-        const float inv = 1.0f / den;
-        __bf16 vals[4] = {(__bf16)(acc[0] * inv), (__bf16)(acc[1] * inv), (__bf16)(acc[2] * inv),
-                          (__bf16)(acc[3] * inv)};
+        __bf16 vals[4] = {(__bf16)acc[k][0], (__bf16)acc[k][1], (__bf16)acc[k][2],
+                          (__bf16)acc[k][3]};
         uint2 pk;
         __builtin_memcpy(&pk, vals, 8);
         *reinterpret_cast<uint2 *>(p.O + ((int64_t)bh * n_q + qr) * D + d0) = pk;
     }
-    if (tid == 0)
-        __hip_atomic_store(p.counters + qtile_id, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) dfp::publish(p.counters + qtile_id, 0u);
 }
 
 // ---------------------------------------------------------------- planning
 constexpr int kCus = 256;
-constexpr int kMaxSplits = 8;
 
 struct Plan {
     int block_m, q_tiles, ntiles, splits, tiles_per_split;
 };
 
-// Pick the key-range split that minimises an estimate of the makespan:
-// rounds of resident workgroups x tiles per workgroup, plus the cost of
-// writing and merging fp32 partials.  One workgroup is resident per CU
-// (the LDS ring and VGPR budget are sized for that).
+// Pick the key-range split that minimises an estimate of the makespan,
+// from per-step times measured for this kernel on MI355X: a 64-key step of
+// one workgroup takes about T_ALONE when the workgroup has its CU to itself
+// and T_SHARED when two share it (d=64 keeps two resident per CU, d=128
+// one).  Workgroups beyond the resident slots run in later rounds.  Every
+// workgroup pays a fixed prologue/epilogue; a split adds the hand-off
+// latency and moves each fp32 partial through memory twice (publish, merge).
 Plan make_plan(int BH, int n_q, int N_kv, int d, bool can_split) {
     Plan pl;
     pl.block_m = d == 64 ? Cfg<64>::BLOCK_M : Cfg<128>::BLOCK_M;
@@ -804,10 +844,13 @@ Plan make_plan(int BH, int n_q, int N_kv, int d, bool can_split) {
     pl.splits = 1;
     pl.tiles_per_split = pl.ntiles;
     if (!can_split) return pl;
+    const int per_cu = d == 64 ? Cfg<64>::WG_PER_CU : Cfg<128>::WG_PER_CU;
+    const double t_alone = d == 64 ? 0.62e-6 : 1.7e-6;   // s per step, CU to itself
+    const double t_shared = 1.09e-6;                     // s per step, two per CU (d=64)
+    const double t_fixed = 3e-6;                         // prologue + epilogue
+    const double t_handoff = 3e-6;                       // publish, arrive, row weights
+    const double merge_bw = 5e12;                        // partial bytes/s, written and read
     const double base = (double)BH * pl.q_tiles;
-    const double tile_flop = 4.0 * pl.block_m * bn * d;
-    const double cu_rate = 1.8e15 / kCus;  // sustained MFMA rate per CU
-    const double part_bw = 4.0e12;         // partial write + merge read
     double best = 1e300;
     const char *env = std::getenv("DFP_ATTN_SPLITS");
     const int forced = env ? std::atoi(env) : 0;
@@ -816,8 +859,17 @@ Plan make_plan(int BH, int n_q, int N_kv, int d, bool can_split) {
         const int s_eff = (pl.ntiles + tps - 1) / tps;
         if (s_eff != s) continue;
         const double wgs = base * s;
-        double t = std::ceil(wgs / kCus) * tps * tile_flop / cu_rate;
-        if (s > 1) t += wgs * pl.block_m * d * 8.0 / part_bw;
+        double t;
+        if (per_cu == 1) {
+            t = std::ceil(wgs / kCus) * tps * t_alone;
+        } else {
+            const double slots = (double)kCus * per_cu;
+            const double full = std::floor(wgs / slots), rem = wgs - full * slots;
+            t = full * tps * t_shared +
+                (rem <= 0 ? 0.0 : tps * (rem <= kCus ? t_alone : t_shared));
+        }
+        t += t_fixed;
+        if (s > 1) t += t_handoff + 2.0 * wgs * pl.block_m * d * 4.0 / merge_bw;
         if (forced > 0 ? s == forced : t < best * 0.98) {
             best = t;
             pl.splits = s;
@@ -850,6 +902,10 @@ size_t dfp_attn_workspace_bytes(int B, int H, int n_q, int N_kv, int d) {
 dfp_status dfp_attn_bf16_launch(void *o, const void *q, const void *k, const void *vt, int BH,
                                 int n_q, int N_kv, int d, float scale, void *ws, size_t ws_bytes,
                                 hipStream_t stream) {
+    // tile copies address one (batch, head)'s K and V^T with 32-bit offsets
+    const int64_t ldv = dfp_v_ld(N_kv, DFP_BF16);
+    if ((int64_t)N_kv * d * 2 >= (int64_t(1) << 31) || (int64_t)d * ldv * 2 >= (int64_t(1) << 31))
+        return DFP_ERR_UNSUPPORTED;
     Plan pl = make_plan(BH, n_q, N_kv, d, true);
     if (pl.splits > 1 && (!ws || ws_bytes < need_bytes(BH, d, pl) ||
                           (reinterpret_cast<uintptr_t>(ws) & 255u) != 0))
@@ -862,7 +918,7 @@ dfp_status dfp_attn_bf16_launch(void *o, const void *q, const void *k, const voi
     p.K = static_cast<const uint16_t *>(k);
     p.Vt = static_cast<const uint16_t *>(vt);
     p.O = static_cast<uint16_t *>(o);
-    p.ldv = dfp_v_ld(N_kv, DFP_BF16);
+    p.ldv = ldv;
     p.n_q = n_q;
     p.N_kv = N_kv;
     p.c_log2 = scale * 1.4426950408889634f;

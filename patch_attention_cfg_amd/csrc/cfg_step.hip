@@ -18,7 +18,9 @@
 // Reduction: fp32 per thread and per wavefront, fp64 per workgroup; the last
 // workgroup to finish (integer completion counter) sums the per-workgroup
 // partials in a fixed order in fp64 and writes the ratio.  No float atomics,
-// so the result is bitwise reproducible run to run.
+// so the result is bitwise reproducible run to run.  The partials move
+// between workgroups through coherent stores and loads (dfp::publish), not
+// through L2-wide cache maintenance.
 #include <cmath>
 
 #include "dfp_common.h"
@@ -129,16 +131,14 @@ __global__ __launch_bounds__(kThreads) void cfg_step_kernel(
             pd += (double)wden[k];
         }
         double *p = partials + 2 * ((int64_t)img * nblk + blk);
-        __hip_atomic_store(p, pn, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(p + 1, pd, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        dfp::publish(p, pn);
+        dfp::publish(p + 1, pd);
+        dfp::published_wait();
         const unsigned total = (unsigned)nblk * gridDim.y;
-        const unsigned prev =
-            __hip_atomic_fetch_add(counter, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-        is_last = (prev == total - 1);
+        is_last = (dfp::arrive(counter) == total - 1);
     }
     __syncthreads();
     if (!is_last) return;
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 
     // last workgroup: fixed-order fp64 sums of every image's partials
     __shared__ double snum[kThreads], sden[kThreads];
@@ -146,8 +146,8 @@ __global__ __launch_bounds__(kThreads) void cfg_step_kernel(
         double a = 0.0, b = 0.0;
         const double *p = partials + 2 * (int64_t)im * nblk;
         for (int k = tid; k < nblk; k += kThreads) {
-            a += __hip_atomic_load(p + 2 * k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            b += __hip_atomic_load(p + 2 * k + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            a += dfp::fetch_published(p + 2 * k);
+            b += dfp::fetch_published(p + 2 * k + 1);
         }
         snum[tid] = a;
         sden[tid] = b;
@@ -162,7 +162,7 @@ __global__ __launch_bounds__(kThreads) void cfg_step_kernel(
         if (tid == 0) out[im] = (float)(snum[0] / sden[0]);
         __syncthreads();
     }
-    if (tid == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) dfp::publish(counter, 0u);
 }
 
 size_t workspace_need(int64_t n_per_image, int batch) {

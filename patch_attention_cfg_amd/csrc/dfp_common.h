@@ -32,4 +32,31 @@ __device__ __forceinline__ T wave_sum(T v) {
     return v;
 }
 
+// Cross-workgroup hand-off without cache maintenance.  A workgroup that
+// publishes partial results writes them with device-scope relaxed atomic
+// stores (coherent writes that go through to the device's coherence point
+// rather than staying in one XCD's L2), calls published_wait() so they have
+// completed, and only then bumps an arrival counter; the last arrival reads
+// the partials with device-scope relaxed atomic loads (coherent reads).
+// A release/acquire fence pair at device scope would also be correct, but
+// it writes back and invalidates the whole L2 of the XCD each time, which
+// every other workgroup on that XCD pays for.
+__device__ __forceinline__ void published_wait() {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+template <typename T>
+__device__ __forceinline__ void publish(T *p, T v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <typename T>
+__device__ __forceinline__ T fetch_published(const T *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ unsigned arrive(unsigned *counter) {
+    return __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 }  // namespace dfp

@@ -7,44 +7,56 @@
 // (batch, head), K row-major and V transposed (channel-major), with no
 // arithmetic.  Both paths move 16-byte vectors; the V path transposes a
 // 64 x 64 element tile through LDS so both its reads (along channels) and its
-// writes (along tokens) stay coalesced.
+// writes (along tokens) stay coalesced.  K and V share one launch (the copy
+// is latency-bound at these sizes, so a second launch would cost as much as
+// the data).
 #include "dfp_common.h"
 
 namespace {
 
+struct ScatterArgs {
+    uint4 *k_dst;             // K buffer, 16-byte vectors
+    const uint4 *k_src;
+    int64_t k_vec_per_bh;     // n * d / VE
+    int64_t k_dst_bh_stride;  // N_buf * d / VE
+    int64_t k_dst_off;        // row0 * d / VE
+    int64_t k_total;          // BH * k_vec_per_bh
+    void *v_dst;              // V^T buffer [BH][d][ldv]
+    const void *v_src;        // [BH][n][d]
+    int n, d, row0;
+    int64_t ldv;
+    int v_tiles_i, v_tiles_c;   // 64-token and 64-channel tiles per (b,h)
+    int v_blocks;               // blocks [0, v_blocks) transpose V; the rest copy K
+};
+
 // K: every (b,h) owns one contiguous run of n*d elements in k_new and one in
 // k_buf starting at row0*d; both runs are multiples of 16 bytes.
-__global__ __launch_bounds__(256) void k_rows_copy(uint4 *__restrict__ dst,
-                                                   const uint4 *__restrict__ src,
-                                                   int64_t vec_per_bh,
-                                                   int64_t dst_bh_stride_vec,
-                                                   int64_t dst_off_vec,
-                                                   int64_t total_vec) {
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; v < total_vec; v += stride) {
-        const int64_t bh = v / vec_per_bh;
-        const int64_t r = v - bh * vec_per_bh;
-        dst[bh * dst_bh_stride_vec + dst_off_vec + r] = src[v];
+__device__ __forceinline__ void k_rows_copy(const ScatterArgs &a, int64_t first, int64_t stride) {
+    for (int64_t v = first; v < a.k_total; v += stride) {
+        const int64_t bh = v / a.k_vec_per_bh;
+        const int64_t r = v - bh * a.k_vec_per_bh;
+        a.k_dst[bh * a.k_dst_bh_stride + a.k_dst_off + r] = a.k_src[v];
     }
 }
 
-// V: dst[bh][c][row0 + i] = src[bh][i][c] for i < n, c < d.
-// Element type E is only a bit container (uint16_t for bf16, uint32_t for f32).
+// V: dst[bh][c][row0 + i] = src[bh][i][c] for one 64 x 64 (token x channel)
+// tile.  Element type E is only a bit container (uint16_t for bf16,
+// uint32_t for f32).
 template <typename E>
-__global__ __launch_bounds__(256) void v_transpose_copy(E *__restrict__ dst,
-                                                        const E *__restrict__ src,
-                                                        int n, int d, int64_t ldv,
-                                                        int row0) {
+__device__ __forceinline__ void v_tile_transpose(const ScatterArgs &a, int tile) {
     constexpr int T = 64;                      // tile edge (tokens x channels)
     constexpr int VE = 16 / sizeof(E);         // elements per 16-byte vector
-    constexpr int PAD = 4 / sizeof(E) + 0;     // one dword of padding per row
-    __shared__ E tile[T][T + PAD];
+    constexpr int PAD = 4 / sizeof(E);         // one dword of padding per row
+    __shared__ E sm_tile[T][T + PAD];
 
-    const int i0 = blockIdx.x * T;             // token tile
-    const int c0 = blockIdx.y * T;             // channel tile
-    const int64_t bh = blockIdx.z;
-    const E *s = src + bh * (int64_t)n * d;
-    E *o = dst + bh * (int64_t)d * ldv;
+    const int ti = tile % a.v_tiles_i;
+    const int rest = tile / a.v_tiles_i;
+    const int tc = rest % a.v_tiles_c;
+    const int64_t bh = rest / a.v_tiles_c;
+    const int i0 = ti * T, c0 = tc * T;
+    const int n = a.n, d = a.d;
+    const E *s = static_cast<const E *>(a.v_src) + bh * (int64_t)n * d;
+    E *o = static_cast<E *>(a.v_dst) + bh * (int64_t)d * a.ldv;
 
     // load: rows i, 16-byte vectors along channels (d is a multiple of VE)
     constexpr int VPR = T / VE;                // vectors per tile row
@@ -60,27 +72,40 @@ __global__ __launch_bounds__(256) void v_transpose_copy(E *__restrict__ dst,
             for (int k = 0; k < VE; ++k) vals[k] = 0;
         }
 #pragma unroll
-        for (int k = 0; k < VE; ++k) tile[i][cv * VE + k] = vals[k];
+        for (int k = 0; k < VE; ++k) sm_tile[i][cv * VE + k] = vals[k];
     }
     __syncthreads();
 
     // store: channel rows c, VE consecutive tokens per thread
-    const bool aligned = ((row0 + i0) % VE) == 0;
+    const bool aligned = ((a.row0 + i0) % VE) == 0;
     for (int t = threadIdx.x; t < T * VPR; t += blockDim.x) {
         const int c = t / VPR, iv = t - c * VPR;
         const int gc = c0 + c, gi = i0 + iv * VE;
         if (gc >= d || gi >= n) continue;
-        E *row = o + (int64_t)gc * ldv + row0 + gi;
+        E *row = o + (int64_t)gc * a.ldv + a.row0 + gi;
         if (aligned && gi + VE <= n) {
             E vals[VE];
 #pragma unroll
-            for (int k = 0; k < VE; ++k) vals[k] = tile[iv * VE + k][c];
+            for (int k = 0; k < VE; ++k) vals[k] = sm_tile[iv * VE + k][c];
             uint4 q;
             __builtin_memcpy(&q, vals, 16);
             *reinterpret_cast<uint4 *>(row) = q;
         } else {
-            for (int k = 0; k < VE && gi + k < n; ++k) row[k] = tile[iv * VE + k][c];
+            for (int k = 0; k < VE && gi + k < n; ++k) row[k] = sm_tile[iv * VE + k][c];
         }
+    }
+}
+
+// One launch lands both K and V: the first v_blocks workgroups transpose one
+// V tile each, the others copy K rows (grid-stride).
+template <typename E>
+__global__ __launch_bounds__(256) void kv_scatter_kernel(ScatterArgs a) {
+    if ((int)blockIdx.x < a.v_blocks) {
+        v_tile_transpose<E>(a, blockIdx.x);
+    } else {
+        const int64_t kb = blockIdx.x - a.v_blocks;
+        const int64_t k_blocks = gridDim.x - a.v_blocks;
+        k_rows_copy(a, kb * blockDim.x + threadIdx.x, k_blocks * blockDim.x);
     }
 }
 
@@ -95,6 +120,7 @@ extern "C" dfp_status dfp_kv_scatter(void *k_buf, void *v_buf_t, const void *k_n
     if (n == 0) return DFP_OK;  // empty tensors may carry null data pointers
     if ((k_buf == nullptr) != (k_new == nullptr) || (v_buf_t == nullptr) != (v_new == nullptr))
         return DFP_ERR_INVALID_ARG;
+    if (!k_buf && !v_buf_t) return DFP_OK;
     auto misaligned = [](const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; };
     if (misaligned(k_buf) || misaligned(k_new) || misaligned(v_buf_t) || misaligned(v_new))
         return DFP_ERR_INVALID_ARG;
@@ -103,31 +129,37 @@ extern "C" dfp_status dfp_kv_scatter(void *k_buf, void *v_buf_t, const void *k_n
     const int VE = 16 / esize;
     if (d % VE != 0) return DFP_ERR_UNSUPPORTED;
     const int64_t BH = (int64_t)B * H;
-    if (BH > 65535) return DFP_ERR_UNSUPPORTED;  // grid z limit of the V path
 
+    ScatterArgs a{};
+    a.n = n;
+    a.d = d;
+    a.row0 = row0;
+    int64_t k_blocks = 0, v_blocks = 0;
     if (k_buf) {
         const int64_t vec_per_row = (int64_t)d / VE;
-        const int64_t vec_per_bh = vec_per_row * n;
-        const int64_t total = vec_per_bh * BH;
-        int64_t blocks = (total + 255) / 256;
-        if (blocks > 8192) blocks = 8192;
-        hipLaunchKernelGGL(k_rows_copy, dim3((unsigned)blocks), dim3(256), 0, stream,
-                           static_cast<uint4 *>(k_buf), static_cast<const uint4 *>(k_new),
-                           vec_per_bh, vec_per_row * N_buf, vec_per_row * row0, total);
-        if (dfp::launch_status() != DFP_OK) return DFP_ERR_HIP;
+        a.k_dst = static_cast<uint4 *>(k_buf);
+        a.k_src = static_cast<const uint4 *>(k_new);
+        a.k_vec_per_bh = vec_per_row * n;
+        a.k_dst_bh_stride = vec_per_row * N_buf;
+        a.k_dst_off = vec_per_row * row0;
+        a.k_total = a.k_vec_per_bh * BH;
+        k_blocks = (a.k_total + 255) / 256;
+        if (k_blocks > 8192) k_blocks = 8192;
     }
     if (v_buf_t) {
-        const int64_t ldv = dfp_v_ld(N_buf, dt);
-        dim3 grid((unsigned)((n + 63) / 64), (unsigned)((d + 63) / 64), (unsigned)BH);
-        if (dt == DFP_BF16)
-            hipLaunchKernelGGL(v_transpose_copy<uint16_t>, grid, dim3(256), 0, stream,
-                               static_cast<uint16_t *>(v_buf_t),
-                               static_cast<const uint16_t *>(v_new), n, d, ldv, row0);
-        else
-            hipLaunchKernelGGL(v_transpose_copy<uint32_t>, grid, dim3(256), 0, stream,
-                               static_cast<uint32_t *>(v_buf_t),
-                               static_cast<const uint32_t *>(v_new), n, d, ldv, row0);
-        if (dfp::launch_status() != DFP_OK) return DFP_ERR_HIP;
+        a.v_dst = v_buf_t;
+        a.v_src = v_new;
+        a.ldv = dfp_v_ld(N_buf, dt);
+        a.v_tiles_i = (n + 63) / 64;
+        a.v_tiles_c = (d + 63) / 64;
+        v_blocks = (int64_t)a.v_tiles_i * a.v_tiles_c * BH;
     }
-    return DFP_OK;
+    if (v_blocks + k_blocks > 0x7FFFFFFF) return DFP_ERR_UNSUPPORTED;
+    a.v_blocks = (int)v_blocks;
+    const dim3 grid((unsigned)(v_blocks + k_blocks));
+    if (dt == DFP_BF16)
+        hipLaunchKernelGGL(kv_scatter_kernel<uint16_t>, grid, dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL(kv_scatter_kernel<uint32_t>, grid, dim3(256), 0, stream, a);
+    return dfp::launch_status();
 }
