@@ -11,7 +11,7 @@ w=7.5):
 All inputs are seeded synthetic arrays resident in HBM before timing starts.
 The timed steps replay one HIP graph of the step (falls back to eager
 launches if capture is refused).  Per-kernel durations for the roofline come
-from HIP events around back-to-back launches on the launch stream.
+from HIP events on the launch stream around batches of back-to-back launches.
 
 Prints ONE JSON line.  `--gpus N` with N > 1 is refused: this library is the
 single-GPU share of the work.
@@ -19,6 +19,7 @@ single-GPU share of the work.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -39,12 +40,36 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="c2", choices=["c2", "c3", "c4", "c5"],
-                    help="c2 (SDXL-1024) is the reported workload; others for exploration")
+    ap.add_argument("--workload", default="sdxl1024",
+                    choices=["sdxl1024", "sdxl2048", "sdxl3840", "dit1024"],
+                    help="sdxl1024 is the reported workload; the others are for exploration")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-reps", type=int, default=50)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="first run one plain device-to-device copy of this many MiB, the "
+                         "reference kernel that scales FETCH_SIZE/WRITE_SIZE counter runs")
     return ap.parse_args()
+
+
+def measured_traffic(kernel_source: str, level_name: str):
+    """HBM bytes per launch of the attention kernel on `level_name`, from the
+    committed rocprofv3 counter summary -- only while the kernel source still
+    hashes to the one the counters were taken on (else None)."""
+    path = os.path.join(ROOT, "profiles", f"attn_bf16_{level_name}_hbm_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+    with open(kernel_source, "rb") as fh:
+        sha = hashlib.sha256(fh.read()).hexdigest()
+    if fields.get("source_sha256") != sha or "traffic_bytes" not in fields:
+        return None
+    return float(fields["traffic_bytes"])
 
 
 class Level:
@@ -118,52 +143,64 @@ class Sampler:
         dfp.cfg_step(self.x, self.g_c[k], self.g_u[k], self.wl.w, c_x, c_e, self.r[k], self.ws)
 
 
-def time_kernel(torch, fn, reps):
-    """Average duration (us) of `fn`'s launches: HIP events around each of
-    `reps` back-to-back launches on the current stream.  A GPU spin queued
-    first lets every launch and event reach the queue before any of them
-    runs, so host launch latency does not land between the events."""
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+def time_kernel(torch, fn, reps, batches=3):
+    """Average launch duration (us) of `fn`: HIP events on the launch stream
+    around `reps` back-to-back launches, divided by `reps`, for each of
+    `batches` batches.  A GPU spin queued first lets every launch reach the
+    queue before any of them runs, so host launch latency does not land
+    between the events; one event pair per batch (not per launch) keeps the
+    events' own packets out of the kernel times.  Returns (mean over batches,
+    min over batches)."""
     fn()
     torch.cuda.synchronize()
-    torch.cuda._sleep(int(2e6 + reps * 1e5))
-    for s, e in zip(starts, ends):
-        s.record()
-        fn()
-        e.record()
-    torch.cuda.synchronize()
-    us = [s.elapsed_time(e) * 1e3 for s, e in zip(starts, ends)]
-    return float(np.mean(us)), float(np.median(us)), float(np.min(us))
+    per = []
+    for _ in range(batches):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(int(2e6 + reps * 1e5))
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        per.append(e0.elapsed_time(e1) * 1e3 / reps)
+    return float(np.mean(per)), float(np.min(per))
 
 
 def cpu_baseline(wl, inputs):
-    """The fp64 oracle, as it stands, on a bounded sample of the workload:
-    the first attention level's patch-1 attention for a fixed subset of its
-    query rows (all batch x head pairs), scaled to TFLOP/s."""
+    """The fp64 oracle, as it stands, on the same workload: one whole step
+    (every attention level's patch attention over its displaced buffer, then
+    the guided sampler step with rel-MAE), repeated until about 10 s of host
+    work; reported like `value` (attention FLOP of the step / step time)."""
     import oracle
-    lv = wl.levels[0]
-    x = inputs.attention_inputs(lv)
-    p = 1 if lv.P > 1 else 0
-    k_eff = oracle.effective_kv(x.k_stale, x.fresh_rows(p)[0], lv.row0(p))
-    v_eff = oracle.effective_kv(x.v_stale, x.fresh_rows(p)[1], lv.row0(p))
-    BH = lv.B * lv.H
-    # grow the row sample until ~10 s of oracle work (bounded at the whole patch)
-    rows = 16
+    levels = []
+    for lv in wl.levels:
+        x = inputs.attention_inputs(lv)
+        p = 1 if lv.P > 1 else 0
+        k_eff = oracle.effective_kv(x.k_stale, x.fresh_rows(p)[0], lv.row0(p))
+        v_eff = oracle.effective_kv(x.v_stale, x.fresh_rows(p)[1], lv.row0(p))
+        if lv.n_text:
+            k_eff = oracle.effective_kv(k_eff, x.text_rows()[0], 0)
+            v_eff = oracle.effective_kv(v_eff, x.text_rows()[1], 0)
+        levels.append((x.q_patch(p), k_eff, v_eff, 1.0 / lv.d ** 0.5, lv.flops()))
+    st = inputs.sampler_stream(wl)
+    g_c, g_u = st.next_pair()
+    sched = oracle.DDIMSchedule(wl.steps) if wl.sampler == "ddim" else oracle.EulerSchedule(wl.steps)
+    flops = sum(lv[4] for lv in levels)
+    reps, t0 = 0, time.perf_counter()
     while True:
-        bh = np.repeat(np.arange(BH), rows)
-        ri = np.tile(np.arange(rows), BH)
-        t0 = time.perf_counter()
-        oracle.attention_rows(x.q_patch(p), k_eff, v_eff, 1.0 / lv.d ** 0.5, bh, ri)
+        for q, k, v, scale, _ in levels:
+            oracle.attention(q, k, v, scale)
+        sched.step(st.x_T, g_c, g_u, wl.w, reps % wl.steps)
+        reps += 1
         dt = time.perf_counter() - t0
-        if dt >= 10.0 or rows >= lv.n:
+        if dt >= 10.0 or reps >= 200:
             break
-        rows = min(lv.n, max(rows * 2, int(rows * 10.0 / max(dt, 1e-3))))
-    flops = 4.0 * bh.size * lv.N_kv * lv.d
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+    return {"value": reps * flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
             "kind": "oracle",
-            "sample": f"{lv.name} patch {p} attention, {rows} query rows x {BH} (batch,head) "
-                      f"pairs x {lv.N_kv} keys in fp64 ({flops / 1e9:.2f} GFLOP, {dt:.1f} s)"}
+            "sample": f"{reps} whole steps of the {wl.name} workload: patch attention of every "
+                      f"level ({flops / 1e9:.2f} GFLOP per step, fp64) and the guided "
+                      f"{wl.sampler} step with rel-MAE on the latent, {dt:.1f} s"}
 
 
 def main():
@@ -181,6 +218,14 @@ def main():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(3)
     dfp.lib()
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib * 1024 * 1024 // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     wl = inputs.WORKLOADS[args.workload]
     levels = [Level(lv, dfp, torch, inputs) for lv in wl.levels]
     sampler = Sampler(wl, dfp, torch, inputs)
@@ -239,31 +284,34 @@ def main():
     reps = args.kernel_reps
     kern = {}
     for L in levels:
-        mean, med, mn = time_kernel(torch, lambda L=L: L.attend(dfp), reps)
+        mean, mn = time_kernel(torch, lambda L=L: L.attend(dfp), reps)
         kern[f"attn_{L.level.name}"] = {
-            "us_mean": mean, "us_median": med, "us_min": mn,
+            "us_mean": mean, "us_min": mn,
             "tflops": L.flops / (mean * 1e-6) / 1e12,
             "frac_bf16_peak": L.flops / (mean * 1e-6) / 1e12 / PEAK_BF16_TFLOPS,
             "flop": L.flops}
-        mean, med, mn = time_kernel(torch, lambda L=L: L.scatter(dfp), reps)
+        mean, mn = time_kernel(torch, lambda L=L: L.scatter(dfp), reps)
         kern[f"scatter_{L.level.name}"] = {
-            "us_mean": mean, "us_median": med,
+            "us_mean": mean, "us_min": mn,
             "gbps": L.fresh_bytes / (mean * 1e-6) / 1e9, "bytes": L.fresh_bytes}
     ctr = [0]
 
     def cfg():
         sampler.step(dfp, ctr[0])
         ctr[0] += 1
-    mean, med, mn = time_kernel(torch, cfg, reps)
-    kern["cfg_step"] = {"us_mean": mean, "us_median": med, "us_min": mn,
+    mean, mn = time_kernel(torch, cfg, reps)
+    kern["cfg_step"] = {"us_mean": mean, "us_min": mn,
                         "gbps": sampler.bytes / (mean * 1e-6) / 1e9,
                         "frac_hbm_peak": sampler.bytes / (mean * 1e-6) / 1e9 / PEAK_HBM_GBPS,
                         "bytes": sampler.bytes}
 
     dom = max(levels, key=lambda L: L.flops)
     dk = kern[f"attn_{dom.level.name}"]
+    traffic = measured_traffic(
+        os.path.join(ROOT, "patch_attention_cfg_amd", "csrc", "attention_bf16.hip"),
+        dom.level.name)
     roofline = {"bound": "mfma", "achieved": dk["tflops"], "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": dk["tflops"] / PEAK_BF16_TFLOPS, "traffic": None,
+                "unit": "TFLOP/s", "frac": dk["tflops"] / PEAK_BF16_TFLOPS, "traffic": traffic,
                 "kernel": f"attn_fwd_bf16<{dom.level.d}> ({dom.level.name}, "
                           f"{dom.flops / 1e9:.2f} GFLOP per launch)"}
 
@@ -285,9 +333,9 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": {"c2": "SDXL-1024-shaped", "c3": "SDXL-2048-shaped",
-                         "c4": "SDXL-3840-shaped", "c5": "DiT/flow-shaped"}[wl.name]
-                        + f" ({wl.name}): one patch per attention level + fused CFG step",
+            "workload": {"sdxl1024": "SDXL-1024-shaped", "sdxl2048": "SDXL-2048-shaped",
+                         "sdxl3840": "SDXL-3840-shaped", "dit1024": "DiT/flow-shaped"}[wl.name]
+                        + " patch-parallel step: one patch per attention level + fused CFG step",
             "attention": [f"{L.level.name}: B{L.level.B} H{L.level.H} n_q{L.level.n} "
                           f"N_kv{L.level.N_kv} d{L.level.d} bf16" for L in levels],
             "latent": list(wl.latent), "sampler": f"{wl.sampler}{wl.steps} fp32", "w": wl.w,

@@ -23,7 +23,7 @@
  *   [AI]  "AIGC 文生图系统如何优化扩散模型推理速度", section 1 (x_T drawn
  *         from N(0,1)) and section 3 (DDIM with eta; eta = 0 deterministic).
  *
- * Readings taken where the pages are silent (each also listed in the design doc):
+ * Readings taken where the pages are silent:
  *   - attention is plain softmax(Q K^T * scale) V with no mask or bias;
  *   - the CFG combine is g = g_u + w (g_c - g_u)  (not printed on [XD]/[HY]);
  *   - DDIM's undefined sigma_t in x0_hat is sqrt(1 - abar_t);

@@ -7,16 +7,20 @@ else on their own.
 
 Workloads (all iid Gaussian; the pages measure quality on real prompts and
 weights, which these synthetic draws stand in for):
-  c1  tiny fp32 case: N=1024 (32x32 grid), P=2, 2 heads x 64, batch 2;
-      latent 4x32x32, 10 DDIM steps, w=7.5.
-  c2  SDXL-1024 shaped, bf16: 64x64 level N=4096, 10 heads, P=4 and 32x32
-      level N=1024, 20 heads, P=4; latent 4x128x128, 50 DDIM steps, w=7.5.
-  c3  SDXL-2048 shaped: N=16384, 10 heads, P=8; latent 4x256x256, 50 steps.
-  c4  SDXL-3840 shaped: N=57600, 10 heads, P=8; latent 4x480x480, 50 steps.
-  c5  DiT/flow shaped: 4096 image tokens + 256 always-fresh text tokens,
-      24 heads x 128, P=4; latent 16x128x128, 28 Euler steps, w=3.5.
+  tiny-f32  fp32 check case: N=1024 (32x32 grid), P=2, 2 heads x 64, batch 2;
+            latent 4x32x32, 10 DDIM steps, w=7.5.
+  sdxl1024  SDXL-1024 shaped, bf16: 64x64 level N=4096, 10 heads, P=4 and
+            32x32 level N=1024, 20 heads, P=4; latent 4x128x128, 50 DDIM
+            steps, w=7.5.
+  sdxl2048  SDXL-2048 shaped: N=16384, 10 heads, P=8; latent 4x256x256, 50
+            steps.
+  sdxl3840  SDXL-3840 shaped: N=57600, 10 heads, P=8; latent 4x480x480, 50
+            steps.
+  dit1024   DiT/flow shaped: 4096 image tokens + 256 always-fresh text
+            tokens, 24 heads x 128, P=4; latent 16x128x128, 28 Euler steps,
+            w=3.5.
 Batch 2 on the attention side is the (cond, uncond) pair of classifier-free
-guidance.  Head dim is 64 except c5 (128).
+guidance.  Head dim is 64 except dit1024 (128).
 
 Draw recipe (numpy PCG64, standard_normal in float32), per attention level:
   q      [B,H,N_img,d]   queries of every image token (a patch uses its rows)
@@ -24,7 +28,8 @@ Draw recipe (numpy PCG64, standard_normal in float32), per attention level:
   nk, nv [B,H,N_kv,d]    noise;  stale = fresh + 0.05 * noise
 then every array is rounded to bf16 (nearest-even) for the bf16 workloads.
 Sampler stream (seed + 200): x_T [1,C,H,W], then per step g_c and g_u.
-Seeds: 1000 + workload number; a workload's second attention level adds 100.
+Seeds: per workload (1001 ... 1005 in the order above); a workload's second
+attention level adds 100.
 """
 from __future__ import annotations
 
@@ -84,24 +89,28 @@ class Workload:
         return c * h * w
 
 
-def _mk(num: int, levels: List[dict], latent, steps, sampler, w) -> Workload:
-    seed = 1000 + num
+def _mk(name: str, seed: int, levels: List[dict], latent, steps, sampler, w) -> Workload:
     lv = tuple(AttnLevel(seed=seed + 100 * i, **kw) for i, kw in enumerate(levels))
-    return Workload(f"c{num}", lv, latent, steps, sampler, w, seed)
+    return Workload(name, lv, latent, steps, sampler, w, seed)
 
 
 WORKLOADS = {
-    "c1": _mk(1, [dict(name="c1", B=2, H=2, N_img=1024, P=2, d=64, dtype="f32")],
-              (1, 4, 32, 32), 10, "ddim", 7.5),
-    "c2": _mk(2, [dict(name="c2a", B=2, H=10, N_img=4096, P=4, d=64),
-                  dict(name="c2b", B=2, H=20, N_img=1024, P=4, d=64)],
-              (1, 4, 128, 128), 50, "ddim", 7.5),
-    "c3": _mk(3, [dict(name="c3", B=2, H=10, N_img=16384, P=8, d=64)],
-              (1, 4, 256, 256), 50, "ddim", 7.5),
-    "c4": _mk(4, [dict(name="c4", B=2, H=10, N_img=57600, P=8, d=64)],
-              (1, 4, 480, 480), 50, "ddim", 7.5),
-    "c5": _mk(5, [dict(name="c5", B=2, H=24, N_img=4096, P=4, d=128, n_text=256)],
-              (1, 16, 128, 128), 28, "euler", 3.5),
+    "tiny-f32": _mk("tiny-f32", 1001,
+                    [dict(name="tiny-f32", B=2, H=2, N_img=1024, P=2, d=64, dtype="f32")],
+                    (1, 4, 32, 32), 10, "ddim", 7.5),
+    "sdxl1024": _mk("sdxl1024", 1002,
+                    [dict(name="sdxl1024-64x64", B=2, H=10, N_img=4096, P=4, d=64),
+                     dict(name="sdxl1024-32x32", B=2, H=20, N_img=1024, P=4, d=64)],
+                    (1, 4, 128, 128), 50, "ddim", 7.5),
+    "sdxl2048": _mk("sdxl2048", 1003,
+                    [dict(name="sdxl2048", B=2, H=10, N_img=16384, P=8, d=64)],
+                    (1, 4, 256, 256), 50, "ddim", 7.5),
+    "sdxl3840": _mk("sdxl3840", 1004,
+                    [dict(name="sdxl3840", B=2, H=10, N_img=57600, P=8, d=64)],
+                    (1, 4, 480, 480), 50, "ddim", 7.5),
+    "dit1024": _mk("dit1024", 1005,
+                   [dict(name="dit1024", B=2, H=24, N_img=4096, P=4, d=128, n_text=256)],
+                   (1, 16, 128, 128), 28, "euler", 3.5),
 }
 
 LEVELS = {lv.name: lv for wl in WORKLOADS.values() for lv in wl.levels}

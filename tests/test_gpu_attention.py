@@ -46,7 +46,7 @@ def _oracle_full(level, x, p):
                                   1.0 / level.d ** 0.5, extra)
 
 
-@pytest.mark.parametrize("name,p", [("c1", 0), ("c1", 1), ("c2b", 0), ("c2b", 3), ("c2a", 2)])
+@pytest.mark.parametrize("name,p", [("tiny-f32", 0), ("tiny-f32", 1), ("sdxl1024-32x32", 0), ("sdxl1024-32x32", 3), ("sdxl1024-64x64", 2)])
 def test_full_patch_every_element(name, p):
     G.require_gpu()
     level = inputs.LEVELS[name]
@@ -57,8 +57,8 @@ def test_full_patch_every_element(name, p):
     _check(got, want, level.dtype, f"{name} p{p}")
 
 
-@pytest.mark.parametrize("name,p,per_bh", [("c3", 0, 24), ("c3", 7, 24), ("c4", 3, 12),
-                                           ("c4", 7, 8), ("c5", 0, 24), ("c5", 2, 24)])
+@pytest.mark.parametrize("name,p,per_bh", [("sdxl2048", 0, 24), ("sdxl2048", 7, 24), ("sdxl3840", 3, 12),
+                                           ("sdxl3840", 7, 8), ("dit1024", 0, 24), ("dit1024", 2, 24)])
 def test_large_patch_sampled_rows(name, p, per_bh):
     G.require_gpu()
     level = inputs.LEVELS[name]
@@ -138,10 +138,10 @@ def test_forced_split_kv_every_element(monkeypatch, splits, B, H, nq, N, d):
 
 def test_constant_values_and_single_key_properties():
     G.require_gpu()
-    G.announce("attention properties (V=1, N_kv=1) at c2a shape")
+    G.announce("attention properties (V=1, N_kv=1) at the SDXL-1024 64x64 shape")
     torch = G.torch_mod()
-    level = inputs.LEVELS["c2a"]
-    x = _inputs("c2a")
+    level = inputs.LEVELS["sdxl1024-64x64"]
+    x = _inputs("sdxl1024-64x64")
     B, H, N, d = level.B, level.H, level.N_kv, level.d
     k_buf, v_buf = dfp.alloc_kv_buffer(B, H, N, d, torch.bfloat16)
     ones = np.ones((B, H, N, d), dtype=np.float32)
@@ -163,9 +163,9 @@ def test_constant_values_and_single_key_properties():
 def test_stale_equal_fresh_gives_full_attention_rows():
     # synchronous warm-up case: the patch's rows of full attention
     G.require_gpu()
-    G.announce("attention stale==fresh c2b")
-    level = inputs.LEVELS["c2b"]
-    x = _inputs("c2b")
+    G.announce("attention stale==fresh SDXL-1024 32x32")
+    level = inputs.LEVELS["sdxl1024-32x32"]
+    x = _inputs("sdxl1024-32x32")
     same = inputs.AttnInputs(level, x.q, x.k_fresh, x.v_fresh, x.k_fresh, x.v_fresh)
     p = 2
     got = G.run_patch(level, same, p)
@@ -175,9 +175,9 @@ def test_stale_equal_fresh_gives_full_attention_rows():
 
 def test_deterministic_bitwise():
     G.require_gpu()
-    G.announce("attention determinism c2a")
-    level = inputs.LEVELS["c2a"]
-    x = _inputs("c2a")
+    G.announce("attention determinism SDXL-1024 64x64")
+    level = inputs.LEVELS["sdxl1024-64x64"]
+    x = _inputs("sdxl1024-64x64")
     a = G.run_patch(level, x, 0)
     b = G.run_patch(level, x, 0)
     np.testing.assert_array_equal(a, b)

@@ -37,7 +37,7 @@ def _gpu_coeffs(wl, i):
     return dfp.euler_coeffs(sig[i], sig[i + 1])
 
 
-@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5"])
+@pytest.mark.parametrize("name", ["tiny-f32", "sdxl1024", "sdxl2048", "sdxl3840", "dit1024"])
 def test_sampler_run_step_by_step(name):
     G.require_gpu()
     wl = inputs.WORKLOADS[name]

@@ -18,7 +18,7 @@ def _bits(a: np.ndarray, kind: str) -> np.ndarray:
 
 @pytest.mark.parametrize("kind", ["bf16", "f32"])
 @pytest.mark.parametrize("B,H,N,d,row0,n", [
-    (2, 2, 1024, 64, 512, 512),     # c1-shaped
+    (2, 2, 1024, 64, 512, 512),     # tiny fp32 workload shape
     (2, 3, 200, 64, 3, 37),          # unaligned offset, ragged n
     (1, 2, 130, 128, 64, 66),        # d=128, ragged tail
     (2, 2, 64, 64, 0, 64),           # whole buffer
