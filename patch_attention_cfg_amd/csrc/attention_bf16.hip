@@ -499,6 +499,42 @@ __device__ __forceinline__ void raise_reference(
             }
 }
 
+// Split-KV merge, phase 2: each thread owns G 16-byte groups of the query
+// tile and folds NS splits per pass, with all G x NS coherent loads of a
+// pass in flight together (at most 24, to bound registers).
+template <int D>
+struct MergeCfg {
+    static constexpr int G = Cfg<D>::BLOCK_M * D / 4 / Cfg<D>::THREADS;
+    static constexpr int NS = 24 / G < 1 ? 1 : (24 / G > 4 ? 4 : 24 / G);
+    static_assert(G * Cfg<D>::THREADS * 4 == Cfg<D>::BLOCK_M * D, "groups tile the query tile");
+};
+
+template <int D, int N>
+__device__ __forceinline__ void merge_pass(f32x4_t (&acc)[MergeCfg<D>::G], const float *part0,
+                                           const float *wts, int s0, int tid) {
+    using C = Cfg<D>;
+    constexpr int G = MergeCfg<D>::G;
+    f32x4_t v[N][G];
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+        const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<float *>(part0) + (int64_t)(s0 + j) * C::BLOCK_M * D, 0,
+            C::BLOCK_M * D * 4, 0x00020000);
+#pragma unroll
+        for (int k = 0; k < G; ++k)
+            v[j][k] = __builtin_bit_cast(
+                f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ro, (tid + k * C::THREADS) * 16, 0,
+                                                               kCoherent));
+    }
+#pragma unroll
+    for (int j = 0; j < N; ++j)
+#pragma unroll
+        for (int k = 0; k < G; ++k) {
+            const int rr = (tid + k * C::THREADS) * 4 / D;
+            acc[k] += wts[rr * kMaxSplits + s0 + j] * v[j][k];
+        }
+}
+
 template <int D>
 struct Smem {
     char k[Cfg<D>::STAGES][Cfg<D>::K_TILE];
@@ -787,23 +823,18 @@ __global__ __launch_bounds__(Cfg<D>::THREADS, Cfg<D>::WG_PER_CU) void attn_fwd_b
             if (s < p.splits) wts[tid * kMaxSplits + s] = ms[s] * inv;
     }
     __syncthreads();
-    constexpr int G = C::BLOCK_M * D / 4 / C::THREADS;   // 16-byte groups per thread
-    static_assert(G * C::THREADS * 4 == C::BLOCK_M * D, "groups tile the query tile");
+    constexpr int G = MergeCfg<D>::G;
+    constexpr int NS = MergeCfg<D>::NS;
     f32x4_t acc[G];
 #pragma unroll
     for (int k = 0; k < G; ++k) acc[k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < p.splits; ++s) {
-        const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
-            p.part_o + (base + s) * C::BLOCK_M * D, 0, C::BLOCK_M * D * 4, 0x00020000);
-        f32x4_t v[G];
-#pragma unroll
-        for (int k = 0; k < G; ++k)
-            v[k] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                                                   ro, (tid + k * C::THREADS) * 16, 0, kCoherent));
-#pragma unroll
-        for (int k = 0; k < G; ++k) {
-            const int rr = (tid + k * C::THREADS) * 4 / D;
-            acc[k] += wts[rr * kMaxSplits + s] * v[k];
+    const float *part0 = p.part_o + base * C::BLOCK_M * D;
+    for (int s0 = 0; s0 < p.splits; s0 += NS) {
+        switch (min(NS, p.splits - s0)) {
+            case 1: merge_pass<D, 1>(acc, part0, wts, s0, tid); break;
+            case 2: merge_pass<D, (NS >= 2 ? 2 : 1)>(acc, part0, wts, s0, tid); break;
+            case 3: merge_pass<D, (NS >= 3 ? 3 : 1)>(acc, part0, wts, s0, tid); break;
+            default: merge_pass<D, NS>(acc, part0, wts, s0, tid); break;
         }
     }
 #pragma unroll
