@@ -46,6 +46,9 @@ def parse():
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-reps", type=int, default=50)
+    ap.add_argument("--sweep", action="store_true",
+                    help="time the one-device patch sweep: every patch of each level in order "
+                         "(scatter, then attention), instead of one patch")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run one plain device-to-device copy of this many MiB, the "
                          "reference kernel that scales FETCH_SIZE/WRITE_SIZE counter runs")
@@ -73,12 +76,14 @@ def measured_traffic(kernel_source: str, level_name: str):
 
 
 class Level:
-    """Device buffers of one attention level, all resident in HBM."""
+    """Device buffers of one attention level, all resident in HBM.  By
+    default the step covers one patch (one GPU's share); with `sweep` it
+    covers every patch of the level in order (the one-device patch sweep)."""
 
-    def __init__(self, level, dfp, torch, inputs):
+    def __init__(self, level, dfp, torch, inputs, sweep=False):
         x = inputs.attention_inputs(level)
         self.level = level
-        self.p = 1 if level.P > 1 else 0
+        self.patches = list(range(level.P)) if sweep else [1 if level.P > 1 else 0]
         bf = torch.bfloat16
 
         def up(a):
@@ -86,29 +91,36 @@ class Level:
 
         self.k_buf, self.v_buf = dfp.alloc_kv_buffer(level.B, level.H, level.N_kv, level.d, bf)
         dfp.kv_scatter(self.k_buf, self.v_buf, up(x.k_stale), up(x.v_stale), 0)
-        kf, vf = x.fresh_rows(self.p)
-        self.k_new, self.v_new = up(kf), up(vf)
-        self.row0 = level.row0(self.p)
+        self.fresh, self.q, self.o = [], [], []
+        for p in self.patches:
+            kf, vf = x.fresh_rows(p)
+            self.fresh.append((up(kf), up(vf), level.row0(p)))
+            self.q.append(up(x.q_patch(p)))
+            self.o.append(torch.empty_like(self.q[-1]))
         self.text = None
         if level.n_text:
             kt, vt = x.text_rows()
             self.text = (up(kt), up(vt))
-        self.q = up(x.q_patch(self.p))
-        self.o = torch.empty_like(self.q)
         self.ws = dfp.attention_workspace(level.B, level.H, level.n, level.N_kv, level.d)
         self.scale = 1.0 / level.d ** 0.5
-        self.flops = level.flops()
-        self.fresh_bytes = 2 * 2 * self.k_new.numel() * 2   # K and V, read + write
+        self.flops = level.flops() * len(self.patches)
+        self.fresh_bytes = 2 * 2 * self.fresh[0][0].numel() * 2   # K and V, read + write
         if self.text:
             self.fresh_bytes += 2 * 2 * self.text[0].numel() * 2
 
-    def scatter(self, dfp):
-        dfp.kv_scatter(self.k_buf, self.v_buf, self.k_new, self.v_new, self.row0)
-        if self.text:
+    def scatter(self, dfp, i=0):
+        if self.text and i == 0:
             dfp.kv_scatter(self.k_buf, self.v_buf, self.text[0], self.text[1], 0)
+        k, v, row0 = self.fresh[i]
+        dfp.kv_scatter(self.k_buf, self.v_buf, k, v, row0)
 
-    def attend(self, dfp):
-        dfp.patch_attention(self.o, self.q, self.k_buf, self.v_buf, self.scale, self.ws)
+    def attend(self, dfp, i=0):
+        dfp.patch_attention(self.o[i], self.q[i], self.k_buf, self.v_buf, self.scale, self.ws)
+
+    def run(self, dfp):
+        for i in range(len(self.patches)):
+            self.scatter(dfp, i)
+            self.attend(dfp, i)
 
 
 class Sampler:
@@ -227,14 +239,13 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     wl = inputs.WORKLOADS[args.workload]
-    levels = [Level(lv, dfp, torch, inputs) for lv in wl.levels]
+    levels = [Level(lv, dfp, torch, inputs, args.sweep) for lv in wl.levels]
     sampler = Sampler(wl, dfp, torch, inputs)
     torch.cuda.synchronize()
 
     def one_step(i):
         for L in levels:
-            L.scatter(dfp)
-            L.attend(dfp)
+            L.run(dfp)
         sampler.step(dfp, i)
 
     for i in range(args.warmup):
@@ -287,9 +298,9 @@ def main():
         mean, mn = time_kernel(torch, lambda L=L: L.attend(dfp), reps)
         kern[f"attn_{L.level.name}"] = {
             "us_mean": mean, "us_min": mn,
-            "tflops": L.flops / (mean * 1e-6) / 1e12,
-            "frac_bf16_peak": L.flops / (mean * 1e-6) / 1e12 / PEAK_BF16_TFLOPS,
-            "flop": L.flops}
+            "tflops": L.level.flops() / (mean * 1e-6) / 1e12,
+            "frac_bf16_peak": L.level.flops() / (mean * 1e-6) / 1e12 / PEAK_BF16_TFLOPS,
+            "flop": L.level.flops()}
         mean, mn = time_kernel(torch, lambda L=L: L.scatter(dfp), reps)
         kern[f"scatter_{L.level.name}"] = {
             "us_mean": mean, "us_min": mn,
@@ -305,7 +316,7 @@ def main():
                         "frac_hbm_peak": sampler.bytes / (mean * 1e-6) / 1e9 / PEAK_HBM_GBPS,
                         "bytes": sampler.bytes}
 
-    dom = max(levels, key=lambda L: L.flops)
+    dom = max(levels, key=lambda L: L.level.flops())
     dk = kern[f"attn_{dom.level.name}"]
     traffic = measured_traffic(
         os.path.join(ROOT, "patch_attention_cfg_amd", "csrc", "attention_bf16.hip"),
@@ -313,7 +324,7 @@ def main():
     roofline = {"bound": "mfma", "achieved": dk["tflops"], "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": dk["tflops"] / PEAK_BF16_TFLOPS, "traffic": traffic,
                 "kernel": f"attn_fwd_bf16<{dom.level.d}> ({dom.level.name}, "
-                          f"{dom.flops / 1e9:.2f} GFLOP per launch)"}
+                          f"{dom.level.flops() / 1e9:.2f} GFLOP per launch)"}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -335,7 +346,9 @@ def main():
         "config": {
             "workload": {"sdxl1024": "SDXL-1024-shaped", "sdxl2048": "SDXL-2048-shaped",
                          "sdxl3840": "SDXL-3840-shaped", "dit1024": "DiT/flow-shaped"}[wl.name]
-                        + " patch-parallel step: one patch per attention level + fused CFG step",
+                        + (" one-device patch sweep: every patch of each attention level in order"
+                           " + fused CFG step" if args.sweep else
+                           " patch-parallel step: one patch per attention level + fused CFG step"),
             "attention": [f"{L.level.name}: B{L.level.B} H{L.level.H} n_q{L.level.n} "
                           f"N_kv{L.level.N_kv} d{L.level.d} bf16" for L in levels],
             "latent": list(wl.latent), "sampler": f"{wl.sampler}{wl.steps} fp32", "w": wl.w,

@@ -166,6 +166,34 @@ def patch_attention(q_patch, k_stale, v_stale, k_fresh_rows, v_fresh_rows,
     return attention(q_patch, k_eff, v_eff, scale)
 
 
+def patch_sweep(q, k_stale, v_stale, k_fresh, v_fresh, P: int, scale: float, n_text: int = 0):
+    """One device running every patch of a layer in order ("xDiT: an
+    Inference Engine for Diffusion Transformers (DiTs) with Massive
+    Parallelism", 三.2 PipeFusion: M non-overlapping patches processed one
+    after another, each reusing the previous step's activations for the
+    patches it has not reached): patch m lands its fresh K/V, then attends
+    over fresh rows for patches 0..m and the previous step's rows for patches
+    m+1..P-1; always-fresh text rows [0, n_text) land first.
+
+    q [..., N_img, d] holds every image token's query; k/v fresh and stale
+    [..., n_text + N_img, d].  Returns the P patch outputs [..., N_img/P, d]."""
+    N_img = q.shape[-2]
+    if P <= 0 or N_img % P:
+        raise ValueError("P must divide the image tokens")
+    n = N_img // P
+    k_eff, v_eff = _f64(k_stale), _f64(v_stale)
+    if n_text:
+        k_eff = effective_kv(k_eff, _f64(k_fresh)[..., :n_text, :], 0)
+        v_eff = effective_kv(v_eff, _f64(v_fresh)[..., :n_text, :], 0)
+    outs = []
+    for m in range(P):
+        r0 = n_text + m * n
+        k_eff = effective_kv(k_eff, _f64(k_fresh)[..., r0:r0 + n, :], r0)
+        v_eff = effective_kv(v_eff, _f64(v_fresh)[..., r0:r0 + n, :], r0)
+        outs.append(attention(_f64(q)[..., m * n:(m + 1) * n, :], k_eff, v_eff, scale))
+    return outs
+
+
 # --------------------------------------------------------------------------
 # Schedules, guidance, samplers, rel-MAE
 # --------------------------------------------------------------------------

@@ -215,3 +215,57 @@ def test_rows_subset_matches_full():
     np.testing.assert_array_equal(oracle.attention_rows(q, k, v, 0.5, bh, ii), full[bh, ii])
     with pytest.raises(ValueError):
         oracle.attention_rows(q, k, v, 0.5, [6], [0])
+
+
+# ---------------------------------------------------------------- patch sweep
+def _sweep_case(seed, B=1, H=2, N_img=48, P=4, d=8, n_text=0):
+    rng = np.random.default_rng(seed)
+    N = n_text + N_img
+    q = rng.standard_normal((B, H, N_img, d))
+    kf, vf = rng.standard_normal((B, H, N, d)), rng.standard_normal((B, H, N, d))
+    ks, vs = rng.standard_normal((B, H, N, d)), rng.standard_normal((B, H, N, d))
+    return q, kf, vf, ks, vs
+
+
+@pytest.mark.parametrize("n_text", [0, 5])
+def test_sweep_last_patch_is_full_fresh_attention(n_text):
+    q, kf, vf, ks, vs = _sweep_case(11, n_text=n_text)
+    outs = oracle.patch_sweep(q, ks, vs, kf, vf, 4, 0.3, n_text)
+    full = oracle.attention(q, kf, vf, 0.3)
+    np.testing.assert_allclose(outs[-1], full[..., 36:48, :], rtol=0, atol=1e-13)
+
+
+def test_sweep_first_patch_is_displaced_patch_attention():
+    q, kf, vf, ks, vs = _sweep_case(12)
+    outs = oracle.patch_sweep(q, ks, vs, kf, vf, 4, 0.3)
+    want = oracle.patch_attention(q[..., :12, :], ks, vs, kf[..., :12, :], vf[..., :12, :], 0, 0.3)
+    np.testing.assert_array_equal(outs[0], want)
+
+
+def test_sweep_reads_fresh_up_to_its_patch_and_stale_after():
+    """Patch m's output ignores the stale rows of patches <= m and the fresh
+    rows of patches > m (perturbing either changes nothing), and does move
+    when a fresh row of patch m or a stale row after it changes."""
+    q, kf, vf, ks, vs = _sweep_case(13)
+    base = oracle.patch_sweep(q, ks, vs, kf, vf, 4, 0.3)
+    m, n = 1, 12
+    ks2, vs2 = ks.copy(), vs.copy()
+    ks2[..., :(m + 1) * n, :] += 3.0
+    vs2[..., :(m + 1) * n, :] -= 2.0
+    kf2, vf2 = kf.copy(), vf.copy()
+    kf2[..., (m + 1) * n:, :] += 3.0
+    vf2[..., (m + 1) * n:, :] -= 2.0
+    np.testing.assert_array_equal(oracle.patch_sweep(q, ks2, vs2, kf2, vf2, 4, 0.3)[m], base[m])
+    vf3 = vf.copy()
+    vf3[..., m * n, :] += 1.0
+    assert np.abs(oracle.patch_sweep(q, ks, vs, kf, vf3, 4, 0.3)[m] - base[m]).max() > 1e-6
+    vs3 = vs.copy()
+    vs3[..., (m + 1) * n, :] += 1.0
+    assert np.abs(oracle.patch_sweep(q, ks, vs3, kf, vf, 4, 0.3)[m] - base[m]).max() > 1e-6
+
+
+def test_sweep_with_stale_equal_fresh_is_full_attention():
+    q, kf, vf, _, _ = _sweep_case(14, n_text=3)
+    outs = oracle.patch_sweep(q, kf, vf, kf, vf, 4, 0.3, 3)
+    full = oracle.attention(q, kf, vf, 0.3)
+    np.testing.assert_allclose(np.concatenate(outs, axis=-2), full, rtol=0, atol=1e-13)
