@@ -49,6 +49,9 @@ def parse():
     ap.add_argument("--sweep", action="store_true",
                     help="time the one-device patch sweep: every patch of each level in order "
                          "(scatter, then attention), instead of one patch")
+    ap.add_argument("--eta", type=float, default=0.0,
+                    help="DDIM noise scale (DDIM workloads): > 0 runs the fused step with the "
+                         "sampler-noise term (dfp_cfg_step_noise)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run one plain device-to-device copy of this many MiB, the "
                          "reference kernel that scales FETCH_SIZE/WRITE_SIZE counter runs")
@@ -124,15 +127,19 @@ class Level:
 
 
 class Sampler:
-    """Latent, per-step prediction pairs and coefficients, all in HBM."""
+    """Latent, per-step prediction pairs (and sampler noise when eta > 0) and
+    coefficients, all in HBM."""
 
-    def __init__(self, wl, dfp, torch, inputs):
+    def __init__(self, wl, dfp, torch, inputs, eta=0.0):
         st = inputs.sampler_stream(wl)
         self.wl = wl
+        self.eta = eta if wl.sampler == "ddim" else 0.0
         self.x = torch.from_numpy(st.x_T).cuda()
         pairs = [st.next_pair() for _ in range(wl.steps)]
         self.g_c = [torch.from_numpy(a).cuda() for a, _ in pairs]
         self.g_u = [torch.from_numpy(b).cuda() for _, b in pairs]
+        self.z = ([torch.from_numpy(st.next_noise()).cuda() for _ in range(wl.steps)]
+                  if self.eta > 0 else None)
         self.coeffs = []
         if wl.sampler == "ddim":
             abar = dfp.scaled_linear_abar(1000, 0.00085, 0.012)
@@ -140,19 +147,25 @@ class Sampler:
             S = wl.steps
             for i in range(S):
                 a_prev = 1.0 if i == S - 1 else abar[ts[S - 2 - i]]
-                self.coeffs.append(dfp.ddim_coeffs(abar[ts[S - 1 - i]], a_prev))
+                self.coeffs.append(dfp.ddim_eta_coeffs(abar[ts[S - 1 - i]], a_prev, self.eta))
         else:
             for i in range(wl.steps):
-                self.coeffs.append(dfp.euler_coeffs(1 - i / wl.steps, 1 - (i + 1) / wl.steps))
+                self.coeffs.append(dfp.euler_coeffs(1 - i / wl.steps, 1 - (i + 1) / wl.steps)
+                                   + (0.0,))
         batch = wl.latent[0]
         self.ws = dfp.cfg_workspace(wl.n_latent, batch)
         self.r = torch.empty((wl.steps, batch), dtype=torch.float32, device="cuda")
-        self.bytes = 16 * self.x.numel()
+        self.bytes = (20 if self.z else 16) * self.x.numel()
 
     def step(self, dfp, i):
         k = i % self.wl.steps
-        c_x, c_e = self.coeffs[k]
-        dfp.cfg_step(self.x, self.g_c[k], self.g_u[k], self.wl.w, c_x, c_e, self.r[k], self.ws)
+        c_x, c_e, c_z = self.coeffs[k]
+        if self.z:
+            dfp.cfg_step_noise(self.x, self.g_c[k], self.g_u[k], self.z[k], self.wl.w, c_x, c_e,
+                               c_z, self.r[k], self.ws)
+        else:
+            dfp.cfg_step(self.x, self.g_c[k], self.g_u[k], self.wl.w, c_x, c_e, self.r[k],
+                         self.ws)
 
 
 def time_kernel(torch, fn, reps, batches=3):
@@ -240,7 +253,7 @@ def main():
         del src, dst
     wl = inputs.WORKLOADS[args.workload]
     levels = [Level(lv, dfp, torch, inputs, args.sweep) for lv in wl.levels]
-    sampler = Sampler(wl, dfp, torch, inputs)
+    sampler = Sampler(wl, dfp, torch, inputs, args.eta)
     torch.cuda.synchronize()
 
     def one_step(i):
@@ -351,7 +364,8 @@ def main():
                            " patch-parallel step: one patch per attention level + fused CFG step"),
             "attention": [f"{L.level.name}: B{L.level.B} H{L.level.H} n_q{L.level.n} "
                           f"N_kv{L.level.N_kv} d{L.level.d} bf16" for L in levels],
-            "latent": list(wl.latent), "sampler": f"{wl.sampler}{wl.steps} fp32", "w": wl.w,
+            "latent": list(wl.latent), "sampler": f"{wl.sampler}{wl.steps} fp32"
+            + (f" eta={sampler.eta}" if sampler.eta > 0 else ""), "w": wl.w,
             "launch": launch},
         "cfg_step_gbps": kern["cfg_step"]["gbps"],
         "cfg_step_frac_hbm_peak": kern["cfg_step"]["frac_hbm_peak"],

@@ -177,6 +177,21 @@ dfp_status dfp_cfg_step(float *x, const float *g_c, const float *g_u,
                         double c_e, float *relmae_out, void *workspace,
                         size_t ws_bytes, hipStream_t stream);
 
+/* Fused step with a noise term: DDIM with eta > 0 ([AI] section 3, the
+ * sigma_eta * z term of the same update).  Per element:
+ *   x <- c_x * x + c_e * g + c_z * z
+ * with g the guided prediction as above and z a standard-normal draw the
+ * caller supplies (same shape and layout as x; drawn by the caller so any
+ * generator can feed the step).  See dfp_ddim_eta_coeffs for (c_x, c_e, c_z).
+ * rel-MAE, workspace rules and errors are those of dfp_cfg_step, plus
+ * INVALID_ARG for a null z or non-finite c_z.  Reads 20 bytes and writes 4
+ * per element. */
+dfp_status dfp_cfg_step_noise(float *x, const float *g_c, const float *g_u,
+                              const float *z, int64_t n_per_image, int batch,
+                              float w, double c_x, double c_e, double c_z,
+                              float *relmae_out, void *workspace,
+                              size_t ws_bytes, hipStream_t stream);
+
 /* (a7) rel-MAE alone ([HY] 关键设计 2):
  *   out[b] = sum |g_c - g_u| / sum |g_u|  over image b's n_per_image values.
  * Same reduction, workspace rules and errors as dfp_cfg_step. */
@@ -199,6 +214,19 @@ size_t dfp_workspace_bytes(int op, int64_t n_per_image, int batch, int B, int H,
  * Pass abar_prev = 1 on the last step (the step that returns the x0 estimate).
  * INVALID_ARG unless 0 < abar_t <= 1 and 0 < abar_prev <= 1, or a null output. */
 dfp_status dfp_ddim_coeffs(double abar_t, double abar_prev, double *c_x, double *c_e);
+
+/* [AI] section 3 DDIM with noise scale eta, folded to
+ * x' = c_x x + c_e g + c_z z:
+ *   sigma = eta sqrt((1 - abar_prev)/(1 - abar_t) (1 - abar_t/abar_prev))
+ *   c_x = sqrt(abar_prev / abar_t)
+ *   c_e = sqrt(1 - abar_prev - sigma^2) - sqrt(abar_prev) sqrt(1 - abar_t) / sqrt(abar_t)
+ *   c_z = sigma
+ * eta = 0 gives dfp_ddim_coeffs with c_z = 0; abar_prev = 1 (last step) gives
+ * c_z = 0 for any eta.  INVALID_ARG unless 0 < abar_t < 1, abar_t <= abar_prev
+ * <= 1, eta >= 0 finite and 1 - abar_prev - sigma^2 >= 0 (always so for
+ * eta <= 1), or for a null output. */
+dfp_status dfp_ddim_eta_coeffs(double abar_t, double abar_prev, double eta, double *c_x,
+                               double *c_e, double *c_z);
 
 /* Euler on sigma: x' = x + (sigma_next - sigma) v, i.e. c_x = 1,
  * c_e = sigma_next - sigma.  INVALID_ARG for non-finite input or null output. */

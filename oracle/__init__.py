@@ -56,6 +56,7 @@ def _load():
         "oracle_ddim_timesteps": (None, [i64, i64, I]),
         "oracle_cfg_combine": (None, [D, D, i64, dbl, D]),
         "oracle_ddim_step": (None, [D, D, i64, dbl, dbl, cint]),
+        "oracle_ddim_step_eta": (None, [D, D, D, i64, dbl, dbl, dbl, cint]),
         "oracle_flow_sigmas": (None, [i64, D]),
         "oracle_euler_step": (None, [D, D, i64, dbl, dbl]),
         "oracle_relmae": (dbl, [D, D, i64]),
@@ -239,6 +240,17 @@ def ddim_step(x, eps, abar_t: float, abar_prev: float, last: bool) -> np.ndarray
     return x
 
 
+def ddim_step_eta(x, eps, z, abar_t: float, abar_prev: float, eta: float,
+                  last: bool) -> np.ndarray:
+    x = _f64(x).copy()
+    eps, z = _f64(eps), _f64(z)
+    if eps.shape != x.shape or z.shape != x.shape:
+        raise ValueError("x, eps and z shapes differ")
+    _load().oracle_ddim_step_eta(_pd(x), _pd(eps), _pd(z), x.size, float(abar_t),
+                                 float(abar_prev), float(eta), int(bool(last)))
+    return x
+
+
 def euler_step(x, v, sigma: float, sigma_next: float) -> np.ndarray:
     x = _f64(x).copy()
     v = _f64(v)
@@ -279,6 +291,14 @@ class DDIMSchedule:
         g = cfg_combine(g_c, g_u, w)
         abar_t, abar_prev, last = self.step_args(i)
         return ddim_step(x, g, abar_t, abar_prev, last), r
+
+    def step_eta(self, x, g_c, g_u, w: float, i: int, eta: float, z):
+        """One guided step of DDIM with noise scale eta and standard-normal
+        draw z: returns (x_next, rel-MAE of this step's pair)."""
+        r = relmae(g_c, g_u)
+        g = cfg_combine(g_c, g_u, w)
+        abar_t, abar_prev, last = self.step_args(i)
+        return ddim_step_eta(x, g, z, abar_t, abar_prev, eta, last), r
 
 
 class EulerSchedule:

@@ -237,6 +237,32 @@ void oracle_ddim_step(double *x, const double *eps, int64_t n, double abar_t,
     }
 }
 
+/* [AI] section 3, DDIM with a general eta (the same listing): the noise
+ * scale of the step is
+ *   sigma_eta = eta * sqrt((1 - abar_prev) / (1 - abar_t) * (1 - abar_t / abar_prev))
+ * and the step adds sigma_eta * z for a standard-normal draw z (passed in):
+ *   x0_hat  = (x_t - sigma_t * eps) / sqrt(abar_t)
+ *   not last: x_{t-1} = sqrt(abar_prev) x0_hat
+ *                      + sqrt(1 - abar_prev - sigma_eta^2) eps + sigma_eta z
+ *   last:     x_{t-1} = x0_hat                                            */
+void oracle_ddim_step_eta(double *x, const double *eps, const double *z, int64_t n,
+                          double abar_t, double abar_prev, double eta, int last)
+{
+    double sigma_t = sqrt(1.0 - abar_t);
+    double sqrt_abar_t = sqrt(abar_t);
+    double sigma_eta =
+        eta * sqrt((1.0 - abar_prev) / (1.0 - abar_t) * (1.0 - abar_t / abar_prev));
+    for (int64_t i = 0; i < n; ++i) {
+        double x0_hat = (x[i] - sigma_t * eps[i]) / sqrt_abar_t;
+        if (last)
+            x[i] = x0_hat;
+        else
+            x[i] = sqrt(abar_prev) * x0_hat +
+                   sqrt(1.0 - abar_prev - sigma_eta * sigma_eta) * eps[i] +
+                   sigma_eta * z[i];
+    }
+}
+
 /* [HY] 损失函数/训练策略: flow-matching models predict a velocity v in place
  * of eps.  Integrator (not on the pages): Euler on sigma,
  *   x <- x + (sigma_next - sigma) * v,  sigma_i = 1 - i/S, i = 0..S. */

@@ -50,11 +50,14 @@ __device__ __forceinline__ void accum(float &num, float &den, float c, float u) 
     den += fabsf(u);
 }
 
-template <bool UPDATE, bool VEC>
+// NOISE adds c_z * z (a caller-drawn standard-normal array shaped like x)
+// to the update: DDIM with eta > 0.
+template <bool UPDATE, bool VEC, bool NOISE>
 __global__ __launch_bounds__(kThreads) void cfg_step_kernel(
     float *__restrict__ x, const float *__restrict__ g_c, const float *__restrict__ g_u,
-    int64_t n, float w, float c_x, float c_e, double *__restrict__ partials,
-    unsigned *__restrict__ counter, float *__restrict__ out, int reduce) {
+    const float *__restrict__ z, int64_t n, float w, float c_x, float c_e, float c_z,
+    double *__restrict__ partials, unsigned *__restrict__ counter, float *__restrict__ out,
+    int reduce) {
     const int img = blockIdx.y;
     const int blk = blockIdx.x;
     const int nblk = gridDim.x;
@@ -67,9 +70,10 @@ __global__ __launch_bounds__(kThreads) void cfg_step_kernel(
         float4 *x4 = reinterpret_cast<float4 *>(x + base);
         const float4 *c4 = reinterpret_cast<const float4 *>(g_c + base);
         const float4 *u4 = reinterpret_cast<const float4 *>(g_u + base);
+        const float4 *z4 = reinterpret_cast<const float4 *>(z + (NOISE ? base : 0));
         const int64_t step = (int64_t)nblk * kThreads * kUnroll;
         for (int64_t i0 = (int64_t)blk * kThreads * kUnroll + tid; i0 < n4; i0 += step) {
-            float4 cv[kUnroll], uv[kUnroll], xv[kUnroll];
+            float4 cv[kUnroll], uv[kUnroll], xv[kUnroll], zv[kUnroll];
 #pragma unroll
             for (int k = 0; k < kUnroll; ++k) {
                 const int64_t i = i0 + (int64_t)k * kThreads;
@@ -77,6 +81,7 @@ __global__ __launch_bounds__(kThreads) void cfg_step_kernel(
                     cv[k] = c4[i];
                     uv[k] = u4[i];
                     if (UPDATE) xv[k] = x4[i];
+                    if (NOISE) zv[k] = z4[i];
                 }
             }
 #pragma unroll
@@ -93,6 +98,12 @@ __global__ __launch_bounds__(kThreads) void cfg_step_kernel(
                         r.y = fmaf(c_x, xv[k].y, c_e * fmaf(w, cv[k].y - uv[k].y, uv[k].y));
                         r.z = fmaf(c_x, xv[k].z, c_e * fmaf(w, cv[k].z - uv[k].z, uv[k].z));
                         r.w = fmaf(c_x, xv[k].w, c_e * fmaf(w, cv[k].w - uv[k].w, uv[k].w));
+                        if (NOISE) {
+                            r.x = fmaf(c_z, zv[k].x, r.x);
+                            r.y = fmaf(c_z, zv[k].y, r.y);
+                            r.z = fmaf(c_z, zv[k].z, r.z);
+                            r.w = fmaf(c_z, zv[k].w, r.w);
+                        }
                         x4[i] = r;
                     }
                 }
@@ -106,7 +117,10 @@ __global__ __launch_bounds__(kThreads) void cfg_step_kernel(
         for (int64_t i = (int64_t)blk * kThreads + tid; i < n; i += step) {
             const float c = cs[i], u = us[i];
             accum(num, den, c, u);
-            if (UPDATE) xs[i] = fmaf(c_x, xs[i], c_e * fmaf(w, c - u, u));
+            if (UPDATE) {
+                const float r = fmaf(c_x, xs[i], c_e * fmaf(w, c - u, u));
+                xs[i] = NOISE ? fmaf(c_z, z[base + i], r) : r;
+            }
         }
     }
 
@@ -171,11 +185,12 @@ size_t workspace_need(int64_t n_per_image, int batch) {
 }
 
 template <bool UPDATE>
-dfp_status launch(float *x, const float *g_c, const float *g_u, int64_t n, int batch,
-                  float w, float c_x, float c_e, float *out, void *ws, size_t ws_bytes,
-                  hipStream_t stream) {
+dfp_status launch(float *x, const float *g_c, const float *g_u, const float *z, int64_t n,
+                  int batch, float w, float c_x, float c_e, float c_z, float *out, void *ws,
+                  size_t ws_bytes, hipStream_t stream) {
     if (!g_c || !g_u || (UPDATE && !x) || n <= 0 || batch <= 0 || batch > 65535)
         return DFP_ERR_INVALID_ARG;
+    const bool noise = UPDATE && z != nullptr;
     const int reduce = out != nullptr;
     if (reduce && (!ws || ws_bytes < workspace_need(n, batch) ||
                    (reinterpret_cast<uintptr_t>(ws) % 256) != 0))
@@ -183,17 +198,23 @@ dfp_status launch(float *x, const float *g_c, const float *g_u, int64_t n, int b
     const Grid g = plan(n);
     const bool vec = (n % 4 == 0) && (reinterpret_cast<uintptr_t>(g_c) % 16 == 0) &&
                      (reinterpret_cast<uintptr_t>(g_u) % 16 == 0) &&
-                     (!UPDATE || reinterpret_cast<uintptr_t>(x) % 16 == 0);
+                     (!UPDATE || reinterpret_cast<uintptr_t>(x) % 16 == 0) &&
+                     (!noise || reinterpret_cast<uintptr_t>(z) % 16 == 0);
     unsigned *counter = reduce ? static_cast<unsigned *>(ws) : nullptr;
     double *partials =
         reduce ? reinterpret_cast<double *>(static_cast<char *>(ws) + kCounterBytes) : nullptr;
     dim3 grid((unsigned)g.blocks_per_image, (unsigned)batch);
-    if (vec)
-        hipLaunchKernelGGL((cfg_step_kernel<UPDATE, true>), grid, dim3(kThreads), 0, stream, x,
-                           g_c, g_u, n, w, c_x, c_e, partials, counter, out, reduce);
-    else
-        hipLaunchKernelGGL((cfg_step_kernel<UPDATE, false>), grid, dim3(kThreads), 0, stream, x,
-                           g_c, g_u, n, w, c_x, c_e, partials, counter, out, reduce);
+#define DFP_CFG_LAUNCH(V, N)                                                                 \
+    hipLaunchKernelGGL((cfg_step_kernel<UPDATE, V, N>), grid, dim3(kThreads), 0, stream, x,   \
+                       g_c, g_u, z, n, w, c_x, c_e, c_z, partials, counter, out, reduce)
+    if (noise) {
+        if (vec) DFP_CFG_LAUNCH(true, true);
+        else DFP_CFG_LAUNCH(false, true);
+    } else {
+        if (vec) DFP_CFG_LAUNCH(true, false);
+        else DFP_CFG_LAUNCH(false, false);
+    }
+#undef DFP_CFG_LAUNCH
     return dfp::launch_status();
 }
 
@@ -210,14 +231,25 @@ extern "C" dfp_status dfp_cfg_step(float *x, const float *g_c, const float *g_u,
                                    size_t ws_bytes, hipStream_t stream) {
     if (!std::isfinite(w) || !std::isfinite(c_x) || !std::isfinite(c_e))
         return DFP_ERR_INVALID_ARG;
-    return launch<true>(x, g_c, g_u, n_per_image, batch, w, (float)c_x, (float)c_e, relmae_out,
-                        workspace, ws_bytes, stream);
+    return launch<true>(x, g_c, g_u, nullptr, n_per_image, batch, w, (float)c_x, (float)c_e,
+                        0.f, relmae_out, workspace, ws_bytes, stream);
+}
+
+extern "C" dfp_status dfp_cfg_step_noise(float *x, const float *g_c, const float *g_u,
+                                         const float *z, int64_t n_per_image, int batch, float w,
+                                         double c_x, double c_e, double c_z, float *relmae_out,
+                                         void *workspace, size_t ws_bytes, hipStream_t stream) {
+    if (!z || !std::isfinite(w) || !std::isfinite(c_x) || !std::isfinite(c_e) ||
+        !std::isfinite(c_z))
+        return DFP_ERR_INVALID_ARG;
+    return launch<true>(x, g_c, g_u, z, n_per_image, batch, w, (float)c_x, (float)c_e,
+                        (float)c_z, relmae_out, workspace, ws_bytes, stream);
 }
 
 extern "C" dfp_status dfp_relmae(const float *g_c, const float *g_u, int64_t n_per_image,
                                  int batch, float *out, void *workspace, size_t ws_bytes,
                                  hipStream_t stream) {
     if (!out) return DFP_ERR_INVALID_ARG;
-    return launch<false>(nullptr, g_c, g_u, n_per_image, batch, 0.f, 0.f, 0.f, out, workspace,
-                         ws_bytes, stream);
+    return launch<false>(nullptr, g_c, g_u, nullptr, n_per_image, batch, 0.f, 0.f, 0.f, 0.f,
+                         out, workspace, ws_bytes, stream);
 }

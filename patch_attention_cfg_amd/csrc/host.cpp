@@ -41,6 +41,22 @@ dfp_status dfp_ddim_coeffs(double abar_t, double abar_prev, double *c_x, double 
     return DFP_OK;
 }
 
+dfp_status dfp_ddim_eta_coeffs(double abar_t, double abar_prev, double eta, double *c_x,
+                               double *c_e, double *c_z) {
+    if (!c_x || !c_e || !c_z) return DFP_ERR_INVALID_ARG;
+    if (!(abar_t > 0.0 && abar_t < 1.0) || !(abar_prev > 0.0 && abar_prev <= 1.0) ||
+        !(abar_t <= abar_prev) || !(eta >= 0.0) || !std::isfinite(eta))
+        return DFP_ERR_INVALID_ARG;
+    const double st = std::sqrt(abar_t), sp = std::sqrt(abar_prev);
+    const double s2 = eta * eta * (1.0 - abar_prev) / (1.0 - abar_t) * (1.0 - abar_t / abar_prev);
+    const double keep = 1.0 - abar_prev - s2;
+    if (keep < 0.0) return DFP_ERR_INVALID_ARG;
+    *c_x = sp / st;
+    *c_e = std::sqrt(keep) - sp * std::sqrt(1.0 - abar_t) / st;
+    *c_z = std::sqrt(s2);
+    return DFP_OK;
+}
+
 dfp_status dfp_euler_coeffs(double sigma, double sigma_next, double *c_x, double *c_e) {
     if (!c_x || !c_e) return DFP_ERR_INVALID_ARG;
     if (!std::isfinite(sigma) || !std::isfinite(sigma_next)) return DFP_ERR_INVALID_ARG;

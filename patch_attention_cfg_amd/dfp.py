@@ -28,9 +28,11 @@ SIGNATURES = {
     "dfp_kv_scatter": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P]),
     "dfp_patch_attention": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _SZ, _P]),
     "dfp_cfg_step": (_I, [_P, _P, _P, _I64, _I, _F, _D, _D, _P, _P, _SZ, _P]),
+    "dfp_cfg_step_noise": (_I, [_P, _P, _P, _P, _I64, _I, _F, _D, _D, _D, _P, _P, _SZ, _P]),
     "dfp_relmae": (_I, [_P, _P, _I64, _I, _P, _P, _SZ, _P]),
     "dfp_workspace_bytes": (_SZ, [_I, _I64, _I, _I, _I, _I, _I, _I]),
     "dfp_ddim_coeffs": (_I, [_D, _D, _P, _P]),
+    "dfp_ddim_eta_coeffs": (_I, [_D, _D, _D, _P, _P, _P]),
     "dfp_euler_coeffs": (_I, [_D, _D, _P, _P]),
     "dfp_scaled_linear_abar": (_I, [_I, _D, _D, _P]),
     "dfp_ddim_timesteps": (_I, [_I, _I, _P]),
@@ -118,6 +120,13 @@ def ddim_coeffs(abar_t: float, abar_prev: float):
     _check(lib().dfp_ddim_coeffs(abar_t, abar_prev, ctypes.byref(cx), ctypes.byref(ce)),
            "dfp_ddim_coeffs")
     return cx.value, ce.value
+
+
+def ddim_eta_coeffs(abar_t: float, abar_prev: float, eta: float):
+    cx, ce, cz = ctypes.c_double(), ctypes.c_double(), ctypes.c_double()
+    _check(lib().dfp_ddim_eta_coeffs(abar_t, abar_prev, eta, ctypes.byref(cx), ctypes.byref(ce),
+                                     ctypes.byref(cz)), "dfp_ddim_eta_coeffs")
+    return cx.value, ce.value, cz.value
 
 
 def euler_coeffs(sigma: float, sigma_next: float):
@@ -214,6 +223,17 @@ def cfg_step(x, g_c, g_u, w: float, c_x: float, c_e: float, relmae_out=None, wor
                             float(c_e), _ptr(relmae_out), _ptr(workspace), ws_bytes,
                             _stream(stream))
     _check(st, "dfp_cfg_step")
+
+
+def cfg_step_noise(x, g_c, g_u, z, w: float, c_x: float, c_e: float, c_z: float,
+                   relmae_out=None, workspace=None, stream=None) -> None:
+    batch = x.shape[0]
+    n = x.numel() // batch
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib().dfp_cfg_step_noise(_ptr(x), _ptr(g_c), _ptr(g_u), _ptr(z), n, batch, float(w),
+                                  float(c_x), float(c_e), float(c_z), _ptr(relmae_out),
+                                  _ptr(workspace), ws_bytes, _stream(stream))
+    _check(st, "dfp_cfg_step_noise")
 
 
 def relmae(g_c, g_u, out, workspace, stream=None) -> None:

@@ -27,7 +27,8 @@ Draw recipe (numpy PCG64, standard_normal in float32), per attention level:
   k, v   [B,H,N_kv,d]    this step's ("fresh") keys / values, text rows first
   nk, nv [B,H,N_kv,d]    noise;  stale = fresh + 0.05 * noise
 then every array is rounded to bf16 (nearest-even) for the bf16 workloads.
-Sampler stream (seed + 200): x_T [1,C,H,W], then per step g_c and g_u.
+Sampler stream (seed + 200): x_T [1,C,H,W], then per step g_c and g_u;
+sampler noise z for DDIM with eta > 0 comes from its own stream (seed + 300).
 Seeds: per workload (1001 ... 1005 in the order above); a workload's second
 attention level adds 100.
 """
@@ -203,6 +204,7 @@ class SamplerStream:
     workload: Workload
     rng: np.random.Generator = field(repr=False)
     x_T: np.ndarray = None
+    noise_rng: np.random.Generator = field(default=None, repr=False)
 
     def next_pair(self):
         """This step's (g_c, g_u), each shaped like x, float32 N(0,1)."""
@@ -211,9 +213,15 @@ class SamplerStream:
         g_u = self.rng.standard_normal(shape, dtype=np.float32)
         return g_c, g_u
 
+    def next_noise(self):
+        """This step's sampler noise z (DDIM with eta > 0), shaped like x,
+        float32 N(0,1), from its own stream so the prediction draws do not
+        depend on whether noise is drawn."""
+        return self.noise_rng.standard_normal(self.workload.latent, dtype=np.float32)
+
 
 def sampler_stream(workload: Workload, seed: int | None = None) -> SamplerStream:
     s = workload.seed + 200 if seed is None else seed
     rng = np.random.Generator(np.random.PCG64(s))
     x_T = rng.standard_normal(workload.latent, dtype=np.float32)
-    return SamplerStream(workload, rng, x_T)
+    return SamplerStream(workload, rng, x_T, np.random.Generator(np.random.PCG64(s + 100)))

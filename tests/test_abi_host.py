@@ -170,3 +170,28 @@ def test_coefficient_edge_cases(L):
         dfp.euler_coeffs(math.nan, 0.0)
     with pytest.raises(dfp.DFPError):
         dfp.scaled_linear_abar(1, 0.1, 0.2)
+
+
+@pytest.mark.parametrize("eta", [0.0, 0.5, 1.0])
+def test_folded_eta_coefficients_reproduce_two_stage_step(L, eta):
+    # x' = c_x x + c_e g + c_z z must equal the oracle's literal eta step
+    sch = oracle.DDIMSchedule(50)
+    r = np.random.Generator(np.random.PCG64(77))
+    x, g, z = (r.standard_normal(256) for _ in range(3))
+    for i in range(50):
+        at, ap, last = sch.step_args(i)
+        cx, ce, cz = dfp.ddim_eta_coeffs(at, ap, eta)
+        want = oracle.ddim_step_eta(x, g, z, at, ap, eta, last)
+        np.testing.assert_allclose(cx * x + ce * g + cz * z, want, rtol=1e-12, atol=1e-12)
+
+
+def test_eta_coefficient_edges(L):
+    assert dfp.ddim_eta_coeffs(0.3, 0.6, 0.0) == pytest.approx(dfp.ddim_coeffs(0.3, 0.6) + (0.0,),
+                                                               abs=1e-15)
+    assert dfp.ddim_eta_coeffs(0.3, 1.0, 1.0)[2] == 0.0          # last step: no noise
+    with pytest.raises(dfp.DFPError):
+        dfp.ddim_eta_coeffs(0.3, 0.6, 3.0)                       # sigma^2 > 1 - abar_prev
+    with pytest.raises(dfp.DFPError):
+        dfp.ddim_eta_coeffs(0.6, 0.3, 0.5)                       # abar_t > abar_prev
+    with pytest.raises(dfp.DFPError):
+        dfp.ddim_eta_coeffs(0.3, 0.6, -0.1)

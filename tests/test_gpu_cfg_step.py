@@ -76,6 +76,39 @@ def test_sampler_run_step_by_step(name):
     assert np.isfinite(x_host).all()
 
 
+@pytest.mark.parametrize("name,eta", [("tiny-f32", 1.0), ("sdxl1024", 0.5), ("sdxl3840", 1.0)])
+def test_ddim_eta_run_step_by_step(name, eta):
+    """DDIM with eta > 0 through dfp_cfg_step_noise: every step against the
+    oracle's literal eta step, on the same fp32 x_t, predictions and noise."""
+    G.require_gpu()
+    wl = inputs.WORKLOADS[name]
+    G.announce(f"cfg step with noise {name}: eta {eta}, {wl.steps} steps on {wl.latent}")
+    torch = G.torch_mod()
+    stream = inputs.sampler_stream(wl)
+    sch = oracle.DDIMSchedule(wl.steps)
+    batch = wl.latent[0]
+    ws = dfp.cfg_workspace(wl.n_latent, batch)
+    r_dev = torch.empty(batch, dtype=torch.float32, device="cuda")
+    x_host = stream.x_T.astype(np.float32)
+    for i in range(wl.steps):
+        g_c, g_u = stream.next_pair()
+        z = stream.next_noise()
+        at, ap, last = sch.step_args(i)
+        c_x, c_e, c_z = dfp.ddim_eta_coeffs(at, ap, eta)
+        x = torch.from_numpy(x_host).cuda()
+        dfp.cfg_step_noise(x, torch.from_numpy(g_c).cuda(), torch.from_numpy(g_u).cuda(),
+                           torch.from_numpy(z).cuda(), wl.w, c_x, c_e, c_z, r_dev, ws)
+        torch.cuda.synchronize()
+        got = x.cpu().numpy()
+        want, r_want = sch.step_eta(x_host, g_c, g_u, wl.w, i, eta, z)
+        err = G.rel_l2(got, want)
+        rerr = abs(float(r_dev[0].item()) - r_want) / abs(r_want)
+        assert err <= STEP_REL_L2, f"{name} step {i}: rel L2 {err}"
+        assert rerr <= RELMAE_REL, f"{name} step {i}: rel-MAE error {rerr}"
+        x_host = got
+    assert np.isfinite(x_host).all()
+
+
 def test_relmae_alone_batch_and_determinism():
     G.require_gpu()
     G.announce("relmae batch=3, determinism")

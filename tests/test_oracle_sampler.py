@@ -195,3 +195,55 @@ def test_relmae_iid_gaussian_near_sqrt2():
     r = _rng(7)
     val = oracle.relmae(r.standard_normal(200000), r.standard_normal(200000))
     assert abs(val - math.sqrt(2)) < 0.01
+
+
+# ------------------------------------------------------------ DDIM with eta > 0
+def test_ddim_eta_zero_is_the_deterministic_step():
+    rng = np.random.default_rng(21)
+    x, e, z = (rng.standard_normal(64) for _ in range(3))
+    for last in (False, True):
+        np.testing.assert_array_equal(oracle.ddim_step_eta(x, e, z, 0.3, 0.7, 0.0, last),
+                                      oracle.ddim_step(x, e, 0.3, 0.7, last))
+
+
+@pytest.mark.parametrize("eta", [0.25, 0.5, 1.0])
+@pytest.mark.parametrize("abar_t,abar_prev", [(0.2, 0.45), (0.004660098513077238, 0.016009281935883385),
+                                              (0.8803525730500632, 0.99915)])
+def test_ddim_eta_preserves_the_forward_marginal(eta, abar_t, abar_prev):
+    """Whatever eta, a step from x_t = sqrt(abar_t) x0 + sqrt(1 - abar_t) eps
+    with the exact eps lands on sqrt(abar_prev) x0 + c_e eps + c_z z with
+    c_e^2 + c_z^2 = 1 - abar_prev: the same N(sqrt(abar_prev) x0, 1 - abar_prev)
+    marginal as the forward process at the previous timestep (DDIM's defining
+    property).  The coefficients are read off the oracle by unit inputs."""
+    x0 = np.array([0.7])
+    unit, zero = np.array([1.0]), np.array([0.0])
+    def run(eps, z):
+        x = np.sqrt(abar_t) * x0 + np.sqrt(1.0 - abar_t) * eps
+        return oracle.ddim_step_eta(x, eps, z, abar_t, abar_prev, eta, False)[0]
+    base = run(zero, zero)
+    np.testing.assert_allclose(base, np.sqrt(abar_prev) * x0[0], rtol=0, atol=1e-13)
+    c_e = run(unit, zero) - base
+    c_z = run(zero, unit) - base
+    assert c_z > 0
+    np.testing.assert_allclose(c_e ** 2 + c_z ** 2, 1.0 - abar_prev, rtol=1e-12, atol=0)
+
+
+def test_ddim_eta_one_noise_is_the_posterior_scale():
+    """At eta = 1 the added noise has the scale of the Gaussian posterior
+    q(x_prev | x_t, x0) of the forward process, derived here from the forward
+    process alone: with a = abar_prev, b = abar_t / abar_prev, the posterior
+    variance is (1 - a) (1 - b) / (1 - a b)."""
+    a_t, a_p = 0.2, 0.45
+    unit, zero = np.array([1.0]), np.array([0.0])
+    x = np.array([0.3])
+    c_z = (oracle.ddim_step_eta(x, zero, unit, a_t, a_p, 1.0, False)
+           - oracle.ddim_step_eta(x, zero, zero, a_t, a_p, 1.0, False))[0]
+    a, b = a_p, a_t / a_p
+    np.testing.assert_allclose(c_z ** 2, (1 - a) * (1 - b) / (1 - a * b), rtol=1e-13)
+
+
+def test_ddim_eta_last_step_adds_no_noise():
+    rng = np.random.default_rng(22)
+    x, e, z = (rng.standard_normal(16) for _ in range(3))
+    np.testing.assert_array_equal(oracle.ddim_step_eta(x, e, z, 0.9, 1.0, 1.0, True),
+                                  oracle.ddim_step(x, e, 0.9, 1.0, True))
