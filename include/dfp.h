@@ -232,6 +232,23 @@ dfp_status dfp_ddim_eta_coeffs(double abar_t, double abar_prev, double eta, doub
  * c_e = sigma_next - sigma.  INVALID_ARG for non-finite input or null output. */
 dfp_status dfp_euler_coeffs(double sigma, double sigma_next, double *c_x, double *c_e);
 
+/* Three-phase switch points from a rel-MAE series ("Accelerating Diffusion via
+ * Hybrid Data-Pipeline Parallelism Based on Conditional Guidance Scheduling",
+ * 关键设计 3).  relmae: host, S values, relmae[t] the discrepancy of step t
+ * (t = 0 the first, noisiest step), e.g. the per-step outputs of
+ * dfp_cfg_step.  With G_t = (relmae[t] - relmae[t-L]) / L for t >= L:
+ *   tau1' = first t with 0 <= G_t < g_slope,
+ *   tau_cap = first step of the series' minimum,
+ *   tau1 = min(tau1', tau_cap) (tau_cap if there is no such t),
+ *   tau2 = min(tau1 + k, S).
+ * Warm-up is steps [0, tau1], parallel (tau1, tau2), fully-connecting
+ * [tau2, S).  The page fixes k = 5 and leaves L and g_slope open; tau_cap
+ * needs the whole series (e.g. from a profiling run).
+ * INVALID_ARG for null pointers, S < 1, L < 1, k < 0, non-finite g_slope or
+ * a non-finite series value. */
+dfp_status dfp_switch_points(const float *relmae, int S, int L, double g_slope, int k,
+                             int *tau1, int *tau2);
+
 /* The scaled-linear schedule: beta_i = (sqrt(b0) + (sqrt(b1)-sqrt(b0)) i/(T-1))^2,
  * abar[t] = prod_{i<=t} (1 - beta_i), t = 0..T-1.  abar: host, T doubles. */
 dfp_status dfp_scaled_linear_abar(int T, double beta_start, double beta_end, double *abar);

@@ -57,6 +57,7 @@ def _load():
         "oracle_cfg_combine": (None, [D, D, i64, dbl, D]),
         "oracle_ddim_step": (None, [D, D, i64, dbl, dbl, cint]),
         "oracle_ddim_step_eta": (None, [D, D, D, i64, dbl, dbl, dbl, cint]),
+        "oracle_switch_points": (cint, [D, i64, i64, dbl, i64, I, I]),
         "oracle_flow_sigmas": (None, [i64, D]),
         "oracle_euler_step": (None, [D, D, i64, dbl, dbl]),
         "oracle_relmae": (dbl, [D, D, i64]),
@@ -312,3 +313,17 @@ class EulerSchedule:
         r = relmae(v_c, v_u)
         g = cfg_combine(v_c, v_u, w)
         return euler_step(x, g, float(self.sigmas[i]), float(self.sigmas[i + 1])), r
+
+
+def switch_points(relmae_series, L: int, g_slope: float, k: int = 5):
+    """(tau1, tau2) of the three-phase schedule from a rel-MAE series
+    ("Accelerating Diffusion via Hybrid Data-Pipeline Parallelism Based on
+    Conditional Guidance Scheduling", 关键设计 3); steps are indices into the
+    series, 0 = the first denoising step."""
+    M = _f64(relmae_series).ravel()
+    t1 = np.zeros(1, dtype=np.int64)
+    t2 = np.zeros(1, dtype=np.int64)
+    if _load().oracle_switch_points(_pd(M), M.size, int(L), float(g_slope), int(k), _pi(t1),
+                                    _pi(t2)) != 0:
+        raise ValueError("need a non-empty series and L >= 1")
+    return int(t1[0]), int(t2[0])

@@ -305,3 +305,35 @@ int oracle_num_threads(void)
     return 1;
 #endif
 }
+
+/* [HY] 关键设计 3 (adaptive switching over the rel-MAE curve): with M_t the
+ * denoising discrepancy of step t (t = 0 the first, noisiest step),
+ *   G_t      = (M_t - M_{t-L}) / L                 for t >= L
+ *   tau1'    = min { t : 0 <= G_t < g_slope }      (undefined if no such t)
+ *   tau_cap  = the step of the curve's global minimum (first on ties)
+ *   tau1     = min(tau1', tau_cap)   (tau_cap alone when tau1' is undefined)
+ *   tau2     = tau1 + k,  clamped to S (no fully-connecting phase then).
+ * Warm-up is steps [0, tau1], parallel (tau1, tau2), fully-connecting
+ * [tau2, S).  Returns 0, or -1 for S < 1 or L < 1. */
+int oracle_switch_points(const double *M, int64_t S, int64_t L, double g_slope, int64_t k,
+                         int64_t *tau1, int64_t *tau2)
+{
+    if (S < 1 || L < 1) return -1;
+    int64_t cap = 0;
+    for (int64_t t = 1; t < S; ++t)
+        if (M[t] < M[cap]) cap = t;
+    int64_t first = -1;
+    for (int64_t t = L; t < S; ++t) {
+        double G = (M[t] - M[t - L]) / (double)L;
+        if (G >= 0.0 && G < g_slope) {
+            first = t;
+            break;
+        }
+    }
+    int64_t t1 = (first >= 0 && first < cap) ? first : cap;
+    int64_t t2 = t1 + k;
+    if (t2 > S) t2 = S;
+    *tau1 = t1;
+    *tau2 = t2;
+    return 0;
+}

@@ -1,5 +1,6 @@
 // host.cpp -- host-only helpers of the C ABI: status text, buffer strides,
 // workspace sizes, and the fp64 sampler coefficients the fused step consumes.
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 
@@ -54,6 +55,28 @@ dfp_status dfp_ddim_eta_coeffs(double abar_t, double abar_prev, double eta, doub
     *c_x = sp / st;
     *c_e = std::sqrt(keep) - sp * std::sqrt(1.0 - abar_t) / st;
     *c_z = std::sqrt(s2);
+    return DFP_OK;
+}
+
+dfp_status dfp_switch_points(const float *relmae, int S, int L, double g_slope, int k,
+                             int *tau1, int *tau2) {
+    if (!relmae || !tau1 || !tau2 || S < 1 || L < 1 || k < 0 || !std::isfinite(g_slope))
+        return DFP_ERR_INVALID_ARG;
+    int cap = 0;  // first step of the global minimum
+    for (int t = 0; t < S; ++t) {
+        if (!std::isfinite(relmae[t])) return DFP_ERR_INVALID_ARG;
+        if (relmae[t] < relmae[cap]) cap = t;
+    }
+    int t1 = cap;
+    for (int t = L; t < cap; ++t) {   // a flat point only matters before the cap
+        const double G = ((double)relmae[t] - (double)relmae[t - L]) / (double)L;
+        if (G >= 0.0 && G < g_slope) {
+            t1 = t;
+            break;
+        }
+    }
+    *tau1 = t1;
+    *tau2 = (int)std::min<int64_t>((int64_t)t1 + k, S);
     return DFP_OK;
 }
 

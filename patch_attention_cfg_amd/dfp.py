@@ -34,6 +34,7 @@ SIGNATURES = {
     "dfp_ddim_coeffs": (_I, [_D, _D, _P, _P]),
     "dfp_ddim_eta_coeffs": (_I, [_D, _D, _D, _P, _P, _P]),
     "dfp_euler_coeffs": (_I, [_D, _D, _P, _P]),
+    "dfp_switch_points": (_I, [_P, _I, _I, _D, _I, _P, _P]),
     "dfp_scaled_linear_abar": (_I, [_I, _D, _D, _P]),
     "dfp_ddim_timesteps": (_I, [_I, _I, _P]),
     "dfp_status_string": (ctypes.c_char_p, [_I]),
@@ -142,6 +143,15 @@ def scaled_linear_abar(T: int = 1000, beta_start: float = 0.00085,
     _check(lib().dfp_scaled_linear_abar(T, beta_start, beta_end, out.ctypes.data),
            "dfp_scaled_linear_abar")
     return out
+
+
+def switch_points(relmae_series, L: int, g_slope: float, k: int = 5):
+    """(tau1, tau2) from a host rel-MAE series (see dfp_switch_points)."""
+    m = np.ascontiguousarray(np.asarray(relmae_series, dtype=np.float32).ravel())
+    t1, t2 = ctypes.c_int(), ctypes.c_int()
+    _check(lib().dfp_switch_points(m.ctypes.data, m.size, int(L), float(g_slope), int(k),
+                                   ctypes.byref(t1), ctypes.byref(t2)), "dfp_switch_points")
+    return t1.value, t2.value
 
 
 def ddim_timesteps(T: int, S: int) -> np.ndarray:

@@ -195,3 +195,32 @@ def test_eta_coefficient_edges(L):
         dfp.ddim_eta_coeffs(0.6, 0.3, 0.5)                       # abar_t > abar_prev
     with pytest.raises(dfp.DFPError):
         dfp.ddim_eta_coeffs(0.3, 0.6, -0.1)
+
+
+def test_switch_points_match_oracle(L):
+    """The library's switch rule against the oracle's on fp32 series: clean
+    U curves, plateaus, noisy curves and strictly monotone ones."""
+    rng = np.random.Generator(np.random.PCG64(31))
+    series = []
+    t = np.arange(50)
+    series.append(((t - 23) ** 2 / 50 + 0.1))
+    series.append(np.concatenate([np.linspace(1, 0.1, 11), np.full(20, 0.1),
+                                  [0.08, 0.06, 0.05, 0.07, 0.1, 0.2]]))
+    series.append(np.linspace(1, 0, 28))
+    for _ in range(100):
+        S = int(rng.integers(1, 60))
+        base = np.abs(np.linspace(-1, 1, S)) + 0.3
+        series.append(base + 0.05 * rng.standard_normal(S))
+    for M in series:
+        M = np.asarray(M, dtype=np.float32)
+        for Lw, g, k in ((1, 0.01, 5), (3, 0.02, 5), (5, 0.005, 10)):
+            assert dfp.switch_points(M, Lw, g, k) == oracle.switch_points(M, Lw, g, k)
+
+
+def test_switch_points_validation(L):
+    with pytest.raises(dfp.DFPError):
+        dfp.switch_points([], 1, 0.1)
+    with pytest.raises(dfp.DFPError):
+        dfp.switch_points([0.3, 0.2], 0, 0.1)
+    with pytest.raises(dfp.DFPError):
+        dfp.switch_points([0.3, float("nan")], 1, 0.1)

@@ -52,6 +52,7 @@ def test_sampler_run_step_by_step(name):
     x_host = stream.x_T.astype(np.float32)
     x_ref_traj = x_host.astype(np.float64)
     worst_step, worst_r = 0.0, 0.0
+    series = []
     for i in range(wl.steps):
         g_c, g_u = stream.next_pair()
         x = torch.from_numpy(x_host).cuda()
@@ -63,6 +64,7 @@ def test_sampler_run_step_by_step(name):
         want, r_want = sch.step(x_host, g_c, g_u, wl.w, i)
         err = G.rel_l2(got, want)
         r_got = float(r_dev[0].item())
+        series.append(r_got)
         rerr = abs(r_got - r_want) / abs(r_want)
         worst_step, worst_r = max(worst_step, err), max(worst_r, rerr)
         assert err <= STEP_REL_L2, f"{name} step {i}: rel L2 {err}"
@@ -74,6 +76,9 @@ def test_sampler_run_step_by_step(name):
     G.announce(f"{name}: worst step relL2 {worst_step:.2e}, worst rel-MAE err {worst_r:.2e}, "
                f"full-trajectory relL2 {traj:.2e}")
     assert np.isfinite(x_host).all()
+    # the three-phase switch rule on the series this run produced
+    for Lw, g in ((1, 0.01), (3, 0.005)):
+        assert dfp.switch_points(series, Lw, g) == oracle.switch_points(series, Lw, g)
 
 
 @pytest.mark.parametrize("name,eta", [("tiny-f32", 1.0), ("sdxl1024", 0.5), ("sdxl3840", 1.0)])

@@ -247,3 +247,53 @@ def test_ddim_eta_last_step_adds_no_noise():
     x, e, z = (rng.standard_normal(16) for _ in range(3))
     np.testing.assert_array_equal(oracle.ddim_step_eta(x, e, z, 0.9, 1.0, 1.0, True),
                                   oracle.ddim_step(x, e, 0.9, 1.0, True))
+
+
+# --------------------------------------------------- three-phase switch points
+def test_switch_clean_u_curve_switches_at_its_minimum():
+    """On a clean U (M_t = (t - c)^2 / S + 0.1) the averaged slope turns
+    non-negative only L/2 steps after the minimum, so the cap decides:
+    tau1 = c, tau2 = c + k."""
+    S, c = 50, 23
+    t = np.arange(S)
+    M = (t - c) ** 2 / S + 0.1
+    for L in (1, 2, 4):
+        assert oracle.switch_points(M, L, 0.05, 5) == (c, c + 5)
+
+
+def test_switch_plateau_before_the_minimum():
+    """A fast drop to a flat plateau, then a deeper minimum later: the first
+    flat point (slope 0 over the last L steps) wins over the cap."""
+    M = np.concatenate([np.linspace(1.0, 0.1, 11),        # steps 0..10 drop
+                        np.full(20, 0.1),                   # 11..30 flat
+                        [0.08, 0.06, 0.05, 0.07, 0.1, 0.2]])  # minimum at step 33
+    assert oracle.switch_points(M, 2, 1e-3, 5) == (12, 17)
+    assert oracle.switch_points(M, 4, 1e-3, 5) == (14, 19)
+
+
+def test_switch_slope_bound_is_strict_and_rising_curves_fall_back_to_the_cap():
+    M = np.array([1.0, 0.5, 0.5 + 0.02, 0.4, 0.3, 0.35])
+    # step 2: G = 0.02 over L = 1; only counts when g_slope > 0.02
+    assert oracle.switch_points(M, 1, 0.02, 1) == (4, 5)
+    assert oracle.switch_points(M, 1, 0.021, 1) == (2, 3)
+    # strictly decreasing: no flat point, the cap is the last step, tau2 clamps
+    assert oracle.switch_points(np.linspace(1, 0, 10), 2, 0.1, 5) == (9, 10)
+
+
+def test_switch_ties_and_properties_on_random_series():
+    rng = np.random.default_rng(5)
+    assert oracle.switch_points([0.3, 0.1, 0.2, 0.1], 1, 0.0, 2) == (1, 3)   # first minimum
+    for _ in range(200):
+        S = int(rng.integers(1, 40))
+        L = int(rng.integers(1, 6))
+        g = float(rng.uniform(0.0, 0.2))
+        M = rng.uniform(0.0, 1.0, S)
+        t1, t2 = oracle.switch_points(M, L, g, 5)
+        cap = int(np.argmin(M))
+        assert 0 <= t1 <= cap and t2 == min(t1 + 5, S)
+        if t1 < cap:                       # chosen by the slope rule: first such step
+            G = (M[t1] - M[t1 - L]) / L
+            assert t1 >= L and 0 <= G < g
+        for t in range(L, t1):             # no earlier step qualifies
+            G = (M[t] - M[t - L]) / L
+            assert not (0 <= G < g)
