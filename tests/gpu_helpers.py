@@ -78,14 +78,16 @@ def run_patch(level, x, p: int, kind: str | None = None, split_ok: bool = True):
     dfp.patch_attention(o, q, k_buf, v_buf, 1.0 / level.d ** 0.5, ws)
     torch.cuda.synchronize()
     if ws is not None:
-        assert_counters_zero(ws, level.B * level.H, level.n)
+        assert_counters_zero(ws, level.B * level.H, level.n, level.d)
     return down(o)
 
 
-def assert_counters_zero(ws, BH: int, n_q: int) -> None:
+def assert_counters_zero(ws, BH: int, n_q: int, d: int = 64) -> None:
     """The attention workspace starts with one uint32 arrival counter per
-    128-row query tile; every call must leave them at zero."""
-    n = BH * ((n_q + 127) // 128) * 4
+    query tile (128 rows at d=64, 256 at d=128); every call must leave them
+    at zero."""
+    block_m = 128 if d == 64 else 256
+    n = BH * ((n_q + block_m - 1) // block_m) * 4
     assert int(ws[:n].sum().item()) == 0
 
 

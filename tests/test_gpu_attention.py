@@ -129,7 +129,7 @@ def test_forced_split_kv_every_element(monkeypatch, splits, B, H, nq, N, d):
     torch.cuda.synchronize()
     first = G.down(o)
     if ws is not None:
-        G.assert_counters_zero(ws, B * H, nq)
+        G.assert_counters_zero(ws, B * H, nq, d)
     _check(first, oracle.attention(q, k, v, 1.0 / d ** 0.5), "bf16", f"split{splits}")
     dfp.patch_attention(o, qd, k_buf, v_buf, None, ws)
     torch.cuda.synchronize()
