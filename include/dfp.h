@@ -163,10 +163,11 @@ dfp_status dfp_patch_attention(void *o, const void *q, const void *k_buf,
  *   relmae_out [batch] fp32 device memory, or NULL to skip the reduction.
  *   workspace  device scratch of >= dfp_workspace_bytes(DFP_OP_CFG_STEP,
  *              n_per_image, batch, ...) bytes, required when relmae_out is
- *              non-NULL.  Its first 256 bytes hold a completion counter that
- *              must be zero before the first call (e.g. allocate it zeroed);
- *              every call leaves it zero again.  The rest holds per-workgroup
- *              partial sums.  The cross-workgroup sum runs in a fixed order
+ *              non-NULL.  It starts with one completion counter per image
+ *              (4 bytes each, padded to a multiple of 256 bytes) that must
+ *              be zero before the first call (e.g. allocate it zeroed);
+ *              every call leaves them zero again.  The rest holds
+ *              per-workgroup partial sums.  The cross-workgroup sum runs in a fixed order
  *              in double precision, so results are bitwise reproducible.
  * Degenerate rel-MAE follows IEEE division (0/0 = NaN, x/0 = +Inf).
  * Errors: INVALID_ARG for null x/g_c/g_u, n_per_image <= 0, batch <= 0,

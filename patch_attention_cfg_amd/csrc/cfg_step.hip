@@ -16,9 +16,10 @@
 //   latent element (x read + write, g_c and g_u read).
 //
 // Reduction: fp32 per thread and per wavefront, fp64 per workgroup; the last
-// workgroup to finish (integer completion counter) sums the per-workgroup
-// partials in a fixed order in fp64 and writes the ratio.  No float atomics,
-// so the result is bitwise reproducible run to run.  The partials move
+// workgroup of each image to finish (an integer completion counter per
+// image) sums that image's per-workgroup partials in a fixed order in fp64
+// and writes the ratio.  No float atomics, so the result is bitwise
+// reproducible run to run.  The partials move
 // between workgroups through coherent stores and loads (dfp::publish), not
 // through L2-wide cache maintenance.
 #include <cmath>
@@ -29,9 +30,17 @@
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kUnroll = 2;            // float4 items per thread per array in flight
-constexpr int kMaxBlocksPerImage = 2048;
-constexpr size_t kCounterBytes = 256;
+constexpr int kUnroll = 4;            // float4 items per thread per array in flight
+// Few, fat workgroups: every workgroup ends with a published partial and an
+// atomic arrival, and that tail, not the data, dominates small steps.  Up to
+// kBlocksSmall workgroups take one pass each; larger images get up to
+// kBlocksLarge workgroups of at least kPassesLarge grid-stride passes.
+constexpr int kBlocksSmall = 128;
+constexpr int kBlocksLarge = 1024;
+constexpr int kPassesLarge = 16;
+
+// One arrival counter per image, padded to whole 256-byte blocks.
+inline size_t counter_bytes(int batch) { return ((size_t)batch * 4 + 255) / 256 * 256; }
 
 struct Grid {
     int blocks_per_image;
@@ -39,10 +48,13 @@ struct Grid {
 
 inline Grid plan(int64_t n_per_image) {
     const int64_t items = (n_per_image + 3) / 4;  // float4 items (or scalar quads)
-    int64_t b = (items + kThreads * kUnroll - 1) / (kThreads * kUnroll);
-    if (b < 1) b = 1;
-    if (b > kMaxBlocksPerImage) b = kMaxBlocksPerImage;
-    return Grid{(int)b};
+    const int64_t per_pass = (int64_t)kThreads * kUnroll;
+    int64_t b = (items + per_pass - 1) / per_pass;  // one pass per workgroup
+    if (b > kBlocksSmall) {
+        const int64_t fat = (items + per_pass * kPassesLarge - 1) / (per_pass * kPassesLarge);
+        b = fat > kBlocksSmall ? (fat < kBlocksLarge ? fat : kBlocksLarge) : kBlocksSmall;
+    }
+    return Grid{(int)(b < 1 ? 1 : b)};
 }
 
 __device__ __forceinline__ void accum(float &num, float &den, float c, float u) {
@@ -148,40 +160,38 @@ __global__ __launch_bounds__(kThreads) void cfg_step_kernel(
         dfp::publish(p, pn);
         dfp::publish(p + 1, pd);
         dfp::published_wait();
-        const unsigned total = (unsigned)nblk * gridDim.y;
-        is_last = (dfp::arrive(counter) == total - 1);
+        is_last = (dfp::arrive(counter + img) == (unsigned)nblk - 1);
     }
     __syncthreads();
     if (!is_last) return;
 
-    // last workgroup: fixed-order fp64 sums of every image's partials
+    // last workgroup of this image: fixed-order fp64 sum of its partials
     __shared__ double snum[kThreads], sden[kThreads];
-    for (int im = 0; im < (int)gridDim.y; ++im) {
-        double a = 0.0, b = 0.0;
-        const double *p = partials + 2 * (int64_t)im * nblk;
-        for (int k = tid; k < nblk; k += kThreads) {
-            a += dfp::fetch_published(p + 2 * k);
-            b += dfp::fetch_published(p + 2 * k + 1);
+    double a = 0.0, b = 0.0;
+    const double *p = partials + 2 * (int64_t)img * nblk;
+    for (int k = tid; k < nblk; k += kThreads) {
+        a += dfp::fetch_published(p + 2 * k);
+        b += dfp::fetch_published(p + 2 * k + 1);
+    }
+    snum[tid] = a;
+    sden[tid] = b;
+    __syncthreads();
+    for (int s = kThreads / 2; s > 0; s >>= 1) {
+        if (tid < s) {
+            snum[tid] += snum[tid + s];
+            sden[tid] += sden[tid + s];
         }
-        snum[tid] = a;
-        sden[tid] = b;
-        __syncthreads();
-        for (int s = kThreads / 2; s > 0; s >>= 1) {
-            if (tid < s) {
-                snum[tid] += snum[tid + s];
-                sden[tid] += sden[tid + s];
-            }
-            __syncthreads();
-        }
-        if (tid == 0) out[im] = (float)(snum[0] / sden[0]);
         __syncthreads();
     }
-    if (tid == 0) dfp::publish(counter, 0u);
+    if (tid == 0) {
+        out[img] = (float)(snum[0] / sden[0]);
+        dfp::publish(counter + img, 0u);
+    }
 }
 
 size_t workspace_need(int64_t n_per_image, int batch) {
     const Grid g = plan(n_per_image);
-    return kCounterBytes + (size_t)batch * g.blocks_per_image * 2 * sizeof(double);
+    return counter_bytes(batch) + (size_t)batch * g.blocks_per_image * 2 * sizeof(double);
 }
 
 template <bool UPDATE>
@@ -202,7 +212,8 @@ dfp_status launch(float *x, const float *g_c, const float *g_u, const float *z, 
                      (!noise || reinterpret_cast<uintptr_t>(z) % 16 == 0);
     unsigned *counter = reduce ? static_cast<unsigned *>(ws) : nullptr;
     double *partials =
-        reduce ? reinterpret_cast<double *>(static_cast<char *>(ws) + kCounterBytes) : nullptr;
+        reduce ? reinterpret_cast<double *>(static_cast<char *>(ws) + counter_bytes(batch))
+               : nullptr;
     dim3 grid((unsigned)g.blocks_per_image, (unsigned)batch);
 #define DFP_CFG_LAUNCH(V, N)                                                                 \
     hipLaunchKernelGGL((cfg_step_kernel<UPDATE, V, N>), grid, dim3(kThreads), 0, stream, x,   \

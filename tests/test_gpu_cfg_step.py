@@ -136,6 +136,29 @@ def test_relmae_alone_batch_and_determinism():
     dfp.relmae(dc, du, out, ws)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(out.cpu().numpy(), a)
+    assert int(ws[:3 * 4].sum().item()) == 0      # every image's counter left at zero
+
+
+def test_relmae_many_images_one_call():
+    """Batch 70 in one call (one completion counter per image, several
+    256-byte counter blocks): every image's ratio against the oracle."""
+    G.require_gpu()
+    G.announce("relmae batch=70")
+    torch = G.torch_mod()
+    r = np.random.Generator(np.random.PCG64(78))
+    batch, n = 70, 4 * 64 * 64
+    g_c = r.standard_normal((batch, n), dtype=np.float32)
+    g_u = r.standard_normal((batch, n), dtype=np.float32) * np.linspace(0.5, 2.0, batch,
+                                                                         dtype=np.float32)[:, None]
+    ws = dfp.cfg_workspace(n, batch)
+    out = torch.empty(batch, dtype=torch.float32, device="cuda")
+    dfp.relmae(torch.from_numpy(g_c).cuda(), torch.from_numpy(g_u).cuda(), out, ws)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    for b in range(batch):
+        want = oracle.relmae(g_c[b], g_u[b])
+        assert abs(got[b] - want) / want <= RELMAE_REL, f"image {b}"
+    assert int(ws[:batch * 4].sum().item()) == 0
 
 
 @pytest.mark.parametrize("n,offset", [(1001, 0), (4096, 1), (3, 0), (1, 0)])
