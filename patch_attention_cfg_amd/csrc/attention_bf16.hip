@@ -25,12 +25,15 @@
 //     O^T = V^T P^T directly.  The lanes of the Q.K^T A operand load K rows
 //     in a permuted order (key_row) that leaves each lane's probabilities
 //     on 8 consecutive keys, so every MFMA operand is one 16-byte LDS read.
-//     LDS rows carry one 16-byte pad slot (a 144-byte pitch at 64 keys or
-//     64 channels), so each 16-lane group of a 16-byte read covers all 64
-//     banks once; lanes whose DMA slot is a pad fetch an in-row chunk that
-//     is never read.
-//   * Three LDS stages per operand: tile t+3's K and tile t+1's V are in
-//     flight while step t computes, one barrier per step.
+//     LDS rows are unpadded; 16-byte slot s of row r is stored at s ^ swz(r),
+//     so each 16-lane group of a 16-byte operand read covers all 64 banks
+//     once.
+//   * Four LDS stages per operand: tile t+3's K and tile t+1's V are in
+//     flight while step t computes, and step t's own copies (K(t+4),
+//     V(t+2)) are issued between its MFMAs; one barrier per step.  The main
+//     loop runs four steps per trip so that every stage address is a
+//     compile-time constant, and copies full tiles through one buffer
+//     resource per (batch, head) with the tile start as the scalar offset.
 //   * Each step is one basic block holding three independent streams:
 //     tile t+1's Q.K^T MFMAs, tile t-1's P.V MFMAs and tile t's softmax
 //     VALU work, interleaved in a fixed order (alternating accumulators,
@@ -182,10 +185,11 @@ __device__ __forceinline__ int32x4_t buffer_rsrc(const void *base, uint32_t byte
 // instead waits for them explicitly (vmcnt) right before the barrier that
 // publishes a stage.  M0 carries the LDS address; nothing else in this
 // kernel uses M0 (checked on the built code object).
-__device__ __forceinline__ void lds_dma16(int32x4_t rsrc, uint32_t voff, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(
+__device__ __forceinline__ void lds_dma16(int32x4_t rsrc, uint32_t voff, uint32_t soff,
+                                          uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"s"(
                      __builtin_amdgcn_readfirstlane(lds)),
-                 "v"(voff), "s"(rsrc)
+                 "v"(voff), "s"(rsrc), "s"(soff)
                  : "memory");
 }
 
@@ -245,6 +249,7 @@ struct TileDma {
 // range gets an empty resource (its copies read zeros, touch no memory).
 struct CopyJob {
     int32x4_t rk, rv;
+    uint32_t sk, sv;   // byte offsets added to every lane's address (tile start)
     uint32_t lk, lv;
 };
 
@@ -257,6 +262,8 @@ __device__ __forceinline__ CopyJob copy_job(const uint16_t *Kh, const uint16_t *
     CopyJob j;
     j.rk = buffer_rsrc(Kh + (int64_t)jk * D, tk < t_end ? (uint32_t)(N_kv - jk) * D * 2 : 0u);
     j.rv = buffer_rsrc(Vh + jv, tv < t_end ? (uint32_t)((int64_t)D * ldv - jv) * 2 : 0u);
+    j.sk = 0u;
+    j.sv = 0u;
     j.lk = lk;
     j.lv = lv;
     return j;
@@ -264,7 +271,8 @@ __device__ __forceinline__ CopyJob copy_job(const uint16_t *Kh, const uint16_t *
 
 template <int D>
 __device__ __forceinline__ void issue_copy(const TileDma<D> &dma, const CopyJob &j, int e) {
-    lds_dma16(e < Cfg<D>::K_DMA_W ? j.rk : j.rv, dma.off[e], dma.lds_of(e, j.lk, j.lv));
+    lds_dma16(e < Cfg<D>::K_DMA_W ? j.rk : j.rv, dma.off[e], e < Cfg<D>::K_DMA_W ? j.sk : j.sv,
+              dma.lds_of(e, j.lk, j.lv));
 }
 
 // Zero V^T columns of keys >= N_kv in a landed tile (ragged last tile).
@@ -601,6 +609,40 @@ __device__ __forceinline__ void tile_step(int t, const Ctx &x, State<D> &st, Sme
     }
 }
 
+// The same step with the stage ring position R4 = (t - t_begin) % 4 known at
+// compile time (LDS operand addresses become immediates) and copies of full
+// in-range tiles only: fixed buffer resources over the whole (batch, head)
+// with the tile start as the scalar offset.
+template <int D, int R4>
+__device__ __forceinline__ void tile_step_static(int t, const Ctx &x, State<D> &st, Smem<D> &sm,
+                                                 const TileDma<D> &dma,
+                                                 const OperandOffsets<D> &oo,
+                                                 const int32x4_t &rk_all, const int32x4_t &rv_all,
+                                                 f32x16_t (&s_cur)[Cfg<D>::SB],
+                                                 f32x16_t (&s_next)[Cfg<D>::SB],
+                                                 const bf16x8_t (&p_prev)[Cfg<D>::SB][2],
+                                                 bf16x8_t (&p_cur)[Cfg<D>::SB][2],
+                                                 bf16x8_t (&carry)[2],
+                                                 const bf16x8_t (&qreg)[Cfg<D>::KC]) {
+    using C = Cfg<D>;
+    constexpr int BN = C::BN;
+    constexpr int sk1 = (R4 + 1) & 3, sk2 = (R4 + 2) & 3, sv_prev = (R4 + 3) & 3;
+    CopyJob job;
+    job.rk = rk_all;
+    job.rv = rv_all;
+    job.sk = (uint32_t)(t + 4) * (uint32_t)(BN * D * 2);
+    job.sv = (uint32_t)(t + 2) * (uint32_t)(BN * 2);
+    job.lk = lds_addr(sm.k[R4]);
+    job.lv = lds_addr(sm.v[(R4 + 2) & 3]);
+    float l_tile = 0.f;
+    region<D>(s_next, st.oacc, p_cur, l_tile, s_cur, p_prev, sm.k[sk1], sm.v[sv_prev], sm.k[sk2],
+              carry, qreg, x.c, st.m_run, oo, dma, job);
+    if (__any(!(l_tile <= kMaxTileSum))) raise_reference<D>(st, s_cur, p_cur, l_tile, x.c);
+    st.l_run += l_tile;
+    wait_dma_keep4();
+    __syncthreads();
+}
+
 template <int D>
 __global__ __launch_bounds__(Cfg<D>::THREADS, Cfg<D>::WG_PER_CU) void attn_fwd_bf16(Params p) {
     using C = Cfg<D>;
@@ -723,6 +765,18 @@ __global__ __launch_bounds__(Cfg<D>::THREADS, Cfg<D>::WG_PER_CU) void attn_fwd_b
     // the last tile can be ragged: the final one or two steps take the path
     // that masks it.
     int t = t0;
+    {
+        // full tiles only: every copy of a static trip lands tiles below n_full
+        const int n_full = min(x.t_end, N_kv / BN);
+        const int32x4_t rk_all = buffer_rsrc(x.Kh, (uint32_t)N_kv * D * 2);
+        const int32x4_t rv_all = buffer_rsrc(x.Vh, (uint32_t)((int64_t)D * x.ldv * 2));
+        for (; t + 8 <= n_full; t += 4) {
+            tile_step_static<D, 0>(t, x, st, sm, dma, oo, rk_all, rv_all, sA, sB, pB, pA, carry, qreg);
+            tile_step_static<D, 1>(t + 1, x, st, sm, dma, oo, rk_all, rv_all, sB, sA, pA, pB, carry, qreg);
+            tile_step_static<D, 2>(t + 2, x, st, sm, dma, oo, rk_all, rv_all, sA, sB, pB, pA, carry, qreg);
+            tile_step_static<D, 3>(t + 3, x, st, sm, dma, oo, rk_all, rv_all, sB, sA, pA, pB, carry, qreg);
+        }
+    }
     for (; t + 2 < x.t_end; t += 2) {
         tile_step<D, false>(t, x, st, sm, dma, oo, sA, sB, pB, pA, carry, qreg);
         tile_step<D, false>(t + 1, x, st, sm, dma, oo, sB, sA, pA, pB, carry, qreg);
