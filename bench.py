@@ -5,9 +5,14 @@ One timed "step" is the whole hot path once, at the SDXL-1024-shaped workload
 (64x64 level: 4096 tokens, 10 heads x 64, P=4; 32x32 level: 1024 tokens,
 20 heads x 64, P=4; batch 2 = cond/uncond; latent 1x4x128x128, DDIM-50,
 w=7.5):
-  land fresh K/V (64x64 level) -> patch attention (64x64 level)
-  land fresh K/V (32x32 level) -> patch attention (32x32 level)
+  patch attention (64x64 level), reading the patch's fresh K/V from this
+      step's tensors and landing them in the persistent buffer in the same
+      launch (dfp_patch_attention_fresh)
+  the same for the 32x32 level
   fused CFG + DDIM update + rel-MAE on the latent.
+A level whose patch rows are not whole 64-key tiles, or that has always-fresh
+text rows, lands its K/V with dfp_kv_scatter and then runs
+dfp_patch_attention; `--no-fresh` times that path everywhere.
 All inputs are seeded synthetic arrays resident in HBM before timing starts.
 The timed steps replay one HIP graph of the step (falls back to eager
 launches if capture is refused).  Per-kernel durations for the roofline come
@@ -48,7 +53,11 @@ def parse():
     ap.add_argument("--kernel-reps", type=int, default=50)
     ap.add_argument("--sweep", action="store_true",
                     help="time the one-device patch sweep: every patch of each level in order "
-                         "(scatter, then attention), instead of one patch")
+                         "(each landing its fresh K/V for the patches after it), instead of one "
+                         "patch")
+    ap.add_argument("--no-fresh", action="store_true",
+                    help="land fresh K/V with dfp_kv_scatter before dfp_patch_attention instead "
+                         "of the fused dfp_patch_attention_fresh")
     ap.add_argument("--eta", type=float, default=0.0,
                     help="DDIM noise scale (DDIM workloads): > 0 runs the fused step with the "
                          "sampler-noise term (dfp_cfg_step_noise)")
@@ -83,7 +92,7 @@ class Level:
     default the step covers one patch (one GPU's share); with `sweep` it
     covers every patch of the level in order (the one-device patch sweep)."""
 
-    def __init__(self, level, dfp, torch, inputs, sweep=False):
+    def __init__(self, level, dfp, torch, inputs, sweep=False, fresh=True):
         x = inputs.attention_inputs(level)
         self.level = level
         self.patches = list(range(level.P)) if sweep else [1 if level.P > 1 else 0]
@@ -94,10 +103,15 @@ class Level:
 
         self.k_buf, self.v_buf = dfp.alloc_kv_buffer(level.B, level.H, level.N_kv, level.d, bf)
         dfp.kv_scatter(self.k_buf, self.v_buf, up(x.k_stale), up(x.v_stale), 0)
+        # fused path: whole 64-key tiles of fresh rows and no text rows
+        self.fused = (fresh and not level.n_text and level.n % 64 == 0 and
+                      all(level.row0(p) % 64 == 0 for p in self.patches))
         self.fresh, self.q, self.o = [], [], []
         for p in self.patches:
             kf, vf = x.fresh_rows(p)
-            self.fresh.append((up(kf), up(vf), level.row0(p)))
+            # the fused call takes V channel-major ([B,H,d,n]), as a projection can emit it
+            v_in = np.swapaxes(vf, -1, -2) if self.fused else vf
+            self.fresh.append((up(kf), up(v_in), level.row0(p)))
             self.q.append(up(x.q_patch(p)))
             self.o.append(torch.empty_like(self.q[-1]))
         self.text = None
@@ -120,10 +134,18 @@ class Level:
     def attend(self, dfp, i=0):
         dfp.patch_attention(self.o[i], self.q[i], self.k_buf, self.v_buf, self.scale, self.ws)
 
+    def attend_fresh(self, dfp, i=0):
+        k, vt, row0 = self.fresh[i]
+        dfp.patch_attention_fresh(self.o[i], self.q[i], self.k_buf, self.v_buf, k, vt, row0,
+                                  True, self.scale, self.ws)
+
     def run(self, dfp):
         for i in range(len(self.patches)):
-            self.scatter(dfp, i)
-            self.attend(dfp, i)
+            if self.fused:
+                self.attend_fresh(dfp, i)
+            else:
+                self.scatter(dfp, i)
+                self.attend(dfp, i)
 
 
 class Sampler:
@@ -252,7 +274,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     wl = inputs.WORKLOADS[args.workload]
-    levels = [Level(lv, dfp, torch, inputs, args.sweep) for lv in wl.levels]
+    levels = [Level(lv, dfp, torch, inputs, args.sweep, not args.no_fresh) for lv in wl.levels]
     sampler = Sampler(wl, dfp, torch, inputs, args.eta)
     torch.cuda.synchronize()
 
@@ -308,16 +330,21 @@ def main():
     reps = args.kernel_reps
     kern = {}
     for L in levels:
-        mean, mn = time_kernel(torch, lambda L=L: L.attend(dfp), reps)
+        # the attention launch the step runs: fused with the landing, or plain
+        fn = (lambda L=L: L.attend_fresh(dfp)) if L.fused else (lambda L=L: L.attend(dfp))
+        mean, mn = time_kernel(torch, fn, reps)
         kern[f"attn_{L.level.name}"] = {
             "us_mean": mean, "us_min": mn,
             "tflops": L.level.flops() / (mean * 1e-6) / 1e12,
             "frac_bf16_peak": L.level.flops() / (mean * 1e-6) / 1e12 / PEAK_BF16_TFLOPS,
-            "flop": L.level.flops()}
-        mean, mn = time_kernel(torch, lambda L=L: L.scatter(dfp), reps)
-        kern[f"scatter_{L.level.name}"] = {
-            "us_mean": mean, "us_min": mn,
-            "gbps": L.fresh_bytes / (mean * 1e-6) / 1e9, "bytes": L.fresh_bytes}
+            "flop": L.level.flops(),
+            "launch": "dfp_patch_attention_fresh (attention + landing of the fresh K/V)"
+                      if L.fused else "dfp_patch_attention"}
+        if not L.fused:
+            mean, mn = time_kernel(torch, lambda L=L: L.scatter(dfp), reps)
+            kern[f"scatter_{L.level.name}"] = {
+                "us_mean": mean, "us_min": mn,
+                "gbps": L.fresh_bytes / (mean * 1e-6) / 1e9, "bytes": L.fresh_bytes}
     ctr = [0]
 
     def cfg():
@@ -353,7 +380,8 @@ def main():
         dom.level.name)
     roofline = {"bound": "mfma", "achieved": dk["tflops"], "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": dk["tflops"] / PEAK_BF16_TFLOPS, "traffic": traffic,
-                "kernel": f"attn_fwd_bf16<{dom.level.d}> ({dom.level.name}, "
+                "kernel": f"attn_fwd_bf16<{dom.level.d}{', fresh' if dom.fused else ''}> "
+                          f"({dom.level.name}, "
                           f"{dom.level.flops() / 1e9:.2f} GFLOP per launch)"}
 
     cpu = None
@@ -379,6 +407,8 @@ def main():
                         + (" one-device patch sweep: every patch of each attention level in order"
                            " + fused CFG step" if args.sweep else
                            " patch-parallel step: one patch per attention level + fused CFG step"),
+            "kv_landing": {L.level.name: "fused into the attention launch" if L.fused
+                           else "dfp_kv_scatter before the attention" for L in levels},
             "attention": [f"{L.level.name}: B{L.level.B} H{L.level.H} n_q{L.level.n} "
                           f"N_kv{L.level.N_kv} d{L.level.d} bf16" for L in levels],
             "latent": list(wl.latent), "sampler": f"{wl.sampler}{wl.steps} fp32"

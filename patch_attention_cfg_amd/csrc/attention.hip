@@ -1,7 +1,10 @@
-// attention.hip -- C-ABI entry point of patch attention, and the fp32 path.
+// attention.hip -- C-ABI entry points of patch attention, and the fp32 path.
 //
 // dfp_patch_attention validates its arguments and dispatches to the bf16
-// matrix-core kernel (attention_bf16.hip) or to the fp32 kernel below.  The
+// matrix-core kernel (attention_bf16.hip) or to the fp32 kernel below;
+// dfp_patch_attention_fresh runs the bf16 kernel with the patch's fresh
+// rows read from this step's tensors (and landed in the buffer by the same
+// launch).  The
 // fp32 kernel exists for full-precision checks of the method on small
 // workloads; it is plain vector-ALU code (one query per lane, online
 // softmax, K and V^T tiles broadcast from LDS) with no performance target.
@@ -144,6 +147,30 @@ extern "C" dfp_status dfp_patch_attention(void *o, const void *q, const void *k_
     if (BH > 0x7FFFFFFF) return DFP_ERR_UNSUPPORTED;
     if (dt == DFP_BF16)
         return dfp_attn_bf16_launch(o, q, k_buf, v_buf_t, (int)BH, n_q, N_kv, d, scale, workspace,
-                                    ws_bytes, stream);
+                                    ws_bytes, nullptr, stream);
     return attn_f32_launch(o, q, k_buf, v_buf_t, (int)BH, n_q, N_kv, d, scale, stream);
+}
+
+extern "C" dfp_status dfp_patch_attention_fresh(void *o, const void *q, void *k_buf, void *v_buf_t,
+                                                const void *k_new, const void *v_new_t, int B,
+                                                int H, int n_q, int N_kv, int d, int row0, int n,
+                                                int land, float scale, dfp_dtype dt,
+                                                void *workspace, size_t ws_bytes,
+                                                hipStream_t stream) {
+    if (B <= 0 || H <= 0 || N_kv <= 0 || n_q < 0) return DFP_ERR_INVALID_ARG;
+    if (!(scale > 0.f) || !std::isfinite(scale)) return DFP_ERR_INVALID_ARG;
+    if (row0 < 0 || n <= 0 || (int64_t)row0 + n > N_kv) return DFP_ERR_INVALID_ARG;
+    if (dt != DFP_BF16) return DFP_ERR_UNSUPPORTED;
+    if (d != 64 && d != 128) return DFP_ERR_UNSUPPORTED;
+    if (row0 % 64 != 0 || n % 64 != 0) return DFP_ERR_UNSUPPORTED;
+    if (n_q == 0 && !land) return DFP_OK;
+    if (!k_buf || !v_buf_t || !k_new || !v_new_t) return DFP_ERR_INVALID_ARG;
+    if (!aligned16(k_buf) || !aligned16(v_buf_t) || !aligned16(k_new) || !aligned16(v_new_t))
+        return DFP_ERR_INVALID_ARG;
+    if (n_q > 0 && (!o || !q || !aligned16(o) || !aligned16(q))) return DFP_ERR_INVALID_ARG;
+    const int64_t BH = (int64_t)B * H;
+    if (BH > 0x7FFFFFFF) return DFP_ERR_UNSUPPORTED;
+    const dfp_fresh_rows fresh{k_new, v_new_t, k_buf, v_buf_t, row0, n, land ? 1 : 0};
+    return dfp_attn_bf16_launch(o, q, k_buf, v_buf_t, (int)BH, n_q, N_kv, d, scale, workspace,
+                                ws_bytes, &fresh, stream);
 }

@@ -91,7 +91,17 @@ struct Params {
     int q_tiles;
     int splits;
     int tiles_per_split;
-    int total_wg;
+    int total_wg;        // attention workgroups; landing workgroups follow them
+    // Fresh rows (dfp_patch_attention_fresh): key tiles [f_t0, f_t1), rows
+    // [f_row0, f_row0 + f_n), are read from Kf / Vtf instead of the buffer,
+    // and land_wg workgroups after the attention ones copy them into it.
+    const uint16_t *Kf;  // [BH][f_n][D]
+    const uint16_t *Vtf; // [BH][D][f_n]
+    uint16_t *Kw;        // the buffer again, writable (landing)
+    uint16_t *Vtw;
+    int f_t0, f_t1, f_row0, f_n;
+    int BH;
+    int land_wg;
 };
 
 template <int D>
@@ -219,9 +229,10 @@ template <int D>
 struct TileDma {
     using C = Cfg<D>;
     uint32_t off[C::DMA_W];   // byte offset of this lane's chunk within a tile
+    uint32_t offf[C::DMA_W - C::K_DMA_W];   // V^T chunks of a fresh tile (row stride ldn)
     int wave;
 
-    __device__ __forceinline__ void init(int wv, int lane, int64_t ldv) {
+    __device__ __forceinline__ void init(int wv, int lane, int64_t ldv, int64_t ldn) {
         wave = __builtin_amdgcn_readfirstlane(wv);
 #pragma unroll
         for (int e = 0; e < C::DMA_W; ++e) {
@@ -233,6 +244,7 @@ struct TileDma {
                 const int z = (wave + (e - C::K_DMA_W) * C::NW) * 64 + lane;
                 const int row = z / C::V_SLOTS, slot = (z % C::V_SLOTS) ^ swz<C::V_ROW>(row);
                 off[e] = (uint32_t)(row * ldv * 2 + slot * 16);
+                offf[e - C::K_DMA_W] = (uint32_t)(row * ldn * 2 + slot * 16);
             }
         }
     }
@@ -251,27 +263,68 @@ struct CopyJob {
     int32x4_t rk, rv;
     uint32_t sk, sv;   // byte offsets added to every lane's address (tile start)
     uint32_t lk, lv;
+    bool vf;           // the V^T tile is a fresh one (row stride f_n, not ldv)
 };
 
-template <int D>
-__device__ __forceinline__ CopyJob copy_job(const uint16_t *Kh, const uint16_t *Vh, int64_t ldv,
-                                            int N_kv, int t_end, int tk, int tv, uint32_t lk,
+struct Ctx {
+    const uint16_t *Kh;
+    const uint16_t *Vh;
+    const uint16_t *Kf;   // this (batch, head)'s fresh rows (FRESH only)
+    const uint16_t *Vf;
+    int64_t ldv;
+    int N_kv, t_begin, t_end;
+    int f_t0, f_t1, f_n;
+    float c;   // log2(e) * scale
+    int tid, ql, g;
+};
+
+// Key tiles [f_t0, f_t1) of a FRESH launch come from the fresh tensors.
+template <bool FRESH>
+__device__ __forceinline__ bool is_fresh(const Ctx &x, int t) {
+    return FRESH && (unsigned)(t - x.f_t0) < (unsigned)(x.f_t1 - x.f_t0);
+}
+
+template <int D, bool FRESH>
+__device__ __forceinline__ CopyJob copy_job(const Ctx &x, int tk, int tv, uint32_t lk,
                                             uint32_t lv) {
     using C = Cfg<D>;
     const int jk = tk * C::BN, jv = tv * C::BN;
     CopyJob j;
-    j.rk = buffer_rsrc(Kh + (int64_t)jk * D, tk < t_end ? (uint32_t)(N_kv - jk) * D * 2 : 0u);
-    j.rv = buffer_rsrc(Vh + jv, tv < t_end ? (uint32_t)((int64_t)D * ldv - jv) * 2 : 0u);
+    const bool kf = tk < x.t_end && is_fresh<FRESH>(x, tk);
+    const bool vf = tv < x.t_end && is_fresh<FRESH>(x, tv);
+    if (kf) {
+        const int r = jk - x.f_t0 * C::BN;   // row within the fresh rows
+        j.rk = buffer_rsrc(x.Kf + (int64_t)r * D, (uint32_t)(x.f_n - r) * D * 2);
+    } else {
+        j.rk = buffer_rsrc(x.Kh + (int64_t)jk * D,
+                           tk < x.t_end ? (uint32_t)(x.N_kv - jk) * D * 2 : 0u);
+    }
+    if (vf) {
+        const int r = jv - x.f_t0 * C::BN;
+        j.rv = buffer_rsrc(x.Vf + r, (uint32_t)((int64_t)D * x.f_n - r) * 2);
+    } else {
+        j.rv = buffer_rsrc(x.Vh + jv,
+                           tv < x.t_end ? (uint32_t)((int64_t)D * x.ldv - jv) * 2 : 0u);
+    }
     j.sk = 0u;
     j.sv = 0u;
     j.lk = lk;
     j.lv = lv;
+    j.vf = vf;
     return j;
 }
 
 template <int D>
 __device__ __forceinline__ void issue_copy(const TileDma<D> &dma, const CopyJob &j, int e) {
-    lds_dma16(e < Cfg<D>::K_DMA_W ? j.rk : j.rv, dma.off[e], e < Cfg<D>::K_DMA_W ? j.sk : j.sv,
+    using C = Cfg<D>;
+    // select values, not arrays: a selected array address would force the
+    // offsets into scratch memory
+    uint32_t voff = dma.off[e];
+    if (e >= C::K_DMA_W) {
+        const uint32_t fresh_off = dma.offf[e >= C::K_DMA_W ? e - C::K_DMA_W : 0];
+        voff = j.vf ? fresh_off : voff;
+    }
+    lds_dma16(e < C::K_DMA_W ? j.rk : j.rv, voff, e < C::K_DMA_W ? j.sk : j.sv,
               dma.lds_of(e, j.lk, j.lv));
 }
 
@@ -549,15 +602,6 @@ struct Smem {
     char v[Cfg<D>::STAGES][Cfg<D>::V_TILE];
 };
 
-struct Ctx {
-    const uint16_t *Kh;
-    const uint16_t *Vh;
-    int64_t ldv;
-    int N_kv, t_begin, t_end;
-    float c;   // log2(e) * scale
-    int tid, ql, g;
-};
-
 // One pipeline step for tile t, r = t - t_begin.  Tile t' of K and of V^T
 // lives in stage (t' - t_begin) % 4 (V "tile t_begin - 1", all zeros, in
 // stage 3).  On entry K(t+1), K(t+2), V(t-1) and V(t) are published (landed,
@@ -567,7 +611,7 @@ struct Ctx {
 // V(t-2), freed by the previous barrier; it then waits until only its own
 // copies are in flight and publishes K(t+3), V(t+1) with a barrier.  A tile
 // is thus published one step before it is read and copied two steps ahead.
-template <int D, bool RAGGED>
+template <int D, bool RAGGED, bool FRESH>
 __device__ __forceinline__ void tile_step(int t, const Ctx &x, State<D> &st, Smem<D> &sm,
                                           const TileDma<D> &dma, const OperandOffsets<D> &oo,
                                           f32x16_t (&s_cur)[Cfg<D>::SB],
@@ -590,8 +634,8 @@ __device__ __forceinline__ void tile_step(int t, const Ctx &x, State<D> &st, Sme
                 if (key >= x.N_kv) s_cur[sb][i] = -INFINITY;
             }
     }
-    const CopyJob job = copy_job<D>(x.Kh, x.Vh, x.ldv, x.N_kv, x.t_end, t + 4, t + 2,
-                                    lds_addr(sm.k[r & 3]), lds_addr(sm.v[(r + 2) & 3]));
+    const CopyJob job = copy_job<D, FRESH>(x, t + 4, t + 2, lds_addr(sm.k[r & 3]),
+                                           lds_addr(sm.v[(r + 2) & 3]));
 
     float l_tile = 0.f;
     region<D>(s_next, st.oacc, p_cur, l_tile, s_cur, p_prev, sm.k[sk1], sm.v[sv_prev], sm.k[sk2],
@@ -612,12 +656,13 @@ __device__ __forceinline__ void tile_step(int t, const Ctx &x, State<D> &st, Sme
 // The same step with the stage ring position R4 = (t - t_begin) % 4 known at
 // compile time (LDS operand addresses become immediates) and copies of full
 // in-range tiles only: fixed buffer resources over the whole (batch, head)
-// with the tile start as the scalar offset.
-template <int D, int R4>
+// (and over its fresh rows) with the tile start as the scalar offset.
+template <int D, int R4, bool FRESH>
 __device__ __forceinline__ void tile_step_static(int t, const Ctx &x, State<D> &st, Smem<D> &sm,
                                                  const TileDma<D> &dma,
                                                  const OperandOffsets<D> &oo,
                                                  const int32x4_t &rk_all, const int32x4_t &rv_all,
+                                                 const int32x4_t &rk_f, const int32x4_t &rv_f,
                                                  f32x16_t (&s_cur)[Cfg<D>::SB],
                                                  f32x16_t (&s_next)[Cfg<D>::SB],
                                                  const bf16x8_t (&p_prev)[Cfg<D>::SB][2],
@@ -628,12 +673,14 @@ __device__ __forceinline__ void tile_step_static(int t, const Ctx &x, State<D> &
     constexpr int BN = C::BN;
     constexpr int sk1 = (R4 + 1) & 3, sk2 = (R4 + 2) & 3, sv_prev = (R4 + 3) & 3;
     CopyJob job;
-    job.rk = rk_all;
-    job.rv = rv_all;
-    job.sk = (uint32_t)(t + 4) * (uint32_t)(BN * D * 2);
-    job.sv = (uint32_t)(t + 2) * (uint32_t)(BN * 2);
+    const bool kf = is_fresh<FRESH>(x, t + 4), vf = is_fresh<FRESH>(x, t + 2);
+    job.rk = kf ? rk_f : rk_all;
+    job.rv = vf ? rv_f : rv_all;
+    job.sk = (uint32_t)(kf ? t + 4 - x.f_t0 : t + 4) * (uint32_t)(BN * D * 2);
+    job.sv = (uint32_t)(vf ? t + 2 - x.f_t0 : t + 2) * (uint32_t)(BN * 2);
     job.lk = lds_addr(sm.k[R4]);
     job.lv = lds_addr(sm.v[(R4 + 2) & 3]);
+    job.vf = vf;
     float l_tile = 0.f;
     region<D>(s_next, st.oacc, p_cur, l_tile, s_cur, p_prev, sm.k[sk1], sm.v[sv_prev], sm.k[sk2],
               carry, qreg, x.c, st.m_run, oo, dma, job);
@@ -643,12 +690,63 @@ __device__ __forceinline__ void tile_step_static(int t, const Ctx &x, State<D> &
     __syncthreads();
 }
 
+// Landing workgroups of a FRESH launch: copy the fresh rows into the
+// buffer (K rows row-major, V^T channel rows), as dfp_kv_scatter would.  No
+// attention workgroup of the launch reads those buffer rows.  Four 16-byte
+// vectors per thread per pass, all loads before the stores.
 template <int D>
+__device__ __forceinline__ void land_fresh(const Params &p) {
+    // 32-bit vector indices (the launcher checks that they fit)
+    constexpr int U = 4;
+    const uint32_t stride = (uint32_t)p.land_wg * Cfg<D>::THREADS;
+    const uint32_t first = (uint32_t)((int)blockIdx.x - p.total_wg) * Cfg<D>::THREADS + threadIdx.x;
+    const uint32_t per_bh = (uint32_t)p.f_n * D / 8;   // vectors of one (b,h)'s fresh K rows
+    const uint32_t per_row = (uint32_t)p.f_n / 8;      // vectors of one fresh V^T channel row
+    const uint32_t nk = per_bh * p.BH, nv = per_row * p.BH * D;
+    const uint4 *kf = reinterpret_cast<const uint4 *>(p.Kf);
+    const uint4 *vf = reinterpret_cast<const uint4 *>(p.Vtf);
+    uint4 *kw = reinterpret_cast<uint4 *>(p.Kw + (int64_t)p.f_row0 * D);
+    uint4 *vw = reinterpret_cast<uint4 *>(p.Vtw + p.f_row0);
+    const uint32_t kw_bh = (uint32_t)p.N_kv * D / 8;   // buffer vectors per (b,h)
+    const uint32_t vw_row = (uint32_t)(p.ldv / 8);      // buffer vectors per V^T row
+    for (uint32_t v0 = first; v0 < nk; v0 += U * stride) {
+        uint4 a[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint32_t v = v0 + u * stride;
+            a[u] = v < nk ? kf[v] : make_uint4(0u, 0u, 0u, 0u);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint32_t v = v0 + u * stride, bh = v / per_bh;
+            if (v < nk) kw[(uint64_t)bh * kw_bh + (v - bh * per_bh)] = a[u];
+        }
+    }
+    for (uint32_t v0 = first; v0 < nv; v0 += U * stride) {
+        uint4 a[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint32_t v = v0 + u * stride;
+            a[u] = v < nv ? vf[v] : make_uint4(0u, 0u, 0u, 0u);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint32_t v = v0 + u * stride, row = v / per_row;
+            if (v < nv) vw[(uint64_t)row * vw_row + (v - row * per_row)] = a[u];
+        }
+    }
+}
+
+template <int D, bool FRESH>
 __global__ __launch_bounds__(Cfg<D>::THREADS, Cfg<D>::WG_PER_CU) void attn_fwd_bf16(Params p) {
     using C = Cfg<D>;
     constexpr int BN = C::BN;
     __shared__ __attribute__((aligned(16))) Smem<D> sm;
     __shared__ int s_last;
+    if (FRESH && (int)blockIdx.x >= p.total_wg) {
+        land_fresh<D>(p);
+        return;
+    }
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -670,6 +768,11 @@ __global__ __launch_bounds__(Cfg<D>::THREADS, Cfg<D>::WG_PER_CU) void attn_fwd_b
     Ctx x;
     x.Kh = p.K + (int64_t)bh * N_kv * D;
     x.Vh = p.Vt + (int64_t)bh * D * p.ldv;
+    x.Kf = FRESH ? p.Kf + (int64_t)bh * p.f_n * D : nullptr;
+    x.Vf = FRESH ? p.Vtf + (int64_t)bh * D * p.f_n : nullptr;
+    x.f_t0 = FRESH ? p.f_t0 : 0;
+    x.f_t1 = FRESH ? p.f_t1 : 0;
+    x.f_n = FRESH ? p.f_n : 0;
     x.ldv = p.ldv;
     x.N_kv = N_kv;
     const int ntiles = (N_kv + BN - 1) / BN;
@@ -702,17 +805,17 @@ __global__ __launch_bounds__(Cfg<D>::THREADS, Cfg<D>::WG_PER_CU) void attn_fwd_b
     // it; S(t0) and the reference max; the first step's first operands;
     // K(t0+3) and V(t0+1) in flight (the loop's entry state).
     TileDma<D> dma;
-    dma.init(wave, lane, p.ldv);
+    dma.init(wave, lane, p.ldv, FRESH ? p.f_n : 0);
     OperandOffsets<D> oo;
     oo.init(ql, g);
     const int t0 = x.t_begin;
     {
-        const CopyJob j0 = copy_job<D>(x.Kh, x.Vh, x.ldv, N_kv, x.t_end, t0, t0,
-                                       lds_addr(sm.k[0]), lds_addr(sm.v[0]));
-        const CopyJob j1 = copy_job<D>(x.Kh, x.Vh, x.ldv, N_kv, x.t_end, t0 + 1, t0 + 1,
-                                       lds_addr(sm.k[1]), lds_addr(sm.v[1]));
-        const CopyJob j2 = copy_job<D>(x.Kh, x.Vh, x.ldv, N_kv, x.t_end, t0 + 2, t0 + 2,
-                                       lds_addr(sm.k[2]), lds_addr(sm.v[2]));
+        const CopyJob j0 =
+            copy_job<D, FRESH>(x, t0, t0, lds_addr(sm.k[0]), lds_addr(sm.v[0]));
+        const CopyJob j1 =
+            copy_job<D, FRESH>(x, t0 + 1, t0 + 1, lds_addr(sm.k[1]), lds_addr(sm.v[1]));
+        const CopyJob j2 =
+            copy_job<D, FRESH>(x, t0 + 2, t0 + 2, lds_addr(sm.k[2]), lds_addr(sm.v[2]));
 #pragma unroll
         for (int e = 0; e < C::DMA_W; ++e) issue_copy<D>(dma, j0, e);   // K(t0), V(t0)
 #pragma unroll
@@ -753,8 +856,8 @@ __global__ __launch_bounds__(Cfg<D>::THREADS, Cfg<D>::WG_PER_CU) void attn_fwd_b
     bf16x8_t carry[2] = {step_operand<D>(0, sm.k[1], sm.v[0], oo),
                          step_operand<D>(1, sm.k[1], sm.v[0], oo)};
     {
-        const CopyJob j3 = copy_job<D>(x.Kh, x.Vh, x.ldv, N_kv, x.t_end, t0 + 3, t0 + 1,
-                                       lds_addr(sm.k[3]), lds_addr(sm.v[1]));
+        const CopyJob j3 =
+            copy_job<D, FRESH>(x, t0 + 3, t0 + 1, lds_addr(sm.k[3]), lds_addr(sm.v[1]));
 #pragma unroll
         for (int e = 0; e < C::DMA_W; ++e) issue_copy<D>(dma, j3, e);   // K(t0+3), V(t0+1)
     }
@@ -770,23 +873,29 @@ __global__ __launch_bounds__(Cfg<D>::THREADS, Cfg<D>::WG_PER_CU) void attn_fwd_b
         const int n_full = min(x.t_end, N_kv / BN);
         const int32x4_t rk_all = buffer_rsrc(x.Kh, (uint32_t)N_kv * D * 2);
         const int32x4_t rv_all = buffer_rsrc(x.Vh, (uint32_t)((int64_t)D * x.ldv * 2));
+        const int32x4_t rk_f = buffer_rsrc(x.Kf, (uint32_t)x.f_n * D * 2);
+        const int32x4_t rv_f = buffer_rsrc(x.Vf, (uint32_t)((int64_t)D * x.f_n * 2));
         for (; t + 8 <= n_full; t += 4) {
-            tile_step_static<D, 0>(t, x, st, sm, dma, oo, rk_all, rv_all, sA, sB, pB, pA, carry, qreg);
-            tile_step_static<D, 1>(t + 1, x, st, sm, dma, oo, rk_all, rv_all, sB, sA, pA, pB, carry, qreg);
-            tile_step_static<D, 2>(t + 2, x, st, sm, dma, oo, rk_all, rv_all, sA, sB, pB, pA, carry, qreg);
-            tile_step_static<D, 3>(t + 3, x, st, sm, dma, oo, rk_all, rv_all, sB, sA, pA, pB, carry, qreg);
+            tile_step_static<D, 0, FRESH>(t, x, st, sm, dma, oo, rk_all, rv_all, rk_f, rv_f, sA,
+                                          sB, pB, pA, carry, qreg);
+            tile_step_static<D, 1, FRESH>(t + 1, x, st, sm, dma, oo, rk_all, rv_all, rk_f, rv_f,
+                                          sB, sA, pA, pB, carry, qreg);
+            tile_step_static<D, 2, FRESH>(t + 2, x, st, sm, dma, oo, rk_all, rv_all, rk_f, rv_f,
+                                          sA, sB, pB, pA, carry, qreg);
+            tile_step_static<D, 3, FRESH>(t + 3, x, st, sm, dma, oo, rk_all, rv_all, rk_f, rv_f,
+                                          sB, sA, pA, pB, carry, qreg);
         }
     }
     for (; t + 2 < x.t_end; t += 2) {
-        tile_step<D, false>(t, x, st, sm, dma, oo, sA, sB, pB, pA, carry, qreg);
-        tile_step<D, false>(t + 1, x, st, sm, dma, oo, sB, sA, pA, pB, carry, qreg);
+        tile_step<D, false, FRESH>(t, x, st, sm, dma, oo, sA, sB, pB, pA, carry, qreg);
+        tile_step<D, false, FRESH>(t + 1, x, st, sm, dma, oo, sB, sA, pA, pB, carry, qreg);
     }
     if (t + 1 < x.t_end) {
-        tile_step<D, true>(t, x, st, sm, dma, oo, sA, sB, pB, pA, carry, qreg);
-        tile_step<D, true>(t + 1, x, st, sm, dma, oo, sB, sA, pA, pB, carry, qreg);
+        tile_step<D, true, FRESH>(t, x, st, sm, dma, oo, sA, sB, pB, pA, carry, qreg);
+        tile_step<D, true, FRESH>(t + 1, x, st, sm, dma, oo, sB, sA, pA, pB, carry, qreg);
         pv_tile<D>(st.oacc, pB, sm.v[(t + 1 - t0) & 3], oo);
     } else {
-        tile_step<D, true>(t, x, st, sm, dma, oo, sA, sB, pB, pA, carry, qreg);
+        tile_step<D, true, FRESH>(t, x, st, sm, dma, oo, sA, sB, pB, pA, carry, qreg);
         pv_tile<D>(st.oacc, pA, sm.v[(t - t0) & 3], oo);
     }
     wait_dma_all();   // no copy may outlive the workgroup's LDS
@@ -986,7 +1095,7 @@ size_t dfp_attn_workspace_bytes(int B, int H, int n_q, int N_kv, int d) {
 
 dfp_status dfp_attn_bf16_launch(void *o, const void *q, const void *k, const void *vt, int BH,
                                 int n_q, int N_kv, int d, float scale, void *ws, size_t ws_bytes,
-                                hipStream_t stream) {
+                                const dfp_fresh_rows *fresh, hipStream_t stream) {
     // tile copies address one (batch, head)'s K and V^T with 32-bit offsets
     const int64_t ldv = dfp_v_ld(N_kv, DFP_BF16);
     if ((int64_t)N_kv * d * 2 >= (int64_t(1) << 31) || (int64_t)d * ldv * 2 >= (int64_t(1) << 31))
@@ -996,7 +1105,19 @@ dfp_status dfp_attn_bf16_launch(void *o, const void *q, const void *k, const voi
                           (reinterpret_cast<uintptr_t>(ws) & 255u) != 0))
         pl = make_plan(BH, n_q, N_kv, d, false);
     const int64_t blocks = (int64_t)pl.q_tiles * BH * pl.splits;
-    if (blocks > 0x7FFFFFFF) return DFP_ERR_UNSUPPORTED;
+    // landing workgroups take the resident slots the attention grid leaves
+    // free in its last round (at least 16, at most 64)
+    int land_wg = 0;
+    if (fresh && fresh->land) {
+        const int64_t slots = (int64_t)kCus * (d == 64 ? Cfg<64>::WG_PER_CU : Cfg<128>::WG_PER_CU);
+        const int64_t free = (slots - blocks % slots) % slots;
+        land_wg = (int)(free < 16 ? 16 : (free > 64 ? 64 : free));
+    }
+    if (blocks + land_wg > 0x7FFFFFFF) return DFP_ERR_UNSUPPORTED;
+    // landing indexes 16-byte vectors of the fresh tensors with 32 bits
+    if (fresh && ((int64_t)BH * fresh->n * d / 8 >= (int64_t(1) << 31) ||
+                  (int64_t)N_kv * d / 8 >= (int64_t(1) << 31)))
+        return DFP_ERR_UNSUPPORTED;
 
     Params p{};
     p.Q = static_cast<const uint16_t *>(q);
@@ -1011,6 +1132,18 @@ dfp_status dfp_attn_bf16_launch(void *o, const void *q, const void *k, const voi
     p.splits = pl.splits;
     p.tiles_per_split = pl.tiles_per_split;
     p.total_wg = (int)blocks;
+    p.BH = BH;
+    if (fresh) {
+        p.Kf = static_cast<const uint16_t *>(fresh->k_new);
+        p.Vtf = static_cast<const uint16_t *>(fresh->v_new_t);
+        p.Kw = static_cast<uint16_t *>(fresh->k_buf);
+        p.Vtw = static_cast<uint16_t *>(fresh->v_buf_t);
+        p.f_row0 = fresh->row0;
+        p.f_n = fresh->n;
+        p.f_t0 = fresh->row0 / 64;
+        p.f_t1 = (fresh->row0 + fresh->n) / 64;
+        p.land_wg = land_wg;
+    }
     if (pl.splits > 1) {
         char *w = static_cast<char *>(ws);
         p.counters = reinterpret_cast<unsigned *>(w);
@@ -1020,12 +1153,17 @@ dfp_status dfp_attn_bf16_launch(void *o, const void *q, const void *k, const voi
         w += slots * pl.block_m * d * sizeof(float);
         p.part_ml = reinterpret_cast<float *>(w);
     }
-    if (d == 64)
-        hipLaunchKernelGGL(attn_fwd_bf16<64>, dim3((unsigned)blocks), dim3(Cfg<64>::THREADS), 0,
-                           stream, p);
+    const dim3 grid((unsigned)(blocks + land_wg));
+    if (d == 64 && fresh)
+        hipLaunchKernelGGL((attn_fwd_bf16<64, true>), grid, dim3(Cfg<64>::THREADS), 0, stream, p);
+    else if (d == 64)
+        hipLaunchKernelGGL((attn_fwd_bf16<64, false>), grid, dim3(Cfg<64>::THREADS), 0, stream, p);
+    else if (d == 128 && fresh)
+        hipLaunchKernelGGL((attn_fwd_bf16<128, true>), grid, dim3(Cfg<128>::THREADS), 0, stream,
+                           p);
     else if (d == 128)
-        hipLaunchKernelGGL(attn_fwd_bf16<128>, dim3((unsigned)blocks), dim3(Cfg<128>::THREADS), 0,
-                           stream, p);
+        hipLaunchKernelGGL((attn_fwd_bf16<128, false>), grid, dim3(Cfg<128>::THREADS), 0, stream,
+                           p);
     else
         return DFP_ERR_UNSUPPORTED;
     return dfp::launch_status();

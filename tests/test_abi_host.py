@@ -100,6 +100,39 @@ def test_attention_validation(L, args, expect):
     assert L.dfp_patch_attention(*args, NULL, 0, S0) == expect
 
 
+MIS = ctypes.c_void_p(0x100008)   # 8-byte aligned only
+
+
+# (o, q, k_buf, v_buf_t, k_new, v_new_t, B, H, n_q, N_kv, d, row0, n, land, scale, dt)
+@pytest.mark.parametrize("args,expect", [
+    # fresh range outside the buffer, empty or negative
+    ((FAKE,) * 6 + (2, 2, 16, 256, 64, 192, 128, 1, 0.125, dfp.BF16), dfp.ERR_INVALID_ARG),
+    ((FAKE,) * 6 + (2, 2, 16, 256, 64, -64, 128, 1, 0.125, dfp.BF16), dfp.ERR_INVALID_ARG),
+    ((FAKE,) * 6 + (2, 2, 16, 256, 64, 0, 0, 1, 0.125, dfp.BF16), dfp.ERR_INVALID_ARG),
+    # not whole 64-key tiles
+    ((FAKE,) * 6 + (2, 2, 16, 256, 64, 32, 128, 1, 0.125, dfp.BF16), dfp.ERR_UNSUPPORTED),
+    ((FAKE,) * 6 + (2, 2, 16, 256, 64, 64, 100, 1, 0.125, dfp.BF16), dfp.ERR_UNSUPPORTED),
+    # bf16 only; d 64 or 128
+    ((FAKE,) * 6 + (2, 2, 16, 256, 64, 64, 128, 1, 0.125, dfp.F32), dfp.ERR_UNSUPPORTED),
+    ((FAKE,) * 6 + (2, 2, 16, 256, 96, 64, 128, 1, 0.125, dfp.BF16), dfp.ERR_UNSUPPORTED),
+    # null or misaligned pointers, bad scale, bad sizes
+    ((FAKE, FAKE, FAKE, FAKE, NULL, FAKE, 2, 2, 16, 256, 64, 64, 128, 1, 0.125, dfp.BF16),
+     dfp.ERR_INVALID_ARG),
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, MIS, 2, 2, 16, 256, 64, 64, 128, 1, 0.125, dfp.BF16),
+     dfp.ERR_INVALID_ARG),
+    ((NULL, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 2, 16, 256, 64, 64, 128, 1, 0.125, dfp.BF16),
+     dfp.ERR_INVALID_ARG),
+    ((FAKE,) * 6 + (2, 2, 16, 256, 64, 64, 128, 1, float("nan"), dfp.BF16), dfp.ERR_INVALID_ARG),
+    ((FAKE,) * 6 + (0, 2, 16, 256, 64, 64, 128, 1, 0.125, dfp.BF16), dfp.ERR_INVALID_ARG),
+    ((FAKE,) * 6 + (2, 2, -1, 256, 64, 64, 128, 1, 0.125, dfp.BF16), dfp.ERR_INVALID_ARG),
+    # no queries and no landing: nothing to do
+    ((NULL, NULL, NULL, NULL, NULL, NULL, 2, 2, 0, 256, 64, 64, 128, 0, 0.125, dfp.BF16),
+     dfp.OK),
+])
+def test_fresh_attention_validation(L, args, expect):
+    assert L.dfp_patch_attention_fresh(*args, NULL, 0, S0) == expect
+
+
 def test_cfg_step_validation(L):
     ws_need = dfp.workspace_bytes(dfp.OP_CFG_STEP, 4096, 1)
     assert ws_need > 256

@@ -136,6 +136,62 @@ def test_forced_split_kv_every_element(monkeypatch, splits, B, H, nq, N, d):
     np.testing.assert_array_equal(G.down(o), first)
 
 
+@pytest.mark.parametrize("land", [False, True])
+@pytest.mark.parametrize("B,H,nq,N,d,row0,n,splits", [
+    (1, 2, 200, 1000, 64, 256, 512, 0),    # ragged last tile after the fresh rows
+    (1, 2, 200, 1000, 64, 256, 512, 3),    # split key ranges that start inside them
+    (2, 1, 130, 1024, 64, 0, 256, 0),      # fresh rows first
+    (2, 1, 130, 1024, 64, 768, 256, 5),    # fresh rows last
+    (1, 1, 64, 64, 64, 0, 64, 0),          # the whole buffer is one fresh tile
+    (1, 2, 300, 1024, 64, 64, 768, 0),     # long fresh range through the four-step loop
+    (1, 2, 300, 700, 128, 128, 384, 0),    # d=128
+    (1, 2, 300, 700, 128, 128, 384, 2),
+])
+def test_fresh_rows_every_element(monkeypatch, B, H, nq, N, d, row0, n, splits, land):
+    """dfp_patch_attention_fresh: the buffer's own rows in the fresh range
+    hold NaN and must never be read; the output matches the oracle over the
+    effective K/V and is bitwise the output of scatter + dfp_patch_attention;
+    with land the buffer ends up exactly as dfp_kv_scatter leaves it, without
+    it untouched."""
+    G.require_gpu()
+    G.announce(f"attention fresh rows land={land} B{B} H{H} nq{nq} N{N} d{d} "
+               f"row0={row0} n={n} splits={splits}")
+    if splits:
+        monkeypatch.setenv("DFP_ATTN_SPLITS", str(splits))
+    torch = G.torch_mod()
+    q, k_st, v_st = inputs.random_attention_arrays(B, H, nq, N, d, seed=row0 + n + d)
+    _, k_new, v_new = inputs.random_attention_arrays(B, H, 1, n, d, seed=row0 + n + d + 1)
+    k_buf, v_buf = dfp.alloc_kv_buffer(B, H, N, d, torch.bfloat16)
+    dfp.kv_scatter(k_buf, v_buf, G.up(k_st, "bf16"), G.up(v_st, "bf16"), 0)
+    k_buf[:, :, row0:row0 + n] = float("nan")
+    v_buf[:, :, :, row0:row0 + n] = float("nan")
+    kd = G.up(k_new, "bf16")
+    vtd = G.up(np.swapaxes(v_new, -1, -2), "bf16")
+    qd = G.up(q, "bf16")
+    o = torch.empty_like(qd)
+    ws = dfp.attention_workspace(B, H, nq, N, d)
+    dfp.patch_attention_fresh(o, qd, k_buf, v_buf, kd, vtd, row0, land, None, ws)
+    torch.cuda.synchronize()
+    got = G.down(o)
+    if ws is not None:
+        G.assert_counters_zero(ws, B * H, nq, d)
+    k_eff, v_eff = k_st.copy(), v_st.copy()
+    k_eff[:, :, row0:row0 + n], v_eff[:, :, row0:row0 + n] = k_new, v_new
+    _check(got, oracle.attention(q, k_eff, v_eff, 1.0 / d ** 0.5), "bf16", "fresh")
+    if land:
+        np.testing.assert_array_equal(G.down(k_buf), k_eff)
+        np.testing.assert_array_equal(G.v_buffer_to_rows(v_buf, N), v_eff)
+    else:
+        assert np.isnan(G.down(k_buf)[:, :, row0:row0 + n]).all()
+        assert np.isnan(G.down(v_buf)[:, :, :, row0:row0 + n]).all()
+        k_buf[:, :, row0:row0 + n] = kd            # the scatter's result, for the reference
+        v_buf[:, :, :, row0:row0 + n] = vtd
+    o2 = torch.empty_like(qd)
+    dfp.patch_attention(o2, qd, k_buf, v_buf, None, ws)   # same plan over the landed buffer
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(G.down(o2), got)
+
+
 def test_constant_values_and_single_key_properties():
     G.require_gpu()
     G.announce("attention properties (V=1, N_kv=1) at the SDXL-1024 64x64 shape")

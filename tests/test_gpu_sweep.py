@@ -23,14 +23,21 @@ BF16_MAX_ABS = 2e-2
 F32_MAX_ABS = 1e-4
 
 
-@pytest.mark.parametrize("name,heads", [("tiny-f32", None), ("sdxl1024-64x64", None),
-                                        ("sdxl1024-32x32", None), ("dit1024", 2),
-                                        ("sdxl2048", 1)])
-def test_patch_sweep_every_patch(name, heads):
+@pytest.mark.parametrize("name,heads,fresh", [("tiny-f32", None, False),
+                                              ("sdxl1024-64x64", None, False),
+                                              ("sdxl1024-32x32", None, False),
+                                              ("dit1024", 2, False), ("sdxl2048", 1, False),
+                                              ("sdxl1024-64x64", None, True),
+                                              ("sdxl1024-32x32", None, True),
+                                              ("sdxl2048", 1, True)])
+def test_patch_sweep_every_patch(name, heads, fresh):
+    """With `fresh` each patch runs dfp_patch_attention_fresh (reading its own
+    rows from the fresh tensors and landing them) instead of scatter +
+    dfp_patch_attention."""
     G.require_gpu()
     torch = G.torch_mod()
     level = inputs.LEVELS[name]
-    G.announce(f"patch sweep {name} (P={level.P})")
+    G.announce(f"patch sweep {name} (P={level.P}) fresh={fresh}")
     kind = level.dtype
     x = inputs.attention_inputs(level, stale_std=1.0)
     B, H, N, d, n = level.B, level.H, level.N_kv, level.d, level.n
@@ -45,10 +52,15 @@ def test_patch_sweep_every_patch(name, heads):
     ws = dfp.attention_workspace(B, H, n, N, d)
     for m in range(level.P):
         kf, vf = x.fresh_rows(m)
-        dfp.kv_scatter(k_buf, v_buf, G.up(kf, kind), G.up(vf, kind), level.row0(m))
         q = G.up(x.q_patch(m), kind)
         o = torch.empty_like(q)
-        dfp.patch_attention(o, q, k_buf, v_buf, 1.0 / d ** 0.5, ws)
+        if fresh:
+            dfp.patch_attention_fresh(o, q, k_buf, v_buf, G.up(kf, kind),
+                                      G.up(np.swapaxes(vf, -1, -2), kind), level.row0(m),
+                                      True, 1.0 / d ** 0.5, ws)
+        else:
+            dfp.kv_scatter(k_buf, v_buf, G.up(kf, kind), G.up(vf, kind), level.row0(m))
+            dfp.patch_attention(o, q, k_buf, v_buf, 1.0 / d ** 0.5, ws)
         torch.cuda.synchronize()
         got = G.down(o)[sl]
         err = np.abs(got - want[m]).max()
