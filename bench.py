@@ -10,8 +10,8 @@ w=7.5):
       launch (dfp_patch_attention_fresh)
   the same for the 32x32 level
   fused CFG + DDIM update + rel-MAE on the latent.
-A level whose patch rows are not whole 64-key tiles, or that has always-fresh
-text rows, lands its K/V with dfp_kv_scatter and then runs
+A level whose patch rows are not whole 64-key tiles (SDXL-3840), or with
+d = 128 (DiT), lands its K/V with dfp_kv_scatter and then runs
 dfp_patch_attention; `--no-fresh` times that path everywhere.
 All inputs are seeded synthetic arrays resident in HBM before timing starts.
 The timed steps replay one HIP graph of the step (falls back to eager
@@ -103,8 +103,12 @@ class Level:
 
         self.k_buf, self.v_buf = dfp.alloc_kv_buffer(level.B, level.H, level.N_kv, level.d, bf)
         dfp.kv_scatter(self.k_buf, self.v_buf, up(x.k_stale), up(x.v_stale), 0)
-        # fused path: whole 64-key tiles of fresh rows and no text rows
-        self.fused = (fresh and not level.n_text and level.n % 64 == 0 and
+        # fused path: every fresh range (the patch, a DiT's text rows) whole 64-key
+        # tiles, and d = 64: at d = 128 the fused kernel's extra per-range copy
+        # offsets spill from the full register file inside the main loop and cost
+        # more than the separate landing kernel saves
+        self.fused = (fresh and level.d == 64 and level.n % 64 == 0 and
+                      level.n_text % 64 == 0 and
                       all(level.row0(p) % 64 == 0 for p in self.patches))
         self.fresh, self.q, self.o = [], [], []
         for p in self.patches:
@@ -117,7 +121,7 @@ class Level:
         self.text = None
         if level.n_text:
             kt, vt = x.text_rows()
-            self.text = (up(kt), up(vt))
+            self.text = (up(kt), up(np.swapaxes(vt, -1, -2) if self.fused else vt))
         self.ws = dfp.attention_workspace(level.B, level.H, level.n, level.N_kv, level.d)
         self.scale = 1.0 / level.d ** 0.5
         self.flops = level.flops() * len(self.patches)
@@ -135,9 +139,9 @@ class Level:
         dfp.patch_attention(self.o[i], self.q[i], self.k_buf, self.v_buf, self.scale, self.ws)
 
     def attend_fresh(self, dfp, i=0):
-        k, vt, row0 = self.fresh[i]
-        dfp.patch_attention_fresh(self.o[i], self.q[i], self.k_buf, self.v_buf, k, vt, row0,
-                                  True, self.scale, self.ws)
+        ranges = ([(self.text[0], self.text[1], 0)] if self.text else []) + [self.fresh[i]]
+        dfp.patch_attention_fresh(self.o[i], self.q[i], self.k_buf, self.v_buf, ranges, True,
+                                  self.scale, self.ws)
 
     def run(self, dfp):
         for i in range(len(self.patches)):
@@ -380,7 +384,7 @@ def main():
         dom.level.name)
     roofline = {"bound": "mfma", "achieved": dk["tflops"], "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": dk["tflops"] / PEAK_BF16_TFLOPS, "traffic": traffic,
-                "kernel": f"attn_fwd_bf16<{dom.level.d}{', fresh' if dom.fused else ''}> "
+                "kernel": f"attn_fwd_bf16<{dom.level.d}, {1 if dom.fused else 0}> "
                           f"({dom.level.name}, "
                           f"{dom.level.flops() / 1e9:.2f} GFLOP per launch)"}
 

@@ -148,38 +148,50 @@ dfp_status dfp_patch_attention(void *o, const void *q, const void *k_buf,
                                void *workspace, size_t ws_bytes,
                                hipStream_t stream);
 
+/* One range of fresh rows for dfp_patch_attention_fresh: this step's keys
+ * and values of buffer rows row0..row0+n-1.
+ *   k    [B][H][n][d]   device pointer, 16-byte aligned.
+ *   v_t  [B][H][d][n]   device pointer, 16-byte aligned; values stored
+ *                       TRANSPOSED (channel-major), as the buffer stores V --
+ *                       a projection can emit this layout directly by
+ *                       swapping its GEMM operands.
+ *   row0, n             multiples of 64 (whole 64-key tiles). */
+typedef struct {
+    const void *k;
+    const void *v_t;
+    int row0;
+    int n;
+} dfp_fresh_rows;
+
 /* (a1-a4) One patch's attention with its fresh rows read straight from this
  * step's K/V, and (optionally) their landing in the buffer, in one launch.
- * [DF]: the device computes fresh activations for its own patch and attends
- * over them together with the previous step's activations of every other
- * patch; the fresh ones are also what the next step reuses.  The result is
- * dfp_patch_attention over the buffer with rows [row0, row0+n) replaced by
- * the fresh rows; the buffer's own rows there are never read, so the
- * landing (land != 0) can write them during the same launch, exactly as
- * dfp_kv_scatter(k_new, transpose(v_new_t), row0) would.
+ * [DF]: the device computes fresh activations for its own patch (and a
+ * DiT's always-fresh text tokens) and attends over them together with the
+ * previous step's activations of every other patch; the fresh ones are also
+ * what the next step reuses.  The result is dfp_patch_attention over the
+ * buffer with the rows of every fresh range replaced by that range's rows;
+ * the buffer's own rows there are never read, so the landing (land != 0)
+ * can write them during the same launch, exactly as dfp_kv_scatter(k,
+ * transpose(v_t), row0) of each range would.
  *
  *   o, q, scale, workspace/ws_bytes   as dfp_patch_attention (bf16 only).
- *   k_buf   [B][H][N_kv][d]   read outside [row0, row0+n); rows inside are
- *                             overwritten with k_new when land != 0.
- *   v_buf_t [B][H][d][ldv]    likewise for columns [row0, row0+n).
- *   k_new   [B][H][n][d]      this step's keys of rows row0..row0+n-1.
- *   v_new_t [B][H][d][n]      this step's values of those rows, stored
- *                             TRANSPOSED (channel-major), as the buffer
- *                             stores V; a projection can emit this layout
- *                             directly by swapping its GEMM operands.
- * row0 and n must be multiples of 64 (whole 64-key tiles); inputs must not
- * alias the buffer.  With land == 0 the buffer is not written.  n_q == 0
- * with land != 0 only lands (o and q may then be NULL).
- * Errors: INVALID_ARG for null or misaligned pointers, non-positive B/H/N_kv,
- * negative n_q, n <= 0, row0 < 0, row0 + n > N_kv, a bad scale; UNSUPPORTED
- * for dt other than bf16, d other than 64/128, row0 or n not a multiple of
- * 64, or a (b,h) slice of k_buf or v_buf_t reaching 2 GiB. */
+ *   k_buf   [B][H][N_kv][d]   read outside the fresh ranges; rows inside are
+ *                             overwritten with the fresh keys when land != 0.
+ *   v_buf_t [B][H][d][ldv]    likewise for the fresh columns.
+ *   fresh   host array of n_fresh (1 or 2) non-overlapping ranges.
+ * Inputs must not alias the buffer.  With land == 0 the buffer is not
+ * written.  n_q == 0 with land != 0 only lands (o and q may then be NULL).
+ * Errors: INVALID_ARG for null or misaligned pointers, a NULL fresh array or
+ * n_fresh < 1, a range with n <= 0, row0 < 0 or row0 + n > N_kv, overlapping
+ * ranges, non-positive B/H/N_kv, negative n_q, a bad scale; UNSUPPORTED for
+ * n_fresh > 2, dt other than bf16, d other than 64/128, a range not made of
+ * whole 64-key tiles, or a (b,h) slice of k_buf or v_buf_t reaching 2 GiB. */
 dfp_status dfp_patch_attention_fresh(void *o, const void *q, void *k_buf,
-                                     void *v_buf_t, const void *k_new,
-                                     const void *v_new_t, int B, int H, int n_q,
-                                     int N_kv, int d, int row0, int n, int land,
-                                     float scale, dfp_dtype dt, void *workspace,
-                                     size_t ws_bytes, hipStream_t stream);
+                                     void *v_buf_t, const dfp_fresh_rows *fresh,
+                                     int n_fresh, int B, int H, int n_q, int N_kv,
+                                     int d, int land, float scale, dfp_dtype dt,
+                                     void *workspace, size_t ws_bytes,
+                                     hipStream_t stream);
 
 /* (a5-a7) Fused guidance + sampler update + rel-MAE, one pass over HBM.
  * [XD] 三.3 / [HY] 关键设计 1: the step consumes a conditional and an

@@ -152,25 +152,33 @@ extern "C" dfp_status dfp_patch_attention(void *o, const void *q, const void *k_
 }
 
 extern "C" dfp_status dfp_patch_attention_fresh(void *o, const void *q, void *k_buf, void *v_buf_t,
-                                                const void *k_new, const void *v_new_t, int B,
-                                                int H, int n_q, int N_kv, int d, int row0, int n,
-                                                int land, float scale, dfp_dtype dt,
-                                                void *workspace, size_t ws_bytes,
-                                                hipStream_t stream) {
+                                                const dfp_fresh_rows *fresh, int n_fresh, int B,
+                                                int H, int n_q, int N_kv, int d, int land,
+                                                float scale, dfp_dtype dt, void *workspace,
+                                                size_t ws_bytes, hipStream_t stream) {
     if (B <= 0 || H <= 0 || N_kv <= 0 || n_q < 0) return DFP_ERR_INVALID_ARG;
     if (!(scale > 0.f) || !std::isfinite(scale)) return DFP_ERR_INVALID_ARG;
-    if (row0 < 0 || n <= 0 || (int64_t)row0 + n > N_kv) return DFP_ERR_INVALID_ARG;
+    if (!fresh || n_fresh < 1) return DFP_ERR_INVALID_ARG;
+    if (n_fresh > 2) return DFP_ERR_UNSUPPORTED;
+    for (int r = 0; r < n_fresh; ++r) {
+        const dfp_fresh_rows &f = fresh[r];
+        if (f.row0 < 0 || f.n <= 0 || (int64_t)f.row0 + f.n > N_kv) return DFP_ERR_INVALID_ARG;
+        if (!f.k || !f.v_t || !aligned16(f.k) || !aligned16(f.v_t)) return DFP_ERR_INVALID_ARG;
+    }
+    if (n_fresh == 2 && fresh[0].row0 < fresh[1].row0 + fresh[1].n &&
+        fresh[1].row0 < fresh[0].row0 + fresh[0].n)
+        return DFP_ERR_INVALID_ARG;   // overlapping ranges
     if (dt != DFP_BF16) return DFP_ERR_UNSUPPORTED;
     if (d != 64 && d != 128) return DFP_ERR_UNSUPPORTED;
-    if (row0 % 64 != 0 || n % 64 != 0) return DFP_ERR_UNSUPPORTED;
+    for (int r = 0; r < n_fresh; ++r)
+        if (fresh[r].row0 % 64 != 0 || fresh[r].n % 64 != 0) return DFP_ERR_UNSUPPORTED;
     if (n_q == 0 && !land) return DFP_OK;
-    if (!k_buf || !v_buf_t || !k_new || !v_new_t) return DFP_ERR_INVALID_ARG;
-    if (!aligned16(k_buf) || !aligned16(v_buf_t) || !aligned16(k_new) || !aligned16(v_new_t))
+    if (!k_buf || !v_buf_t || !aligned16(k_buf) || !aligned16(v_buf_t))
         return DFP_ERR_INVALID_ARG;
     if (n_q > 0 && (!o || !q || !aligned16(o) || !aligned16(q))) return DFP_ERR_INVALID_ARG;
     const int64_t BH = (int64_t)B * H;
     if (BH > 0x7FFFFFFF) return DFP_ERR_UNSUPPORTED;
-    const dfp_fresh_rows fresh{k_new, v_new_t, k_buf, v_buf_t, row0, n, land ? 1 : 0};
+    const dfp_fresh_launch launch{fresh, n_fresh, k_buf, v_buf_t, land ? 1 : 0};
     return dfp_attn_bf16_launch(o, q, k_buf, v_buf_t, (int)BH, n_q, N_kv, d, scale, workspace,
-                                ws_bytes, &fresh, stream);
+                                ws_bytes, &launch, stream);
 }

@@ -92,14 +92,15 @@ struct Params {
     int splits;
     int tiles_per_split;
     int total_wg;        // attention workgroups; landing workgroups follow them
-    // Fresh rows (dfp_patch_attention_fresh): key tiles [f_t0, f_t1), rows
-    // [f_row0, f_row0 + f_n), are read from Kf / Vtf instead of the buffer,
-    // and land_wg workgroups after the attention ones copy them into it.
-    const uint16_t *Kf;  // [BH][f_n][D]
-    const uint16_t *Vtf; // [BH][D][f_n]
-    uint16_t *Kw;        // the buffer again, writable (landing)
+    // Fresh rows (dfp_patch_attention_fresh), up to two ranges r: key tiles
+    // [f_t0[r], f_t1[r]), rows [f_row0[r], f_row0[r] + f_n[r]), are read
+    // from Kf[r] / Vtf[r] instead of the buffer, and land_wg workgroups
+    // after the attention ones copy them into it.
+    const uint16_t *Kf[2];   // [BH][f_n][D]
+    const uint16_t *Vtf[2];  // [BH][D][f_n]
+    uint16_t *Kw;            // the buffer again, writable (landing)
     uint16_t *Vtw;
-    int f_t0, f_t1, f_row0, f_n;
+    int f_t0[2], f_t1[2], f_row0[2], f_n[2];
     int BH;
     int land_wg;
 };
@@ -229,10 +230,11 @@ template <int D>
 struct TileDma {
     using C = Cfg<D>;
     uint32_t off[C::DMA_W];   // byte offset of this lane's chunk within a tile
-    uint32_t offf[C::DMA_W - C::K_DMA_W];   // V^T chunks of a fresh tile (row stride ldn)
+    uint32_t offf[2][C::DMA_W - C::K_DMA_W];   // V^T chunks of a fresh tile of range r
     int wave;
 
-    __device__ __forceinline__ void init(int wv, int lane, int64_t ldv, int64_t ldn) {
+    __device__ __forceinline__ void init(int wv, int lane, int64_t ldv, int64_t ldn0,
+                                         int64_t ldn1) {
         wave = __builtin_amdgcn_readfirstlane(wv);
 #pragma unroll
         for (int e = 0; e < C::DMA_W; ++e) {
@@ -244,7 +246,8 @@ struct TileDma {
                 const int z = (wave + (e - C::K_DMA_W) * C::NW) * 64 + lane;
                 const int row = z / C::V_SLOTS, slot = (z % C::V_SLOTS) ^ swz<C::V_ROW>(row);
                 off[e] = (uint32_t)(row * ldv * 2 + slot * 16);
-                offf[e - C::K_DMA_W] = (uint32_t)(row * ldn * 2 + slot * 16);
+                offf[0][e - C::K_DMA_W] = (uint32_t)(row * ldn0 * 2 + slot * 16);
+                offf[1][e - C::K_DMA_W] = (uint32_t)(row * ldn1 * 2 + slot * 16);
             }
         }
     }
@@ -263,45 +266,57 @@ struct CopyJob {
     int32x4_t rk, rv;
     uint32_t sk, sv;   // byte offsets added to every lane's address (tile start)
     uint32_t lk, lv;
-    bool vf;           // the V^T tile is a fresh one (row stride f_n, not ldv)
+    int vf;            // the V^T tile's source: 0 buffer, 1 + r fresh range r
 };
 
 struct Ctx {
     const uint16_t *Kh;
     const uint16_t *Vh;
-    const uint16_t *Kf;   // this (batch, head)'s fresh rows (FRESH only)
-    const uint16_t *Vf;
+    const uint16_t *Kf[2];   // this (batch, head)'s fresh rows, per range
+    const uint16_t *Vf[2];
     int64_t ldv;
     int N_kv, t_begin, t_end;
-    int f_t0, f_t1, f_n;
+    int f_t0[2], f_t1[2], f_n[2];
     float c;   // log2(e) * scale
     int tid, ql, g;
 };
 
-// Key tiles [f_t0, f_t1) of a FRESH launch come from the fresh tensors.
-template <bool FRESH>
-__device__ __forceinline__ bool is_fresh(const Ctx &x, int t) {
-    return FRESH && (unsigned)(t - x.f_t0) < (unsigned)(x.f_t1 - x.f_t0);
+// The fresh range (0, 1) key tile t of a launch with NF ranges comes from,
+// or -1 for the buffer.
+template <int NF>
+__device__ __forceinline__ int fresh_range(const Ctx &x, int t) {
+    if (NF >= 1 && (unsigned)(t - x.f_t0[0]) < (unsigned)(x.f_t1[0] - x.f_t0[0])) return 0;
+    if (NF >= 2 && (unsigned)(t - x.f_t0[1]) < (unsigned)(x.f_t1[1] - x.f_t0[1])) return 1;
+    return -1;
 }
 
-template <int D, bool FRESH>
+// Value of range r's field (selects on values: an indexed choice would put
+// the arrays in scratch memory).
+template <typename T>
+__device__ __forceinline__ T of_range(int r, T a0, T a1) {
+    return r == 1 ? a1 : a0;
+}
+
+template <int D, int NF>
 __device__ __forceinline__ CopyJob copy_job(const Ctx &x, int tk, int tv, uint32_t lk,
                                             uint32_t lv) {
     using C = Cfg<D>;
     const int jk = tk * C::BN, jv = tv * C::BN;
     CopyJob j;
-    const bool kf = tk < x.t_end && is_fresh<FRESH>(x, tk);
-    const bool vf = tv < x.t_end && is_fresh<FRESH>(x, tv);
-    if (kf) {
-        const int r = jk - x.f_t0 * C::BN;   // row within the fresh rows
-        j.rk = buffer_rsrc(x.Kf + (int64_t)r * D, (uint32_t)(x.f_n - r) * D * 2);
+    const int kr = tk < x.t_end ? fresh_range<NF>(x, tk) : -1;
+    const int vr = tv < x.t_end ? fresh_range<NF>(x, tv) : -1;
+    if (kr >= 0) {
+        const int r = jk - of_range(kr, x.f_t0[0], x.f_t0[1]) * C::BN;   // row in the range
+        j.rk = buffer_rsrc(of_range(kr, x.Kf[0], x.Kf[1]) + (int64_t)r * D,
+                           (uint32_t)(of_range(kr, x.f_n[0], x.f_n[1]) - r) * D * 2);
     } else {
         j.rk = buffer_rsrc(x.Kh + (int64_t)jk * D,
                            tk < x.t_end ? (uint32_t)(x.N_kv - jk) * D * 2 : 0u);
     }
-    if (vf) {
-        const int r = jv - x.f_t0 * C::BN;
-        j.rv = buffer_rsrc(x.Vf + r, (uint32_t)((int64_t)D * x.f_n - r) * 2);
+    if (vr >= 0) {
+        const int r = jv - of_range(vr, x.f_t0[0], x.f_t0[1]) * C::BN;
+        j.rv = buffer_rsrc(of_range(vr, x.Vf[0], x.Vf[1]) + r,
+                           (uint32_t)((int64_t)D * of_range(vr, x.f_n[0], x.f_n[1]) - r) * 2);
     } else {
         j.rv = buffer_rsrc(x.Vh + jv,
                            tv < x.t_end ? (uint32_t)((int64_t)D * x.ldv - jv) * 2 : 0u);
@@ -310,7 +325,7 @@ __device__ __forceinline__ CopyJob copy_job(const Ctx &x, int tk, int tv, uint32
     j.sv = 0u;
     j.lk = lk;
     j.lv = lv;
-    j.vf = vf;
+    j.vf = vr + 1;
     return j;
 }
 
@@ -321,8 +336,9 @@ __device__ __forceinline__ void issue_copy(const TileDma<D> &dma, const CopyJob 
     // offsets into scratch memory
     uint32_t voff = dma.off[e];
     if (e >= C::K_DMA_W) {
-        const uint32_t fresh_off = dma.offf[e >= C::K_DMA_W ? e - C::K_DMA_W : 0];
-        voff = j.vf ? fresh_off : voff;
+        const int i = e >= C::K_DMA_W ? e - C::K_DMA_W : 0;
+        const uint32_t f0 = dma.offf[0][i], f1 = dma.offf[1][i];
+        voff = j.vf == 0 ? voff : (j.vf == 1 ? f0 : f1);
     }
     lds_dma16(e < C::K_DMA_W ? j.rk : j.rv, voff, e < C::K_DMA_W ? j.sk : j.sv,
               dma.lds_of(e, j.lk, j.lv));
@@ -611,7 +627,7 @@ struct Smem {
 // V(t-2), freed by the previous barrier; it then waits until only its own
 // copies are in flight and publishes K(t+3), V(t+1) with a barrier.  A tile
 // is thus published one step before it is read and copied two steps ahead.
-template <int D, bool RAGGED, bool FRESH>
+template <int D, bool RAGGED, int NF>
 __device__ __forceinline__ void tile_step(int t, const Ctx &x, State<D> &st, Smem<D> &sm,
                                           const TileDma<D> &dma, const OperandOffsets<D> &oo,
                                           f32x16_t (&s_cur)[Cfg<D>::SB],
@@ -634,7 +650,7 @@ __device__ __forceinline__ void tile_step(int t, const Ctx &x, State<D> &st, Sme
                 if (key >= x.N_kv) s_cur[sb][i] = -INFINITY;
             }
     }
-    const CopyJob job = copy_job<D, FRESH>(x, t + 4, t + 2, lds_addr(sm.k[r & 3]),
+    const CopyJob job = copy_job<D, NF>(x, t + 4, t + 2, lds_addr(sm.k[r & 3]),
                                            lds_addr(sm.v[(r + 2) & 3]));
 
     float l_tile = 0.f;
@@ -657,12 +673,13 @@ __device__ __forceinline__ void tile_step(int t, const Ctx &x, State<D> &st, Sme
 // compile time (LDS operand addresses become immediates) and copies of full
 // in-range tiles only: fixed buffer resources over the whole (batch, head)
 // (and over its fresh rows) with the tile start as the scalar offset.
-template <int D, int R4, bool FRESH>
+template <int D, int R4, int NF>
 __device__ __forceinline__ void tile_step_static(int t, const Ctx &x, State<D> &st, Smem<D> &sm,
                                                  const TileDma<D> &dma,
                                                  const OperandOffsets<D> &oo,
                                                  const int32x4_t &rk_all, const int32x4_t &rv_all,
-                                                 const int32x4_t &rk_f, const int32x4_t &rv_f,
+                                                 const int32x4_t (&rk_f)[2],
+                                                 const int32x4_t (&rv_f)[2],
                                                  f32x16_t (&s_cur)[Cfg<D>::SB],
                                                  f32x16_t (&s_next)[Cfg<D>::SB],
                                                  const bf16x8_t (&p_prev)[Cfg<D>::SB][2],
@@ -673,14 +690,16 @@ __device__ __forceinline__ void tile_step_static(int t, const Ctx &x, State<D> &
     constexpr int BN = C::BN;
     constexpr int sk1 = (R4 + 1) & 3, sk2 = (R4 + 2) & 3, sv_prev = (R4 + 3) & 3;
     CopyJob job;
-    const bool kf = is_fresh<FRESH>(x, t + 4), vf = is_fresh<FRESH>(x, t + 2);
-    job.rk = kf ? rk_f : rk_all;
-    job.rv = vf ? rv_f : rv_all;
-    job.sk = (uint32_t)(kf ? t + 4 - x.f_t0 : t + 4) * (uint32_t)(BN * D * 2);
-    job.sv = (uint32_t)(vf ? t + 2 - x.f_t0 : t + 2) * (uint32_t)(BN * 2);
+    const int kr = fresh_range<NF>(x, t + 4), vr = fresh_range<NF>(x, t + 2);
+    job.rk = kr < 0 ? rk_all : of_range(kr, rk_f[0], rk_f[1]);
+    job.rv = vr < 0 ? rv_all : of_range(vr, rv_f[0], rv_f[1]);
+    job.sk = (uint32_t)(t + 4 - (kr < 0 ? 0 : of_range(kr, x.f_t0[0], x.f_t0[1]))) *
+             (uint32_t)(BN * D * 2);
+    job.sv = (uint32_t)(t + 2 - (vr < 0 ? 0 : of_range(vr, x.f_t0[0], x.f_t0[1]))) *
+             (uint32_t)(BN * 2);
     job.lk = lds_addr(sm.k[R4]);
     job.lv = lds_addr(sm.v[(R4 + 2) & 3]);
-    job.vf = vf;
+    job.vf = vr + 1;
     float l_tile = 0.f;
     region<D>(s_next, st.oacc, p_cur, l_tile, s_cur, p_prev, sm.k[sk1], sm.v[sv_prev], sm.k[sk2],
               carry, qreg, x.c, st.m_run, oo, dma, job);
@@ -690,23 +709,22 @@ __device__ __forceinline__ void tile_step_static(int t, const Ctx &x, State<D> &
     __syncthreads();
 }
 
-// Landing workgroups of a FRESH launch: copy the fresh rows into the
-// buffer (K rows row-major, V^T channel rows), as dfp_kv_scatter would.  No
-// attention workgroup of the launch reads those buffer rows.  Four 16-byte
-// vectors per thread per pass, all loads before the stores.
+// Copy fresh range r into the buffer.
 template <int D>
-__device__ __forceinline__ void land_fresh(const Params &p) {
+__device__ __forceinline__ void land_range(const Params &p, int r) {
     // 32-bit vector indices (the launcher checks that they fit)
     constexpr int U = 4;
+    const int f_n = r == 1 ? p.f_n[1] : p.f_n[0];
+    const int f_row0 = r == 1 ? p.f_row0[1] : p.f_row0[0];
     const uint32_t stride = (uint32_t)p.land_wg * Cfg<D>::THREADS;
     const uint32_t first = (uint32_t)((int)blockIdx.x - p.total_wg) * Cfg<D>::THREADS + threadIdx.x;
-    const uint32_t per_bh = (uint32_t)p.f_n * D / 8;   // vectors of one (b,h)'s fresh K rows
-    const uint32_t per_row = (uint32_t)p.f_n / 8;      // vectors of one fresh V^T channel row
+    const uint32_t per_bh = (uint32_t)f_n * D / 8;   // vectors of one (b,h)'s fresh K rows
+    const uint32_t per_row = (uint32_t)f_n / 8;      // vectors of one fresh V^T channel row
     const uint32_t nk = per_bh * p.BH, nv = per_row * p.BH * D;
-    const uint4 *kf = reinterpret_cast<const uint4 *>(p.Kf);
-    const uint4 *vf = reinterpret_cast<const uint4 *>(p.Vtf);
-    uint4 *kw = reinterpret_cast<uint4 *>(p.Kw + (int64_t)p.f_row0 * D);
-    uint4 *vw = reinterpret_cast<uint4 *>(p.Vtw + p.f_row0);
+    const uint4 *kf = reinterpret_cast<const uint4 *>(r == 1 ? p.Kf[1] : p.Kf[0]);
+    const uint4 *vf = reinterpret_cast<const uint4 *>(r == 1 ? p.Vtf[1] : p.Vtf[0]);
+    uint4 *kw = reinterpret_cast<uint4 *>(p.Kw + (int64_t)f_row0 * D);
+    uint4 *vw = reinterpret_cast<uint4 *>(p.Vtw + f_row0);
     const uint32_t kw_bh = (uint32_t)p.N_kv * D / 8;   // buffer vectors per (b,h)
     const uint32_t vw_row = (uint32_t)(p.ldv / 8);      // buffer vectors per V^T row
     for (uint32_t v0 = first; v0 < nk; v0 += U * stride) {
@@ -737,14 +755,24 @@ __device__ __forceinline__ void land_fresh(const Params &p) {
     }
 }
 
-template <int D, bool FRESH>
+// Landing workgroups of a fresh launch: copy every fresh range into the
+// buffer (K rows row-major, V^T channel rows), as dfp_kv_scatter would.  No
+// attention workgroup of the launch reads those buffer rows.  Four 16-byte
+// vectors per thread per pass, all loads before the stores.
+template <int D, int NF>
+__device__ __forceinline__ void land_fresh(const Params &p) {
+#pragma unroll
+    for (int r = 0; r < NF; ++r) land_range<D>(p, r);
+}
+
+template <int D, int NF>
 __global__ __launch_bounds__(Cfg<D>::THREADS, Cfg<D>::WG_PER_CU) void attn_fwd_bf16(Params p) {
     using C = Cfg<D>;
     constexpr int BN = C::BN;
     __shared__ __attribute__((aligned(16))) Smem<D> sm;
     __shared__ int s_last;
-    if (FRESH && (int)blockIdx.x >= p.total_wg) {
-        land_fresh<D>(p);
+    if (NF > 0 && (int)blockIdx.x >= p.total_wg) {
+        land_fresh<D, NF>(p);
         return;
     }
 
@@ -768,11 +796,15 @@ __global__ __launch_bounds__(Cfg<D>::THREADS, Cfg<D>::WG_PER_CU) void attn_fwd_b
     Ctx x;
     x.Kh = p.K + (int64_t)bh * N_kv * D;
     x.Vh = p.Vt + (int64_t)bh * D * p.ldv;
-    x.Kf = FRESH ? p.Kf + (int64_t)bh * p.f_n * D : nullptr;
-    x.Vf = FRESH ? p.Vtf + (int64_t)bh * D * p.f_n : nullptr;
-    x.f_t0 = FRESH ? p.f_t0 : 0;
-    x.f_t1 = FRESH ? p.f_t1 : 0;
-    x.f_n = FRESH ? p.f_n : 0;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const bool on = r < NF;
+        x.Kf[r] = on ? p.Kf[r] + (int64_t)bh * p.f_n[r] * D : nullptr;
+        x.Vf[r] = on ? p.Vtf[r] + (int64_t)bh * D * p.f_n[r] : nullptr;
+        x.f_t0[r] = on ? p.f_t0[r] : 0;
+        x.f_t1[r] = on ? p.f_t1[r] : 0;
+        x.f_n[r] = on ? p.f_n[r] : 0;
+    }
     x.ldv = p.ldv;
     x.N_kv = N_kv;
     const int ntiles = (N_kv + BN - 1) / BN;
@@ -805,17 +837,17 @@ __global__ __launch_bounds__(Cfg<D>::THREADS, Cfg<D>::WG_PER_CU) void attn_fwd_b
     // it; S(t0) and the reference max; the first step's first operands;
     // K(t0+3) and V(t0+1) in flight (the loop's entry state).
     TileDma<D> dma;
-    dma.init(wave, lane, p.ldv, FRESH ? p.f_n : 0);
+    dma.init(wave, lane, p.ldv, x.f_n[0], x.f_n[1]);
     OperandOffsets<D> oo;
     oo.init(ql, g);
     const int t0 = x.t_begin;
     {
         const CopyJob j0 =
-            copy_job<D, FRESH>(x, t0, t0, lds_addr(sm.k[0]), lds_addr(sm.v[0]));
+            copy_job<D, NF>(x, t0, t0, lds_addr(sm.k[0]), lds_addr(sm.v[0]));
         const CopyJob j1 =
-            copy_job<D, FRESH>(x, t0 + 1, t0 + 1, lds_addr(sm.k[1]), lds_addr(sm.v[1]));
+            copy_job<D, NF>(x, t0 + 1, t0 + 1, lds_addr(sm.k[1]), lds_addr(sm.v[1]));
         const CopyJob j2 =
-            copy_job<D, FRESH>(x, t0 + 2, t0 + 2, lds_addr(sm.k[2]), lds_addr(sm.v[2]));
+            copy_job<D, NF>(x, t0 + 2, t0 + 2, lds_addr(sm.k[2]), lds_addr(sm.v[2]));
 #pragma unroll
         for (int e = 0; e < C::DMA_W; ++e) issue_copy<D>(dma, j0, e);   // K(t0), V(t0)
 #pragma unroll
@@ -857,7 +889,7 @@ __global__ __launch_bounds__(Cfg<D>::THREADS, Cfg<D>::WG_PER_CU) void attn_fwd_b
                          step_operand<D>(1, sm.k[1], sm.v[0], oo)};
     {
         const CopyJob j3 =
-            copy_job<D, FRESH>(x, t0 + 3, t0 + 1, lds_addr(sm.k[3]), lds_addr(sm.v[1]));
+            copy_job<D, NF>(x, t0 + 3, t0 + 1, lds_addr(sm.k[3]), lds_addr(sm.v[1]));
 #pragma unroll
         for (int e = 0; e < C::DMA_W; ++e) issue_copy<D>(dma, j3, e);   // K(t0+3), V(t0+1)
     }
@@ -873,29 +905,31 @@ __global__ __launch_bounds__(Cfg<D>::THREADS, Cfg<D>::WG_PER_CU) void attn_fwd_b
         const int n_full = min(x.t_end, N_kv / BN);
         const int32x4_t rk_all = buffer_rsrc(x.Kh, (uint32_t)N_kv * D * 2);
         const int32x4_t rv_all = buffer_rsrc(x.Vh, (uint32_t)((int64_t)D * x.ldv * 2));
-        const int32x4_t rk_f = buffer_rsrc(x.Kf, (uint32_t)x.f_n * D * 2);
-        const int32x4_t rv_f = buffer_rsrc(x.Vf, (uint32_t)((int64_t)D * x.f_n * 2));
+        const int32x4_t rk_f[2] = {buffer_rsrc(x.Kf[0], (uint32_t)x.f_n[0] * D * 2),
+                                   buffer_rsrc(x.Kf[1], (uint32_t)x.f_n[1] * D * 2)};
+        const int32x4_t rv_f[2] = {buffer_rsrc(x.Vf[0], (uint32_t)((int64_t)D * x.f_n[0] * 2)),
+                                   buffer_rsrc(x.Vf[1], (uint32_t)((int64_t)D * x.f_n[1] * 2))};
         for (; t + 8 <= n_full; t += 4) {
-            tile_step_static<D, 0, FRESH>(t, x, st, sm, dma, oo, rk_all, rv_all, rk_f, rv_f, sA,
+            tile_step_static<D, 0, NF>(t, x, st, sm, dma, oo, rk_all, rv_all, rk_f, rv_f, sA,
                                           sB, pB, pA, carry, qreg);
-            tile_step_static<D, 1, FRESH>(t + 1, x, st, sm, dma, oo, rk_all, rv_all, rk_f, rv_f,
+            tile_step_static<D, 1, NF>(t + 1, x, st, sm, dma, oo, rk_all, rv_all, rk_f, rv_f,
                                           sB, sA, pA, pB, carry, qreg);
-            tile_step_static<D, 2, FRESH>(t + 2, x, st, sm, dma, oo, rk_all, rv_all, rk_f, rv_f,
+            tile_step_static<D, 2, NF>(t + 2, x, st, sm, dma, oo, rk_all, rv_all, rk_f, rv_f,
                                           sA, sB, pB, pA, carry, qreg);
-            tile_step_static<D, 3, FRESH>(t + 3, x, st, sm, dma, oo, rk_all, rv_all, rk_f, rv_f,
+            tile_step_static<D, 3, NF>(t + 3, x, st, sm, dma, oo, rk_all, rv_all, rk_f, rv_f,
                                           sB, sA, pA, pB, carry, qreg);
         }
     }
     for (; t + 2 < x.t_end; t += 2) {
-        tile_step<D, false, FRESH>(t, x, st, sm, dma, oo, sA, sB, pB, pA, carry, qreg);
-        tile_step<D, false, FRESH>(t + 1, x, st, sm, dma, oo, sB, sA, pA, pB, carry, qreg);
+        tile_step<D, false, NF>(t, x, st, sm, dma, oo, sA, sB, pB, pA, carry, qreg);
+        tile_step<D, false, NF>(t + 1, x, st, sm, dma, oo, sB, sA, pA, pB, carry, qreg);
     }
     if (t + 1 < x.t_end) {
-        tile_step<D, true, FRESH>(t, x, st, sm, dma, oo, sA, sB, pB, pA, carry, qreg);
-        tile_step<D, true, FRESH>(t + 1, x, st, sm, dma, oo, sB, sA, pA, pB, carry, qreg);
+        tile_step<D, true, NF>(t, x, st, sm, dma, oo, sA, sB, pB, pA, carry, qreg);
+        tile_step<D, true, NF>(t + 1, x, st, sm, dma, oo, sB, sA, pA, pB, carry, qreg);
         pv_tile<D>(st.oacc, pB, sm.v[(t + 1 - t0) & 3], oo);
     } else {
-        tile_step<D, true, FRESH>(t, x, st, sm, dma, oo, sA, sB, pB, pA, carry, qreg);
+        tile_step<D, true, NF>(t, x, st, sm, dma, oo, sA, sB, pB, pA, carry, qreg);
         pv_tile<D>(st.oacc, pA, sm.v[(t - t0) & 3], oo);
     }
     wait_dma_all();   // no copy may outlive the workgroup's LDS
@@ -1095,7 +1129,7 @@ size_t dfp_attn_workspace_bytes(int B, int H, int n_q, int N_kv, int d) {
 
 dfp_status dfp_attn_bf16_launch(void *o, const void *q, const void *k, const void *vt, int BH,
                                 int n_q, int N_kv, int d, float scale, void *ws, size_t ws_bytes,
-                                const dfp_fresh_rows *fresh, hipStream_t stream) {
+                                const dfp_fresh_launch *fresh, hipStream_t stream) {
     // tile copies address one (batch, head)'s K and V^T with 32-bit offsets
     const int64_t ldv = dfp_v_ld(N_kv, DFP_BF16);
     if ((int64_t)N_kv * d * 2 >= (int64_t(1) << 31) || (int64_t)d * ldv * 2 >= (int64_t(1) << 31))
@@ -1115,9 +1149,12 @@ dfp_status dfp_attn_bf16_launch(void *o, const void *q, const void *k, const voi
     }
     if (blocks + land_wg > 0x7FFFFFFF) return DFP_ERR_UNSUPPORTED;
     // landing indexes 16-byte vectors of the fresh tensors with 32 bits
-    if (fresh && ((int64_t)BH * fresh->n * d / 8 >= (int64_t(1) << 31) ||
-                  (int64_t)N_kv * d / 8 >= (int64_t(1) << 31)))
-        return DFP_ERR_UNSUPPORTED;
+    if (fresh) {
+        if ((int64_t)N_kv * d / 8 >= (int64_t(1) << 31)) return DFP_ERR_UNSUPPORTED;
+        for (int r = 0; r < fresh->count; ++r)
+            if ((int64_t)BH * fresh->ranges[r].n * d / 8 >= (int64_t(1) << 31))
+                return DFP_ERR_UNSUPPORTED;
+    }
 
     Params p{};
     p.Q = static_cast<const uint16_t *>(q);
@@ -1134,14 +1171,17 @@ dfp_status dfp_attn_bf16_launch(void *o, const void *q, const void *k, const voi
     p.total_wg = (int)blocks;
     p.BH = BH;
     if (fresh) {
-        p.Kf = static_cast<const uint16_t *>(fresh->k_new);
-        p.Vtf = static_cast<const uint16_t *>(fresh->v_new_t);
+        for (int r = 0; r < fresh->count; ++r) {
+            const dfp_fresh_rows &fr = fresh->ranges[r];
+            p.Kf[r] = static_cast<const uint16_t *>(fr.k);
+            p.Vtf[r] = static_cast<const uint16_t *>(fr.v_t);
+            p.f_row0[r] = fr.row0;
+            p.f_n[r] = fr.n;
+            p.f_t0[r] = fr.row0 / 64;
+            p.f_t1[r] = (fr.row0 + fr.n) / 64;
+        }
         p.Kw = static_cast<uint16_t *>(fresh->k_buf);
         p.Vtw = static_cast<uint16_t *>(fresh->v_buf_t);
-        p.f_row0 = fresh->row0;
-        p.f_n = fresh->n;
-        p.f_t0 = fresh->row0 / 64;
-        p.f_t1 = (fresh->row0 + fresh->n) / 64;
         p.land_wg = land_wg;
     }
     if (pl.splits > 1) {
@@ -1154,16 +1194,19 @@ dfp_status dfp_attn_bf16_launch(void *o, const void *q, const void *k, const voi
         p.part_ml = reinterpret_cast<float *>(w);
     }
     const dim3 grid((unsigned)(blocks + land_wg));
-    if (d == 64 && fresh)
-        hipLaunchKernelGGL((attn_fwd_bf16<64, true>), grid, dim3(Cfg<64>::THREADS), 0, stream, p);
-    else if (d == 64)
-        hipLaunchKernelGGL((attn_fwd_bf16<64, false>), grid, dim3(Cfg<64>::THREADS), 0, stream, p);
-    else if (d == 128 && fresh)
-        hipLaunchKernelGGL((attn_fwd_bf16<128, true>), grid, dim3(Cfg<128>::THREADS), 0, stream,
-                           p);
-    else if (d == 128)
-        hipLaunchKernelGGL((attn_fwd_bf16<128, false>), grid, dim3(Cfg<128>::THREADS), 0, stream,
-                           p);
+    const int nf = fresh ? fresh->count : 0;
+    if (d == 64 && nf == 0)
+        hipLaunchKernelGGL((attn_fwd_bf16<64, 0>), grid, dim3(Cfg<64>::THREADS), 0, stream, p);
+    else if (d == 64 && nf == 1)
+        hipLaunchKernelGGL((attn_fwd_bf16<64, 1>), grid, dim3(Cfg<64>::THREADS), 0, stream, p);
+    else if (d == 64 && nf == 2)
+        hipLaunchKernelGGL((attn_fwd_bf16<64, 2>), grid, dim3(Cfg<64>::THREADS), 0, stream, p);
+    else if (d == 128 && nf == 0)
+        hipLaunchKernelGGL((attn_fwd_bf16<128, 0>), grid, dim3(Cfg<128>::THREADS), 0, stream, p);
+    else if (d == 128 && nf == 1)
+        hipLaunchKernelGGL((attn_fwd_bf16<128, 1>), grid, dim3(Cfg<128>::THREADS), 0, stream, p);
+    else if (d == 128 && nf == 2)
+        hipLaunchKernelGGL((attn_fwd_bf16<128, 2>), grid, dim3(Cfg<128>::THREADS), 0, stream, p);
     else
         return DFP_ERR_UNSUPPORTED;
     return dfp::launch_status();

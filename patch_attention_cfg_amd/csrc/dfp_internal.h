@@ -10,15 +10,15 @@ size_t dfp_attn_workspace_bytes(int B, int H, int n_q, int N_kv, int d);
 
 #include "dfp.h"
 
-// Fresh rows of a dfp_patch_attention_fresh call: key rows [row0, row0+n)
-// (both multiples of 64) are read from k_new / v_new_t, and, when land is
-// set, copied into k_buf / v_buf_t by the same launch.
-struct dfp_fresh_rows {
-    const void *k_new;    // [BH][n][d]
-    const void *v_new_t;  // [BH][d][n]
-    void *k_buf;          // the buffer, written when land is set
+// Fresh rows of a dfp_patch_attention_fresh call: up to two validated,
+// non-overlapping ranges of whole 64-key tiles, read instead of the buffer
+// and, when land is set, copied into k_buf / v_buf_t by the same launch.
+struct dfp_fresh_launch {
+    const dfp_fresh_rows *ranges;
+    int count;
+    void *k_buf;   // the buffer, written when land is set
     void *v_buf_t;
-    int row0, n, land;
+    int land;
 };
 
 // bf16 MFMA attention launcher (attention_bf16.hip); arguments already
@@ -26,4 +26,4 @@ struct dfp_fresh_rows {
 // over the buffer.
 dfp_status dfp_attn_bf16_launch(void *o, const void *q, const void *k, const void *vt, int BH,
                                 int n_q, int N_kv, int d, float scale, void *ws, size_t ws_bytes,
-                                const dfp_fresh_rows *fresh, hipStream_t stream);
+                                const dfp_fresh_launch *fresh, hipStream_t stream);

@@ -27,8 +27,8 @@ SIGNATURES = {
     "dfp_v_ld": (_I64, [_I64, _I]),
     "dfp_kv_scatter": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P]),
     "dfp_patch_attention": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _SZ, _P]),
-    "dfp_patch_attention_fresh": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I,
-                                       _F, _I, _P, _SZ, _P]),
+    "dfp_patch_attention_fresh": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I,
+                                       _P, _SZ, _P]),
     "dfp_cfg_step": (_I, [_P, _P, _P, _I64, _I, _F, _D, _D, _P, _P, _SZ, _P]),
     "dfp_cfg_step_noise": (_I, [_P, _P, _P, _P, _I64, _I, _F, _D, _D, _D, _P, _P, _SZ, _P]),
     "dfp_relmae": (_I, [_P, _P, _I64, _I, _P, _P, _SZ, _P]),
@@ -41,6 +41,14 @@ SIGNATURES = {
     "dfp_ddim_timesteps": (_I, [_I, _I, _P]),
     "dfp_status_string": (ctypes.c_char_p, [_I]),
 }
+
+
+
+class FreshRows(ctypes.Structure):
+    """dfp_fresh_rows: one range of fresh rows (device pointers)."""
+    _fields_ = [("k", ctypes.c_void_p), ("v_t", ctypes.c_void_p), ("row0", ctypes.c_int),
+                ("n", ctypes.c_int)]
+
 
 _lib = None
 
@@ -209,30 +217,31 @@ def patch_attention(o, q, k_buf, v_buf_t, scale: float | None = None, workspace=
     _check(st, "dfp_patch_attention")
 
 
-def patch_attention_fresh(o, q, k_buf, v_buf_t, k_new, v_new_t, row0: int, land: bool = True,
+def patch_attention_fresh(o, q, k_buf, v_buf_t, fresh, land: bool = True,
                           scale: float | None = None, workspace=None, stream=None) -> None:
-    """Attention with the patch's fresh rows [row0, row0+n) read from k_new
-    [B,H,n,d] and v_new_t [B,H,d,n] (channel-major), landing them in the
-    buffer in the same launch when `land`."""
+    """Attention with the rows of each fresh range read from this step's
+    tensors, landing them in the buffer in the same launch when `land`.
+    `fresh` is a list of one or two (k_new [B,H,n,d], v_new_t [B,H,d,n]
+    channel-major, row0) tuples."""
     B, H, n_q, d = q.shape
     N_kv = k_buf.shape[2]
-    n = k_new.shape[2]
     if tuple(o.shape) != tuple(q.shape) or k_buf.shape[:2] != q.shape[:2]:
         raise ValueError("o/q/k_buf shapes disagree")
     if tuple(v_buf_t.shape[:3]) != (B, H, d) or v_buf_t.shape[3] != v_ld(N_kv, _dtype_code(q)):
         raise ValueError("v_buf_t must be [B,H,d,dfp_v_ld(N_kv)]")
-    if tuple(k_new.shape) != (B, H, n, d) or tuple(v_new_t.shape) != (B, H, d, n):
-        raise ValueError("k_new must be [B,H,n,d] and v_new_t [B,H,d,n]")
-    for t in (k_new, v_new_t):
-        if not t.is_contiguous():
-            raise ValueError("fresh tensors must be contiguous")
+    ranges = (FreshRows * max(len(fresh), 1))()
+    for i, (k_new, v_new_t, row0) in enumerate(fresh):
+        n = k_new.shape[2]
+        if tuple(k_new.shape) != (B, H, n, d) or tuple(v_new_t.shape) != (B, H, d, n):
+            raise ValueError("fresh k must be [B,H,n,d] and v_t [B,H,d,n]")
+        ranges[i] = FreshRows(_ptr(k_new).value, _ptr(v_new_t).value, int(row0), n)
     if scale is None:
         scale = 1.0 / float(d) ** 0.5
     ws_ptr = _ptr(workspace) if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     st = lib().dfp_patch_attention_fresh(_ptr(o), _ptr(q), _ptr(k_buf), _ptr(v_buf_t),
-                                         _ptr(k_new), _ptr(v_new_t), B, H, n_q, N_kv, d,
-                                         int(row0), n, 1 if land else 0, float(scale),
+                                         ctypes.cast(ranges, ctypes.c_void_p), len(fresh), B, H,
+                                         n_q, N_kv, d, 1 if land else 0, float(scale),
                                          _dtype_code(q), ws_ptr, ws_bytes, _stream(stream))
     _check(st, "dfp_patch_attention_fresh")
 

@@ -103,34 +103,57 @@ def test_attention_validation(L, args, expect):
 MIS = ctypes.c_void_p(0x100008)   # 8-byte aligned only
 
 
-# (o, q, k_buf, v_buf_t, k_new, v_new_t, B, H, n_q, N_kv, d, row0, n, land, scale, dt)
-@pytest.mark.parametrize("args,expect", [
-    # fresh range outside the buffer, empty or negative
-    ((FAKE,) * 6 + (2, 2, 16, 256, 64, 192, 128, 1, 0.125, dfp.BF16), dfp.ERR_INVALID_ARG),
-    ((FAKE,) * 6 + (2, 2, 16, 256, 64, -64, 128, 1, 0.125, dfp.BF16), dfp.ERR_INVALID_ARG),
-    ((FAKE,) * 6 + (2, 2, 16, 256, 64, 0, 0, 1, 0.125, dfp.BF16), dfp.ERR_INVALID_ARG),
+def _ranges(*spec):
+    """A host dfp_fresh_rows array; spec items are (k, v_t, row0, n)."""
+    arr = (dfp.FreshRows * max(len(spec), 1))()
+    for i, (k, vt, row0, n) in enumerate(spec):
+        arr[i] = dfp.FreshRows(k.value if k else None, vt.value if vt else None, row0, n)
+    return ctypes.cast(arr, ctypes.c_void_p), arr
+
+
+R_OK = (FAKE, FAKE, 64, 128)
+
+
+# (ranges, n_fresh, B, H, n_q, N_kv, d, land, scale, dt, buffers/outputs present)
+@pytest.mark.parametrize("ranges,n_fresh,shape,expect", [
+    # a range outside the buffer, empty or negative
+    ([(FAKE, FAKE, 192, 128)], 1, (2, 2, 16, 256, 64, 1, 0.125, dfp.BF16), dfp.ERR_INVALID_ARG),
+    ([(FAKE, FAKE, -64, 128)], 1, (2, 2, 16, 256, 64, 1, 0.125, dfp.BF16), dfp.ERR_INVALID_ARG),
+    ([(FAKE, FAKE, 0, 0)], 1, (2, 2, 16, 256, 64, 1, 0.125, dfp.BF16), dfp.ERR_INVALID_ARG),
     # not whole 64-key tiles
-    ((FAKE,) * 6 + (2, 2, 16, 256, 64, 32, 128, 1, 0.125, dfp.BF16), dfp.ERR_UNSUPPORTED),
-    ((FAKE,) * 6 + (2, 2, 16, 256, 64, 64, 100, 1, 0.125, dfp.BF16), dfp.ERR_UNSUPPORTED),
+    ([(FAKE, FAKE, 32, 128)], 1, (2, 2, 16, 256, 64, 1, 0.125, dfp.BF16), dfp.ERR_UNSUPPORTED),
+    ([(FAKE, FAKE, 64, 100)], 1, (2, 2, 16, 256, 64, 1, 0.125, dfp.BF16), dfp.ERR_UNSUPPORTED),
     # bf16 only; d 64 or 128
-    ((FAKE,) * 6 + (2, 2, 16, 256, 64, 64, 128, 1, 0.125, dfp.F32), dfp.ERR_UNSUPPORTED),
-    ((FAKE,) * 6 + (2, 2, 16, 256, 96, 64, 128, 1, 0.125, dfp.BF16), dfp.ERR_UNSUPPORTED),
-    # null or misaligned pointers, bad scale, bad sizes
-    ((FAKE, FAKE, FAKE, FAKE, NULL, FAKE, 2, 2, 16, 256, 64, 64, 128, 1, 0.125, dfp.BF16),
+    ([R_OK], 1, (2, 2, 16, 256, 64, 1, 0.125, dfp.F32), dfp.ERR_UNSUPPORTED),
+    ([R_OK], 1, (2, 2, 16, 256, 96, 1, 0.125, dfp.BF16), dfp.ERR_UNSUPPORTED),
+    # range count: none, more than two; overlapping ranges
+    ([], 0, (2, 2, 16, 256, 64, 1, 0.125, dfp.BF16), dfp.ERR_INVALID_ARG),
+    ([R_OK, (FAKE, FAKE, 0, 64), (FAKE, FAKE, 192, 64)], 3, (2, 2, 16, 256, 64, 1, 0.125, dfp.BF16),
+     dfp.ERR_UNSUPPORTED),
+    ([R_OK, (FAKE, FAKE, 128, 128)], 2, (2, 2, 16, 256, 64, 1, 0.125, dfp.BF16),
      dfp.ERR_INVALID_ARG),
-    ((FAKE, FAKE, FAKE, FAKE, FAKE, MIS, 2, 2, 16, 256, 64, 64, 128, 1, 0.125, dfp.BF16),
+    ([(FAKE, FAKE, 128, 128), (FAKE, FAKE, 0, 192)], 2, (2, 2, 16, 256, 64, 1, 0.125, dfp.BF16),
      dfp.ERR_INVALID_ARG),
-    ((NULL, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 2, 16, 256, 64, 64, 128, 1, 0.125, dfp.BF16),
-     dfp.ERR_INVALID_ARG),
-    ((FAKE,) * 6 + (2, 2, 16, 256, 64, 64, 128, 1, float("nan"), dfp.BF16), dfp.ERR_INVALID_ARG),
-    ((FAKE,) * 6 + (0, 2, 16, 256, 64, 64, 128, 1, 0.125, dfp.BF16), dfp.ERR_INVALID_ARG),
-    ((FAKE,) * 6 + (2, 2, -1, 256, 64, 64, 128, 1, 0.125, dfp.BF16), dfp.ERR_INVALID_ARG),
+    # null or misaligned fresh pointers, bad scale, bad sizes
+    ([(NULL, FAKE, 64, 128)], 1, (2, 2, 16, 256, 64, 1, 0.125, dfp.BF16), dfp.ERR_INVALID_ARG),
+    ([(FAKE, MIS, 64, 128)], 1, (2, 2, 16, 256, 64, 1, 0.125, dfp.BF16), dfp.ERR_INVALID_ARG),
+    ([R_OK], 1, (2, 2, 16, 256, 64, 1, float("nan"), dfp.BF16), dfp.ERR_INVALID_ARG),
+    ([R_OK], 1, (0, 2, 16, 256, 64, 1, 0.125, dfp.BF16), dfp.ERR_INVALID_ARG),
+    ([R_OK], 1, (2, 2, -1, 256, 64, 1, 0.125, dfp.BF16), dfp.ERR_INVALID_ARG),
     # no queries and no landing: nothing to do
-    ((NULL, NULL, NULL, NULL, NULL, NULL, 2, 2, 0, 256, 64, 64, 128, 0, 0.125, dfp.BF16),
-     dfp.OK),
+    ([R_OK], 1, (2, 2, 0, 256, 64, 0, 0.125, dfp.BF16), dfp.OK),
 ])
-def test_fresh_attention_validation(L, args, expect):
-    assert L.dfp_patch_attention_fresh(*args, NULL, 0, S0) == expect
+def test_fresh_attention_validation(L, ranges, n_fresh, shape, expect):
+    ptr, keep = _ranges(*ranges)
+    B, H, n_q, N_kv, d, land, scale, dt = shape
+    out = (FAKE, FAKE, FAKE, FAKE) if n_q else (NULL, NULL, FAKE, FAKE)
+    assert L.dfp_patch_attention_fresh(*out, ptr, n_fresh, B, H, n_q, N_kv, d, land, scale, dt,
+                                       NULL, 0, S0) == expect
+
+
+def test_fresh_attention_null_range_array(L):
+    assert L.dfp_patch_attention_fresh(FAKE, FAKE, FAKE, FAKE, NULL, 1, 2, 2, 16, 256, 64, 1,
+                                       0.125, dfp.BF16, NULL, 0, S0) == dfp.ERR_INVALID_ARG
 
 
 def test_cfg_step_validation(L):

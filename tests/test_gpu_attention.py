@@ -137,55 +137,63 @@ def test_forced_split_kv_every_element(monkeypatch, splits, B, H, nq, N, d):
 
 
 @pytest.mark.parametrize("land", [False, True])
-@pytest.mark.parametrize("B,H,nq,N,d,row0,n,splits", [
-    (1, 2, 200, 1000, 64, 256, 512, 0),    # ragged last tile after the fresh rows
-    (1, 2, 200, 1000, 64, 256, 512, 3),    # split key ranges that start inside them
-    (2, 1, 130, 1024, 64, 0, 256, 0),      # fresh rows first
-    (2, 1, 130, 1024, 64, 768, 256, 5),    # fresh rows last
-    (1, 1, 64, 64, 64, 0, 64, 0),          # the whole buffer is one fresh tile
-    (1, 2, 300, 1024, 64, 64, 768, 0),     # long fresh range through the four-step loop
-    (1, 2, 300, 700, 128, 128, 384, 0),    # d=128
-    (1, 2, 300, 700, 128, 128, 384, 2),
+@pytest.mark.parametrize("B,H,nq,N,d,ranges,splits", [
+    (1, 2, 200, 1000, 64, [(256, 512)], 0),    # ragged last tile after the fresh rows
+    (1, 2, 200, 1000, 64, [(256, 512)], 3),    # split key ranges that start inside them
+    (2, 1, 130, 1024, 64, [(0, 256)], 0),      # fresh rows first
+    (2, 1, 130, 1024, 64, [(768, 256)], 5),    # fresh rows last
+    (1, 1, 64, 64, 64, [(0, 64)], 0),          # the whole buffer is one fresh tile
+    (1, 2, 300, 1024, 64, [(64, 768)], 0),     # long fresh range through the four-step loop
+    (1, 2, 300, 700, 128, [(128, 384)], 0),    # d=128
+    (1, 2, 300, 700, 128, [(128, 384)], 2),
+    (1, 2, 200, 1344, 64, [(0, 256), (768, 512)], 0),    # text-like rows + a patch
+    (1, 2, 200, 1344, 64, [(768, 512), (0, 256)], 3),    # the same, listed the other way
+    (1, 2, 200, 1344, 64, [(0, 256), (256, 512)], 0),    # adjacent ranges
+    (1, 2, 300, 1300, 128, [(0, 256), (768, 256)], 2),   # d=128, ragged last tile
 ])
-def test_fresh_rows_every_element(monkeypatch, B, H, nq, N, d, row0, n, splits, land):
-    """dfp_patch_attention_fresh: the buffer's own rows in the fresh range
-    hold NaN and must never be read; the output matches the oracle over the
-    effective K/V and is bitwise the output of scatter + dfp_patch_attention;
-    with land the buffer ends up exactly as dfp_kv_scatter leaves it, without
-    it untouched."""
+def test_fresh_rows_every_element(monkeypatch, B, H, nq, N, d, ranges, splits, land):
+    """dfp_patch_attention_fresh with one or two fresh ranges: the buffer's
+    own rows there hold NaN and must never be read; the output matches the
+    oracle over the effective K/V and is bitwise the output of scatter +
+    dfp_patch_attention; with land the buffer ends up exactly as
+    dfp_kv_scatter leaves it, without it untouched."""
     G.require_gpu()
     G.announce(f"attention fresh rows land={land} B{B} H{H} nq{nq} N{N} d{d} "
-               f"row0={row0} n={n} splits={splits}")
+               f"ranges={ranges} splits={splits}")
     if splits:
         monkeypatch.setenv("DFP_ATTN_SPLITS", str(splits))
     torch = G.torch_mod()
-    q, k_st, v_st = inputs.random_attention_arrays(B, H, nq, N, d, seed=row0 + n + d)
-    _, k_new, v_new = inputs.random_attention_arrays(B, H, 1, n, d, seed=row0 + n + d + 1)
+    seed = N + d + sum(r0 + n for r0, n in ranges)
+    q, k_st, v_st = inputs.random_attention_arrays(B, H, nq, N, d, seed=seed)
     k_buf, v_buf = dfp.alloc_kv_buffer(B, H, N, d, torch.bfloat16)
     dfp.kv_scatter(k_buf, v_buf, G.up(k_st, "bf16"), G.up(v_st, "bf16"), 0)
-    k_buf[:, :, row0:row0 + n] = float("nan")
-    v_buf[:, :, :, row0:row0 + n] = float("nan")
-    kd = G.up(k_new, "bf16")
-    vtd = G.up(np.swapaxes(v_new, -1, -2), "bf16")
+    k_eff, v_eff = k_st.copy(), v_st.copy()
+    fresh, dev = [], []
+    for i, (row0, n) in enumerate(ranges):
+        _, k_new, v_new = inputs.random_attention_arrays(B, H, 1, n, d, seed=seed + 1 + i)
+        k_buf[:, :, row0:row0 + n] = float("nan")
+        v_buf[:, :, :, row0:row0 + n] = float("nan")
+        kd, vtd = G.up(k_new, "bf16"), G.up(np.swapaxes(v_new, -1, -2), "bf16")
+        fresh.append((kd, vtd, row0))
+        k_eff[:, :, row0:row0 + n], v_eff[:, :, row0:row0 + n] = k_new, v_new
     qd = G.up(q, "bf16")
     o = torch.empty_like(qd)
     ws = dfp.attention_workspace(B, H, nq, N, d)
-    dfp.patch_attention_fresh(o, qd, k_buf, v_buf, kd, vtd, row0, land, None, ws)
+    dfp.patch_attention_fresh(o, qd, k_buf, v_buf, fresh, land, None, ws)
     torch.cuda.synchronize()
     got = G.down(o)
     if ws is not None:
         G.assert_counters_zero(ws, B * H, nq, d)
-    k_eff, v_eff = k_st.copy(), v_st.copy()
-    k_eff[:, :, row0:row0 + n], v_eff[:, :, row0:row0 + n] = k_new, v_new
     _check(got, oracle.attention(q, k_eff, v_eff, 1.0 / d ** 0.5), "bf16", "fresh")
     if land:
         np.testing.assert_array_equal(G.down(k_buf), k_eff)
         np.testing.assert_array_equal(G.v_buffer_to_rows(v_buf, N), v_eff)
     else:
-        assert np.isnan(G.down(k_buf)[:, :, row0:row0 + n]).all()
-        assert np.isnan(G.down(v_buf)[:, :, :, row0:row0 + n]).all()
-        k_buf[:, :, row0:row0 + n] = kd            # the scatter's result, for the reference
-        v_buf[:, :, :, row0:row0 + n] = vtd
+        for (row0, n), (kd, vtd, _) in zip(ranges, fresh):
+            assert np.isnan(G.down(k_buf)[:, :, row0:row0 + n]).all()
+            assert np.isnan(G.down(v_buf)[:, :, :, row0:row0 + n]).all()
+            k_buf[:, :, row0:row0 + n] = kd        # the scatter's result, for the reference
+            v_buf[:, :, :, row0:row0 + n] = vtd
     o2 = torch.empty_like(qd)
     dfp.patch_attention(o2, qd, k_buf, v_buf, None, ws)   # same plan over the landed buffer
     torch.cuda.synchronize()

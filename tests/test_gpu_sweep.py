@@ -29,11 +29,11 @@ F32_MAX_ABS = 1e-4
                                               ("dit1024", 2, False), ("sdxl2048", 1, False),
                                               ("sdxl1024-64x64", None, True),
                                               ("sdxl1024-32x32", None, True),
-                                              ("sdxl2048", 1, True)])
+                                              ("dit1024", 2, True), ("sdxl2048", 1, True)])
 def test_patch_sweep_every_patch(name, heads, fresh):
     """With `fresh` each patch runs dfp_patch_attention_fresh (reading its own
-    rows from the fresh tensors and landing them) instead of scatter +
-    dfp_patch_attention."""
+    rows, and a DiT's text rows, from the fresh tensors and landing them)
+    instead of scatter + dfp_patch_attention."""
     G.require_gpu()
     torch = G.torch_mod()
     level = inputs.LEVELS[name]
@@ -50,13 +50,17 @@ def test_patch_sweep_every_patch(name, heads, fresh):
     want = oracle.patch_sweep(x.q[sl], x.k_stale[sl], x.v_stale[sl], x.k_fresh[sl],
                               x.v_fresh[sl], level.P, 1.0 / d ** 0.5, level.n_text)
     ws = dfp.attention_workspace(B, H, n, N, d)
+    text = None
+    if fresh and level.n_text:   # the text rows are fresh in every call
+        kt, vt = x.text_rows()
+        text = (G.up(kt, kind), G.up(np.swapaxes(vt, -1, -2), kind), 0)
     for m in range(level.P):
         kf, vf = x.fresh_rows(m)
         q = G.up(x.q_patch(m), kind)
         o = torch.empty_like(q)
         if fresh:
-            dfp.patch_attention_fresh(o, q, k_buf, v_buf, G.up(kf, kind),
-                                      G.up(np.swapaxes(vf, -1, -2), kind), level.row0(m),
+            ranges = [(G.up(kf, kind), G.up(np.swapaxes(vf, -1, -2), kind), level.row0(m))]
+            dfp.patch_attention_fresh(o, q, k_buf, v_buf, ([text] if text else []) + ranges,
                                       True, 1.0 / d ** 0.5, ws)
         else:
             dfp.kv_scatter(k_buf, v_buf, G.up(kf, kind), G.up(vf, kind), level.row0(m))
