@@ -1,0 +1,85 @@
+"""The library's calls captured in a HIP graph, as bench.py times them:
+fused attention with landing (split plan, so the workspace counters are
+used) followed by the fused guidance step, replayed several times with eager
+library calls between the replays.  Every replay must match the same calls
+run eagerly, bit for bit (both are deterministic), and leave the counters at
+zero."""
+import numpy as np
+import pytest
+
+from patch_attention_cfg_amd import dfp, inputs
+from tests import gpu_helpers as G
+
+pytestmark = pytest.mark.gpu
+
+
+def test_graph_replays_match_eager(monkeypatch):
+    G.require_gpu()
+    G.announce("graph replay: fused attention (3-way split) + fused cfg step, 4 replays")
+    monkeypatch.setenv("DFP_ATTN_SPLITS", "3")
+    torch = G.torch_mod()
+    B, H, nq, N, d, row0, n = 2, 2, 256, 1024, 64, 256, 256
+    q, k_st, v_st = inputs.random_attention_arrays(B, H, nq, N, d, seed=41)
+    _, k_new, v_new = inputs.random_attention_arrays(B, H, 1, n, d, seed=42)
+    k_buf, v_buf = dfp.alloc_kv_buffer(B, H, N, d, torch.bfloat16)
+    dfp.kv_scatter(k_buf, v_buf, G.up(k_st, "bf16"), G.up(v_st, "bf16"), 0)
+    fresh = [(G.up(k_new, "bf16"), G.up(np.swapaxes(v_new, -1, -2), "bf16"), row0)]
+    qd = G.up(q, "bf16")
+    ws = dfp.attention_workspace(B, H, nq, N, d)
+    assert ws is not None
+
+    rng = np.random.Generator(np.random.PCG64(43))
+    nl = 4 * 32 * 32
+    x0 = rng.standard_normal((1, nl), dtype=np.float32)
+    g_c = torch.from_numpy(rng.standard_normal((1, nl), dtype=np.float32)).cuda()
+    g_u = torch.from_numpy(rng.standard_normal((1, nl), dtype=np.float32)).cuda()
+    c_x, c_e = dfp.ddim_coeffs(0.5, 0.6)
+    cws = dfp.cfg_workspace(nl, 1)
+
+    def step(o, x, r):
+        dfp.patch_attention_fresh(o, qd, k_buf, v_buf, fresh, True, None, ws)
+        dfp.cfg_step(x, g_c, g_u, 7.5, c_x, c_e, r, cws)
+
+    # eager reference: the attention output and the latent after 1..4 steps
+    o_e = torch.empty_like(qd)
+    x_e = torch.from_numpy(x0.copy()).cuda()
+    r_e = torch.empty(1, dtype=torch.float32, device="cuda")
+    want_x, want_r = [], []
+    for _ in range(4):
+        step(o_e, x_e, r_e)
+        torch.cuda.synchronize()
+        want_x.append(x_e.cpu().numpy().copy())
+        want_r.append(r_e.cpu().numpy().copy())
+    want_o = G.down(o_e)
+
+    o_g = torch.empty_like(qd)
+    x_g = torch.from_numpy(x0.copy()).cuda()
+    r_g = torch.empty(1, dtype=torch.float32, device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):            # warm-up outside capture, then restore x
+        step(o_g, x_g, r_g)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    x_g.copy_(torch.from_numpy(x0))
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(o_g, x_g, r_g)
+    torch.cuda.synchronize()
+    x_g.copy_(torch.from_numpy(x0))
+    torch.cuda.synchronize()
+
+    other = torch.empty_like(qd)
+    for i in range(4):
+        o_g.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(G.down(o_g), want_o, err_msg=f"replay {i} attention")
+        np.testing.assert_array_equal(x_g.cpu().numpy(), want_x[i], err_msg=f"replay {i} latent")
+        np.testing.assert_array_equal(r_g.cpu().numpy(), want_r[i], err_msg=f"replay {i} rel-MAE")
+        G.assert_counters_zero(ws, B * H, nq, d)
+        assert int(cws[:4].view(torch.int32)[0].item()) == 0
+        # eager work on the same workspace between replays
+        dfp.patch_attention(other, qd, k_buf, v_buf, None, ws)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(G.down(other), want_o)
