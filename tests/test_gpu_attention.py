@@ -200,6 +200,33 @@ def test_fresh_rows_every_element(monkeypatch, B, H, nq, N, d, ranges, splits, l
     np.testing.assert_array_equal(G.down(o2), got)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_fresh_landing_only(d):
+    """n_q == 0 with land: the launch is landing workgroups only; the buffer
+    ends up bit-exact as dfp_kv_scatter of both ranges leaves it, rows and
+    padding columns outside the ranges untouched."""
+    G.require_gpu()
+    G.announce(f"attention fresh landing only d={d}")
+    torch = G.torch_mod()
+    B, H, N = 2, 3, 1000
+    _, k_st, v_st = inputs.random_attention_arrays(B, H, 1, N, d, seed=70 + d)
+    k_buf, v_buf = dfp.alloc_kv_buffer(B, H, N, d, torch.bfloat16)
+    v_buf.fill_(float("nan"))
+    dfp.kv_scatter(k_buf, v_buf, G.up(k_st, "bf16"), G.up(v_st, "bf16"), 0)
+    k_eff, v_eff = k_st.copy(), v_st.copy()
+    fresh = []
+    for i, (row0, n) in enumerate([(64, 128), (512, 448)]):
+        _, k_new, v_new = inputs.random_attention_arrays(B, H, 1, n, d, seed=80 + d + i)
+        fresh.append((G.up(k_new, "bf16"), G.up(np.swapaxes(v_new, -1, -2), "bf16"), row0))
+        k_eff[:, :, row0:row0 + n], v_eff[:, :, row0:row0 + n] = k_new, v_new
+    q = torch.empty((B, H, 0, d), dtype=torch.bfloat16, device="cuda")
+    dfp.patch_attention_fresh(q, q, k_buf, v_buf, fresh, True)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(G.down(k_buf), k_eff)
+    np.testing.assert_array_equal(G.v_buffer_to_rows(v_buf, N), v_eff)
+    assert torch.isnan(v_buf[..., N:]).all()   # padding columns untouched
+
+
 def test_constant_values_and_single_key_properties():
     G.require_gpu()
     G.announce("attention properties (V=1, N_kv=1) at the SDXL-1024 64x64 shape")
