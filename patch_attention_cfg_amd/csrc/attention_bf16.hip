@@ -58,6 +58,12 @@
 //     partials in split order, so the result is bitwise reproducible.
 //   * Workgroups are mapped to XCDs so that each XCD streams a contiguous
 //     range of (batch, head) buffers, keeping their K/V in that XCD's L2.
+//   * Fresh rows (the NF = 1, 2 instantiations): key tiles of up to two
+//     ranges -- the patch's own rows, a DiT's text rows -- are copied from
+//     this step's K and channel-major V instead of the buffer, and extra
+//     workgroups after the attention ones land those rows in the buffer
+//     meanwhile.  No attention workgroup reads the buffer rows being landed,
+//     so the landing needs no ordering inside the launch.
 #include <cmath>
 #include <cstdlib>
 
