@@ -10,9 +10,10 @@ w=7.5):
       launch (dfp_patch_attention_fresh)
   the same for the 32x32 level
   fused CFG + DDIM update + rel-MAE on the latent.
-A level whose patch rows are not whole 64-key tiles (SDXL-3840), or with
-d = 128 (DiT), lands its K/V with dfp_kv_scatter and then runs
-dfp_patch_attention; `--no-fresh` times that path everywhere.
+A DiT level passes its always-fresh text rows as a second fresh range.  A
+level whose patch rows are not whole 64-key tiles (SDXL-3840) lands its K/V
+with dfp_kv_scatter and then runs dfp_patch_attention; `--no-fresh` times
+that path everywhere.
 All inputs are seeded synthetic arrays resident in HBM before timing starts.
 The timed steps replay one HIP graph of the step (falls back to eager
 launches if capture is refused).  Per-kernel durations for the roofline come
@@ -103,12 +104,8 @@ class Level:
 
         self.k_buf, self.v_buf = dfp.alloc_kv_buffer(level.B, level.H, level.N_kv, level.d, bf)
         dfp.kv_scatter(self.k_buf, self.v_buf, up(x.k_stale), up(x.v_stale), 0)
-        # fused path: every fresh range (the patch, a DiT's text rows) whole 64-key
-        # tiles, and d = 64: at d = 128 the fused kernel's extra per-range copy
-        # offsets spill from the full register file inside the main loop and cost
-        # more than the separate landing kernel saves
-        self.fused = (fresh and level.d == 64 and level.n % 64 == 0 and
-                      level.n_text % 64 == 0 and
+        # fused path: every fresh range (the patch, a DiT's text rows) whole 64-key tiles
+        self.fused = (fresh and level.n % 64 == 0 and level.n_text % 64 == 0 and
                       all(level.row0(p) % 64 == 0 for p in self.patches))
         self.fresh, self.q, self.o = [], [], []
         for p in self.patches:

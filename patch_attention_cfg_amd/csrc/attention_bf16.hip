@@ -236,7 +236,12 @@ template <int D>
 struct TileDma {
     using C = Cfg<D>;
     uint32_t off[C::DMA_W];   // byte offset of this lane's chunk within a tile
-    uint32_t offf[2][C::DMA_W - C::K_DMA_W];   // V^T chunks of a fresh tile of range r
+    // A fresh range r stores V^T rows with pitch ldn_r instead of ldv: V^T
+    // copy e of a fresh tile reads at off[e] + row * dpitch[r], row =
+    // vrow0(e) + lane / 8, so one lane term and one scalar term per range
+    // (no per-copy offsets to keep live).
+    uint32_t lane_dp[2];      // (lane / 8) * dpitch[r]
+    uint32_t dpitch[2];       // (ldn_r - ldv) * 2 bytes, modulo 2^32 (uniform)
     int wave;
 
     __device__ __forceinline__ void init(int wv, int lane, int64_t ldv, int64_t ldn0,
@@ -252,10 +257,18 @@ struct TileDma {
                 const int z = (wave + (e - C::K_DMA_W) * C::NW) * 64 + lane;
                 const int row = z / C::V_SLOTS, slot = (z % C::V_SLOTS) ^ swz<C::V_ROW>(row);
                 off[e] = (uint32_t)(row * ldv * 2 + slot * 16);
-                offf[0][e - C::K_DMA_W] = (uint32_t)(row * ldn0 * 2 + slot * 16);
-                offf[1][e - C::K_DMA_W] = (uint32_t)(row * ldn1 * 2 + slot * 16);
             }
         }
+        static_assert(C::V_SLOTS == 8, "a V^T copy covers 8 channel rows of 64 lanes");
+        dpitch[0] = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)((ldn0 - ldv) * 2));
+        dpitch[1] = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)((ldn1 - ldv) * 2));
+        lane_dp[0] = (uint32_t)(lane >> 3) * dpitch[0];
+        lane_dp[1] = (uint32_t)(lane >> 3) * dpitch[1];
+    }
+
+    // First V^T row of copy e (e >= K_DMA_W) of this wavefront (uniform).
+    __device__ __forceinline__ uint32_t vrow0(int e) const {
+        return (uint32_t)(wave + (e - C::K_DMA_W) * C::NW) * 8u;
     }
 
     // LDS byte address written by copy e of this wavefront.
@@ -272,7 +285,8 @@ struct CopyJob {
     int32x4_t rk, rv;
     uint32_t sk, sv;   // byte offsets added to every lane's address (tile start)
     uint32_t lk, lv;
-    int vf;            // the V^T tile's source: 0 buffer, 1 + r fresh range r
+    uint32_t vlane;    // fresh V^T tile: this lane's row-pitch term (else 0)
+    uint32_t vpitch;   // fresh V^T tile: pitch difference per row (else 0)
 };
 
 struct Ctx {
@@ -304,8 +318,8 @@ __device__ __forceinline__ T of_range(int r, T a0, T a1) {
 }
 
 template <int D, int NF>
-__device__ __forceinline__ CopyJob copy_job(const Ctx &x, int tk, int tv, uint32_t lk,
-                                            uint32_t lv) {
+__device__ __forceinline__ CopyJob copy_job(const Ctx &x, const TileDma<D> &dma, int tk, int tv,
+                                            uint32_t lk, uint32_t lv) {
     using C = Cfg<D>;
     const int jk = tk * C::BN, jv = tv * C::BN;
     CopyJob j;
@@ -331,7 +345,8 @@ __device__ __forceinline__ CopyJob copy_job(const Ctx &x, int tk, int tv, uint32
     j.sv = 0u;
     j.lk = lk;
     j.lv = lv;
-    j.vf = vr + 1;
+    j.vlane = vr < 0 ? 0u : of_range(vr, dma.lane_dp[0], dma.lane_dp[1]);
+    j.vpitch = vr < 0 ? 0u : of_range(vr, dma.dpitch[0], dma.dpitch[1]);
     return j;
 }
 
@@ -341,11 +356,7 @@ __device__ __forceinline__ void issue_copy(const TileDma<D> &dma, const CopyJob 
     // select values, not arrays: a selected array address would force the
     // offsets into scratch memory
     uint32_t voff = dma.off[e];
-    if (e >= C::K_DMA_W) {
-        const int i = e >= C::K_DMA_W ? e - C::K_DMA_W : 0;
-        const uint32_t f0 = dma.offf[0][i], f1 = dma.offf[1][i];
-        voff = j.vf == 0 ? voff : (j.vf == 1 ? f0 : f1);
-    }
+    if (e >= C::K_DMA_W) voff += j.vlane + dma.vrow0(e) * j.vpitch;   // 0 for buffer tiles
     lds_dma16(e < C::K_DMA_W ? j.rk : j.rv, voff, e < C::K_DMA_W ? j.sk : j.sv,
               dma.lds_of(e, j.lk, j.lv));
 }
@@ -656,7 +667,7 @@ __device__ __forceinline__ void tile_step(int t, const Ctx &x, State<D> &st, Sme
                 if (key >= x.N_kv) s_cur[sb][i] = -INFINITY;
             }
     }
-    const CopyJob job = copy_job<D, NF>(x, t + 4, t + 2, lds_addr(sm.k[r & 3]),
+    const CopyJob job = copy_job<D, NF>(x, dma, t + 4, t + 2, lds_addr(sm.k[r & 3]),
                                            lds_addr(sm.v[(r + 2) & 3]));
 
     float l_tile = 0.f;
@@ -705,7 +716,8 @@ __device__ __forceinline__ void tile_step_static(int t, const Ctx &x, State<D> &
              (uint32_t)(BN * 2);
     job.lk = lds_addr(sm.k[R4]);
     job.lv = lds_addr(sm.v[(R4 + 2) & 3]);
-    job.vf = vr + 1;
+    job.vlane = vr < 0 ? 0u : of_range(vr, dma.lane_dp[0], dma.lane_dp[1]);
+    job.vpitch = vr < 0 ? 0u : of_range(vr, dma.dpitch[0], dma.dpitch[1]);
     float l_tile = 0.f;
     region<D>(s_next, st.oacc, p_cur, l_tile, s_cur, p_prev, sm.k[sk1], sm.v[sv_prev], sm.k[sk2],
               carry, qreg, x.c, st.m_run, oo, dma, job);
@@ -849,11 +861,11 @@ __global__ __launch_bounds__(Cfg<D>::THREADS, Cfg<D>::WG_PER_CU) void attn_fwd_b
     const int t0 = x.t_begin;
     {
         const CopyJob j0 =
-            copy_job<D, NF>(x, t0, t0, lds_addr(sm.k[0]), lds_addr(sm.v[0]));
+            copy_job<D, NF>(x, dma, t0, t0, lds_addr(sm.k[0]), lds_addr(sm.v[0]));
         const CopyJob j1 =
-            copy_job<D, NF>(x, t0 + 1, t0 + 1, lds_addr(sm.k[1]), lds_addr(sm.v[1]));
+            copy_job<D, NF>(x, dma, t0 + 1, t0 + 1, lds_addr(sm.k[1]), lds_addr(sm.v[1]));
         const CopyJob j2 =
-            copy_job<D, NF>(x, t0 + 2, t0 + 2, lds_addr(sm.k[2]), lds_addr(sm.v[2]));
+            copy_job<D, NF>(x, dma, t0 + 2, t0 + 2, lds_addr(sm.k[2]), lds_addr(sm.v[2]));
 #pragma unroll
         for (int e = 0; e < C::DMA_W; ++e) issue_copy<D>(dma, j0, e);   // K(t0), V(t0)
 #pragma unroll
@@ -895,7 +907,7 @@ __global__ __launch_bounds__(Cfg<D>::THREADS, Cfg<D>::WG_PER_CU) void attn_fwd_b
                          step_operand<D>(1, sm.k[1], sm.v[0], oo)};
     {
         const CopyJob j3 =
-            copy_job<D, NF>(x, t0 + 3, t0 + 1, lds_addr(sm.k[3]), lds_addr(sm.v[1]));
+            copy_job<D, NF>(x, dma, t0 + 3, t0 + 1, lds_addr(sm.k[3]), lds_addr(sm.v[1]));
 #pragma unroll
         for (int e = 0; e < C::DMA_W; ++e) issue_copy<D>(dma, j3, e);   // K(t0+3), V(t0+1)
     }
