@@ -236,10 +236,13 @@ template <int D>
 struct TileDma {
     using C = Cfg<D>;
     uint32_t off[C::DMA_W];   // byte offset of this lane's chunk within a tile
-    // A fresh range r stores V^T rows with pitch ldn_r instead of ldv: V^T
-    // copy e of a fresh tile reads at off[e] + row * dpitch[r], row =
-    // vrow0(e) + lane / 8, so one lane term and one scalar term per range
-    // (no per-copy offsets to keep live).
+    // A fresh range r stores V^T rows with pitch ldn_r instead of ldv.  At
+    // d=64 (registers to spare) each V^T copy keeps its fresh offset per
+    // range (offf); at d=128, whose plain kernel already fills the register
+    // file, copy e of a fresh tile reads at off[e] + row * dpitch[r] with
+    // row = vrow0(e) + lane / 8: one lane term and one scalar per range.
+    static constexpr bool kPerCopyFresh = D == 64;
+    uint32_t offf[2][C::DMA_W - C::K_DMA_W];
     uint32_t lane_dp[2];      // (lane / 8) * dpitch[r]
     uint32_t dpitch[2];       // (ldn_r - ldv) * 2 bytes, modulo 2^32 (uniform)
     int wave;
@@ -257,6 +260,8 @@ struct TileDma {
                 const int z = (wave + (e - C::K_DMA_W) * C::NW) * 64 + lane;
                 const int row = z / C::V_SLOTS, slot = (z % C::V_SLOTS) ^ swz<C::V_ROW>(row);
                 off[e] = (uint32_t)(row * ldv * 2 + slot * 16);
+                offf[0][e - C::K_DMA_W] = (uint32_t)(row * ldn0 * 2 + slot * 16);
+                offf[1][e - C::K_DMA_W] = (uint32_t)(row * ldn1 * 2 + slot * 16);
             }
         }
         static_assert(C::V_SLOTS == 8, "a V^T copy covers 8 channel rows of 64 lanes");
@@ -285,8 +290,9 @@ struct CopyJob {
     int32x4_t rk, rv;
     uint32_t sk, sv;   // byte offsets added to every lane's address (tile start)
     uint32_t lk, lv;
-    uint32_t vlane;    // fresh V^T tile: this lane's row-pitch term (else 0)
-    uint32_t vpitch;   // fresh V^T tile: pitch difference per row (else 0)
+    int vsel;          // the V^T tile's source: 0 buffer, 1 + r fresh range r
+    uint32_t vlane;    // fresh V^T tile, d=128: this lane's row-pitch term (else 0)
+    uint32_t vpitch;   // fresh V^T tile, d=128: pitch difference per row (else 0)
 };
 
 struct Ctx {
@@ -345,6 +351,7 @@ __device__ __forceinline__ CopyJob copy_job(const Ctx &x, const TileDma<D> &dma,
     j.sv = 0u;
     j.lk = lk;
     j.lv = lv;
+    j.vsel = vr + 1;
     j.vlane = vr < 0 ? 0u : of_range(vr, dma.lane_dp[0], dma.lane_dp[1]);
     j.vpitch = vr < 0 ? 0u : of_range(vr, dma.dpitch[0], dma.dpitch[1]);
     return j;
@@ -356,7 +363,15 @@ __device__ __forceinline__ void issue_copy(const TileDma<D> &dma, const CopyJob 
     // select values, not arrays: a selected array address would force the
     // offsets into scratch memory
     uint32_t voff = dma.off[e];
-    if (e >= C::K_DMA_W) voff += j.vlane + dma.vrow0(e) * j.vpitch;   // 0 for buffer tiles
+    if (e >= C::K_DMA_W) {
+        if constexpr (TileDma<D>::kPerCopyFresh) {
+            const int i = e >= C::K_DMA_W ? e - C::K_DMA_W : 0;
+            const uint32_t f0 = dma.offf[0][i], f1 = dma.offf[1][i];
+            voff = j.vsel == 0 ? voff : (j.vsel == 1 ? f0 : f1);
+        } else {
+            voff += j.vlane + dma.vrow0(e) * j.vpitch;   // 0 for buffer tiles
+        }
+    }
     lds_dma16(e < C::K_DMA_W ? j.rk : j.rv, voff, e < C::K_DMA_W ? j.sk : j.sv,
               dma.lds_of(e, j.lk, j.lv));
 }
@@ -716,6 +731,7 @@ __device__ __forceinline__ void tile_step_static(int t, const Ctx &x, State<D> &
              (uint32_t)(BN * 2);
     job.lk = lds_addr(sm.k[R4]);
     job.lv = lds_addr(sm.v[(R4 + 2) & 3]);
+    job.vsel = vr + 1;
     job.vlane = vr < 0 ? 0u : of_range(vr, dma.lane_dp[0], dma.lane_dp[1]);
     job.vpitch = vr < 0 ? 0u : of_range(vr, dma.dpitch[0], dma.dpitch[1]);
     float l_tile = 0.f;
