@@ -136,7 +136,9 @@ dfp_status dfp_kv_scatter(void *k_buf, void *v_buf_t, const void *k_new,
  *           arrival counters that must be zero before the first call (e.g.
  *           allocate it zeroed); every call leaves them zero again.  The
  *           split partials are merged in a fixed order, so results are
- *           bitwise reproducible for a given shape.
+ *           bitwise reproducible for a given shape.  Calls that share a
+ *           workspace must not run concurrently (one stream, or streams
+ *           ordered by events).
  * d must be 64 or 128.  n_q == 0 is a no-op (pointers may then be NULL).
  * o must not alias the inputs.
  * Errors: INVALID_ARG for null pointers, non-positive B/H/N_kv, negative n_q,
@@ -212,8 +214,10 @@ dfp_status dfp_patch_attention_fresh(void *o, const void *q, void *k_buf,
  *              (4 bytes each, padded to a multiple of 256 bytes) that must
  *              be zero before the first call (e.g. allocate it zeroed);
  *              every call leaves them zero again.  The rest holds
- *              per-workgroup partial sums.  The cross-workgroup sum runs in a fixed order
- *              in double precision, so results are bitwise reproducible.
+ *              per-workgroup partial sums.  Calls that share a workspace
+ *              must not run concurrently.  The cross-workgroup sum runs
+ *              in a fixed order in double precision, so results are
+ *              bitwise reproducible.
  * Degenerate rel-MAE follows IEEE division (0/0 = NaN, x/0 = +Inf).
  * Errors: INVALID_ARG for null x/g_c/g_u, n_per_image <= 0, batch <= 0,
  * a missing or short workspace when relmae_out is non-NULL, non-finite
