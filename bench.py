@@ -375,13 +375,16 @@ def main():
     del xs, gcs, gus
 
     dom = max(levels, key=lambda L: L.level.flops())
+    lv = dom.level
+    dom_ks = dfp.attention_plan(lv.B, lv.H, lv.n, lv.N_kv, lv.d, dom.ws is not None)[0]
+    dom_nf = (2 if dom.text else 1) if dom.fused else 0   # fresh ranges the launch reads
     dk = kern[f"attn_{dom.level.name}"]
     traffic = measured_traffic(
         os.path.join(ROOT, "patch_attention_cfg_amd", "csrc", "attention_bf16.hip"),
         dom.level.name)
     roofline = {"bound": "mfma", "achieved": dk["tflops"], "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": dk["tflops"] / PEAK_BF16_TFLOPS, "traffic": traffic,
-                "kernel": f"attn_fwd_bf16<{dom.level.d}, {1 if dom.fused else 0}> "
+                "kernel": f"attn_fwd_bf16<{dom.level.d}, {dom_ks}, {dom_nf}> "
                           f"({dom.level.name}, "
                           f"{dom.level.flops() / 1e9:.2f} GFLOP per launch)"}
 

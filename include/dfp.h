@@ -254,6 +254,24 @@ dfp_status dfp_relmae(const float *g_c, const float *g_u, int64_t n_per_image,
 size_t dfp_workspace_bytes(int op, int64_t n_per_image, int batch, int B, int H,
                            int n_q, int N_kv, int d);
 
+/* How a bf16 dfp_patch_attention or dfp_patch_attention_fresh call of these
+ * sizes is laid out on the GPU (host-only query, no GPU work).  The launch
+ * depends only on the sizes, on whether a big enough workspace is passed
+ * (with_workspace != 0) and on the environment overrides DFP_ATTN_SPLITS and
+ * DFP_ATTN_KS read at each call.  Outputs (HOST pointers, each may be NULL):
+ *   key_groups  1, or 2 when every workgroup splits its key range between
+ *               two groups of wavefronts and merges them on chip (d = 64,
+ *               grids too small to fill the GPU);
+ *   splits      workgroups sharing one query tile's key range (> 1 only
+ *               with a workspace);
+ *   workgroups  attention workgroups of the launch (a fresh call adds its
+ *               landing workgroups).
+ * Errors: INVALID_ARG for non-positive B/H/n_q/N_kv; UNSUPPORTED for d other
+ * than 64/128 or B*H beyond int range. */
+dfp_status dfp_attention_plan(int B, int H, int n_q, int N_kv, int d,
+                              int with_workspace, int *key_groups, int *splits,
+                              int64_t *workgroups);
+
 /* ------------------------------------------------------------------------
  * Host helpers (no GPU work).  All outputs are HOST pointers.
  * ------------------------------------------------------------------------ */

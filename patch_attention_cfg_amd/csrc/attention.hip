@@ -182,3 +182,18 @@ extern "C" dfp_status dfp_patch_attention_fresh(void *o, const void *q, void *k_
     return dfp_attn_bf16_launch(o, q, k_buf, v_buf_t, (int)BH, n_q, N_kv, d, scale, workspace,
                                 ws_bytes, &launch, stream);
 }
+
+extern "C" dfp_status dfp_attention_plan(int B, int H, int n_q, int N_kv, int d, int with_workspace,
+                                         int *key_groups, int *splits, int64_t *workgroups) {
+    if (B <= 0 || H <= 0 || n_q <= 0 || N_kv <= 0) return DFP_ERR_INVALID_ARG;
+    if (d != 64 && d != 128) return DFP_ERR_UNSUPPORTED;
+    const int64_t BH = (int64_t)B * H;
+    if (BH > 0x7FFFFFFF) return DFP_ERR_UNSUPPORTED;
+    int ks = 1, sp = 1;
+    int64_t wg = 0;
+    dfp_attn_bf16_plan((int)BH, n_q, N_kv, d, with_workspace != 0, &ks, &sp, &wg);
+    if (key_groups) *key_groups = ks;
+    if (splits) *splits = sp;
+    if (workgroups) *workgroups = wg;
+    return DFP_OK;
+}

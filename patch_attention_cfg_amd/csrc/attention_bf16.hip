@@ -111,12 +111,23 @@ struct Params {
     int land_wg;
 };
 
-template <int D>
+// KS key groups per workgroup: KS = 1 is the normal layout; with KS = 2
+// (d=64 only) the wavefronts form two groups of NWQ that take the two halves
+// of the workgroup's key range for the same NWQ x 32 queries, each with its
+// own LDS ring, and are merged through LDS at the end -- twice the key
+// parallelism for grids too small to fill the GPU, without the memory
+// round trips of a split across workgroups.
+// Fewest steps per key group for which the two-group loop uses unrolled
+// four-step trips.
+constexpr int kStaticMinSteps = 16;
+
+template <int D, int KS>
 struct Cfg {
     static constexpr int NW = D == 64 ? 4 : 8;   // wavefronts per workgroup
-    static constexpr int WG_PER_CU = D == 64 ? 2 : 1;   // resident workgroups per CU
+    static constexpr int NWQ = NW / KS;          // wavefronts per key group
+    static constexpr int WG_PER_CU = (D == 64 && KS == 1) ? 2 : 1;   // resident per CU
     static constexpr int THREADS = NW * dfp::kWave;
-    static constexpr int BLOCK_M = NW * 32;      // query rows per workgroup
+    static constexpr int BLOCK_M = NWQ * 32;     // query rows per workgroup
     static constexpr int BN = 64;                // keys per tile
     static constexpr int K_ROW = D * 2;          // bytes per K row in LDS (no padding)
     static constexpr int V_ROW = BN * 2;         // bytes per V^T row in LDS
@@ -126,15 +137,16 @@ struct Cfg {
     static constexpr int V_TILE = D * V_ROW;
     static constexpr int K_DMA = K_TILE / 1024;  // 64-lane x 16-byte copies per tile
     static constexpr int V_DMA = V_TILE / 1024;
-    static constexpr int DMA_W = (K_DMA + V_DMA) / NW;   // copies per wavefront per step
-    static constexpr int K_DMA_W = K_DMA / NW;           // ... of which K
+    static constexpr int DMA_W = (K_DMA + V_DMA) / NWQ;  // copies per wavefront per step
+    static constexpr int K_DMA_W = K_DMA / NWQ;          // ... of which K
     static constexpr int STAGES = 4;
     static constexpr int SB = BN / 32;           // 32-key score blocks per tile
     static constexpr int DB = D / 32;            // 32-channel output blocks
     static constexpr int KC = D / 16;            // K=16 slices of the Q.K^T product
     static constexpr int KC2 = BN / 16;          // K=16 slices of the P.V product
-    static_assert(K_DMA % NW == 0 && V_DMA % NW == 0, "every wavefront issues as many copies");
-    static_assert(DMA_W == 4, "the end-of-step wait keeps exactly this step's copies in flight");
+    static_assert(KS == 1 || (KS == 2 && D == 64), "two key groups at d=64 only");
+    static_assert(K_DMA % NWQ == 0 && V_DMA % NWQ == 0, "every wavefront issues as many copies");
+    static_assert(DMA_W == 4 || DMA_W == 8, "the end-of-step wait keeps this step's copies");
 };
 
 // LDS swizzle: 16-byte slot s of row r is stored at slot s ^ swz(r).  A
@@ -218,23 +230,28 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
 __device__ __forceinline__ void wait_dma_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 // Wait until at most the 4 copies issued last are still in flight (this
 // step's own; every earlier copy has landed).
-__device__ __forceinline__ void wait_dma_keep4() {
-    asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+template <int N>
+__device__ __forceinline__ void wait_dma_keep() {
+    static_assert(N == 4 || N == 8, "copies per wavefront per step");
+    if constexpr (N == 4)
+        asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    else
+        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
 }
 
 // Direct HBM -> LDS copies of one K tile (rows [j0, j0+64)) and one V^T tile
 // (columns [j0, j0+64)).  Copy instruction i of a tile writes LDS slots
 // [64 i, 64 i + 64): slot z = 64 i + lane is row z / SLOTS, stored slot
 // z % SLOTS, which holds 16-byte chunk (z % SLOTS) ^ swz(row) of that row.
-// Wavefront w issues instructions w, w + NW, ... of the K tile, then of the
+// Wavefront w of a key group issues instructions w, w + NWQ, ... of the K tile, then of the
 // V^T tile (DMA_W in all).  Every lane's byte offset from the tile start is
 // fixed for the kernel; the buffer resource starts at the tile.  K rows
 // past N_kv fall outside the resource and read as zero (their scores are
 // masked anyway); V^T reads past a row's end land in the next row or read
 // as zero, and keys >= N_kv are zeroed in LDS afterwards.
-template <int D>
+template <int D, int KS>
 struct TileDma {
-    using C = Cfg<D>;
+    using C = Cfg<D, KS>;
     uint32_t off[C::DMA_W];   // byte offset of this lane's chunk within a tile
     // A fresh range r stores V^T rows with pitch ldn_r instead of ldv.  At
     // d=64 (registers to spare) each V^T copy keeps its fresh offset per
@@ -253,11 +270,11 @@ struct TileDma {
 #pragma unroll
         for (int e = 0; e < C::DMA_W; ++e) {
             if (e < C::K_DMA_W) {
-                const int z = (wave + e * C::NW) * 64 + lane;
+                const int z = (wave + e * C::NWQ) * 64 + lane;
                 const int row = z / C::K_SLOTS, slot = (z % C::K_SLOTS) ^ swz<C::K_ROW>(row);
                 off[e] = (uint32_t)(row * C::K_ROW + slot * 16);
             } else {
-                const int z = (wave + (e - C::K_DMA_W) * C::NW) * 64 + lane;
+                const int z = (wave + (e - C::K_DMA_W) * C::NWQ) * 64 + lane;
                 const int row = z / C::V_SLOTS, slot = (z % C::V_SLOTS) ^ swz<C::V_ROW>(row);
                 off[e] = (uint32_t)(row * ldv * 2 + slot * 16);
                 offf[0][e - C::K_DMA_W] = (uint32_t)(row * ldn0 * 2 + slot * 16);
@@ -273,13 +290,13 @@ struct TileDma {
 
     // First V^T row of copy e (e >= K_DMA_W) of this wavefront (uniform).
     __device__ __forceinline__ uint32_t vrow0(int e) const {
-        return (uint32_t)(wave + (e - C::K_DMA_W) * C::NW) * 8u;
+        return (uint32_t)(wave + (e - C::K_DMA_W) * C::NWQ) * 8u;
     }
 
     // LDS byte address written by copy e of this wavefront.
     __device__ __forceinline__ uint32_t lds_of(int e, uint32_t k_stage, uint32_t v_stage) const {
-        return e < C::K_DMA_W ? k_stage + (uint32_t)(wave + e * C::NW) * 1024u
-                              : v_stage + (uint32_t)(wave + (e - C::K_DMA_W) * C::NW) * 1024u;
+        return e < C::K_DMA_W ? k_stage + (uint32_t)(wave + e * C::NWQ) * 1024u
+                              : v_stage + (uint32_t)(wave + (e - C::K_DMA_W) * C::NWQ) * 1024u;
     }
 };
 
@@ -302,6 +319,9 @@ struct Ctx {
     const uint16_t *Vf[2];
     int64_t ldv;
     int N_kv, t_begin, t_end;
+    int key_end;     // keys >= key_end are masked: min(N_kv, t_end * 64)
+    int t_stop;      // one past the tile of the group's last step (>= t_end)
+    uint32_t goff;   // LDS byte offset of this key group's ring (0 for KS = 1)
     int f_t0[2], f_t1[2], f_n[2];
     float c;   // log2(e) * scale
     int tid, ql, g;
@@ -323,10 +343,10 @@ __device__ __forceinline__ T of_range(int r, T a0, T a1) {
     return r == 1 ? a1 : a0;
 }
 
-template <int D, int NF>
-__device__ __forceinline__ CopyJob copy_job(const Ctx &x, const TileDma<D> &dma, int tk, int tv,
+template <int D, int KS, int NF>
+__device__ __forceinline__ CopyJob copy_job(const Ctx &x, const TileDma<D, KS> &dma, int tk, int tv,
                                             uint32_t lk, uint32_t lv) {
-    using C = Cfg<D>;
+    using C = Cfg<D, KS>;
     const int jk = tk * C::BN, jv = tv * C::BN;
     CopyJob j;
     const int kr = tk < x.t_end ? fresh_range<NF>(x, tk) : -1;
@@ -357,14 +377,14 @@ __device__ __forceinline__ CopyJob copy_job(const Ctx &x, const TileDma<D> &dma,
     return j;
 }
 
-template <int D>
-__device__ __forceinline__ void issue_copy(const TileDma<D> &dma, const CopyJob &j, int e) {
-    using C = Cfg<D>;
+template <int D, int KS>
+__device__ __forceinline__ void issue_copy(const TileDma<D, KS> &dma, const CopyJob &j, int e) {
+    using C = Cfg<D, KS>;
     // select values, not arrays: a selected array address would force the
     // offsets into scratch memory
     uint32_t voff = dma.off[e];
     if (e >= C::K_DMA_W) {
-        if constexpr (TileDma<D>::kPerCopyFresh) {
+        if constexpr (TileDma<D, KS>::kPerCopyFresh) {
             const int i = e >= C::K_DMA_W ? e - C::K_DMA_W : 0;
             const uint32_t f0 = dma.offf[0][i], f1 = dma.offf[1][i];
             voff = j.vsel == 0 ? voff : (j.vsel == 1 ? f0 : f1);
@@ -376,12 +396,14 @@ __device__ __forceinline__ void issue_copy(const TileDma<D> &dma, const CopyJob 
               dma.lds_of(e, j.lk, j.lv));
 }
 
-// Zero V^T columns of keys >= N_kv in a landed tile (ragged last tile).
-template <int D>
+// Zero V^T columns of keys >= N_kv in a landed tile: the ragged last tile
+// (its columns past N_kv are buffer padding, which may hold anything), or a
+// whole tile past the range (N_kv <= j0).
+template <int D, int KS>
 __device__ __forceinline__ void zero_tail_v(char *Vs, int j0, int N_kv, int tid) {
-    using C = Cfg<D>;
-    const int first = N_kv - j0;   // first masked key within the tile (1..63)
-    for (int e = tid; e < D * C::BN; e += C::THREADS) {
+    using C = Cfg<D, KS>;
+    const int first = N_kv - j0;   // first masked key within the tile (<= 63)
+    for (int e = tid; e < D * C::BN; e += C::NWQ * dfp::kWave) {   // tid: within the key group
         const int row = e / C::BN, kk = e % C::BN;
         if (kk >= first) {
             const int slot = (kk / 8) ^ swz<C::V_ROW>(row);
@@ -407,70 +429,71 @@ __device__ __forceinline__ int score_key(int i, int g) {
 // of key row key_row(ql) (+ sb*32 rows, a constant), V^T slice kc2 of
 // channel ql (+ db*32 rows).  The swizzle depends only on the row modulo 32,
 // so one offset per slice serves every block.
-template <int D>
+template <int D, int KS>
 struct OperandOffsets {
-    using C = Cfg<D>;
+    using C = Cfg<D, KS>;
     uint32_t k[C::KC];
     uint32_t v[C::KC2];
-    __device__ __forceinline__ void init(int ql, int g) {
+    // goff: LDS offset of the key group's ring, folded in once
+    __device__ __forceinline__ void init(int ql, int g, uint32_t goff) {
         const int kr = key_row(ql);
 #pragma unroll
         for (int kc = 0; kc < C::KC; ++kc)
-            k[kc] = (uint32_t)(kr * C::K_ROW + (((kc * 2 + g) ^ swz<C::K_ROW>(kr)) * 16));
+            k[kc] = goff + (uint32_t)(kr * C::K_ROW + (((kc * 2 + g) ^ swz<C::K_ROW>(kr)) * 16));
 #pragma unroll
         for (int kc2 = 0; kc2 < C::KC2; ++kc2)
-            v[kc2] = (uint32_t)(ql * C::V_ROW + (((kc2 * 2 + g) ^ swz<C::V_ROW>(ql)) * 16));
+            v[kc2] = goff + (uint32_t)(ql * C::V_ROW + (((kc2 * 2 + g) ^ swz<C::V_ROW>(ql)) * 16));
     }
 };
 
-template <int D>
-__device__ __forceinline__ bf16x8_t k_operand(const char *Ks, const OperandOffsets<D> &oo, int kc,
+template <int D, int KS>
+__device__ __forceinline__ bf16x8_t k_operand(const char *Ks, const OperandOffsets<D, KS> &oo, int kc,
                                               int sb) {
-    return *reinterpret_cast<const bf16x8_t *>(Ks + oo.k[kc] + sb * 32 * Cfg<D>::K_ROW);
+    return *reinterpret_cast<const bf16x8_t *>(Ks + oo.k[kc] + sb * 32 * Cfg<D, KS>::K_ROW);
 }
 
-template <int D>
-__device__ __forceinline__ bf16x8_t v_operand(const char *Vs, const OperandOffsets<D> &oo, int kc2,
+template <int D, int KS>
+__device__ __forceinline__ bf16x8_t v_operand(const char *Vs, const OperandOffsets<D, KS> &oo, int kc2,
                                               int db) {
-    return *reinterpret_cast<const bf16x8_t *>(Vs + oo.v[kc2] + db * 32 * Cfg<D>::V_ROW);
+    return *reinterpret_cast<const bf16x8_t *>(Vs + oo.v[kc2] + db * 32 * Cfg<D, KS>::V_ROW);
 }
 
 // S^T = K Q^T for one tile: s[sb][i] is the score of key
 // sb*32 + score_key(i, g) (tile-relative) against query ql.
-template <int D>
-__device__ __forceinline__ void qk_tile(f32x16_t (&s)[Cfg<D>::SB], const char *Ks,
-                                        const bf16x8_t (&qreg)[Cfg<D>::KC],
-                                        const OperandOffsets<D> &oo) {
-    using C = Cfg<D>;
+template <int D, int KS>
+__device__ __forceinline__ void qk_tile(f32x16_t (&s)[(Cfg<D, KS>::SB)], const char *Ks,
+                                        const bf16x8_t (&qreg)[(Cfg<D, KS>::KC)],
+                                        const OperandOffsets<D, KS> &oo) {
+    using C = Cfg<D, KS>;
     const f32x16_t zero = {};
 #pragma unroll
     for (int kc = 0; kc < C::KC; ++kc)
 #pragma unroll
         for (int sb = 0; sb < C::SB; ++sb)
-            s[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_operand<D>(Ks, oo, kc, sb), qreg[kc],
+            s[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_operand<D, KS>(Ks, oo, kc, sb), qreg[kc],
                                                             kc == 0 ? zero : s[sb], 0, 0, 0);
 }
 
 // O^T += V^T P^T over one tile's 16-key slices.  MFMA k index g*8 + j of
 // slice kc2 is key kc2*16 + g*8 + j on both operands.
-template <int D>
-__device__ __forceinline__ void pv_tile(f32x16_t (&oacc)[Cfg<D>::DB],
-                                        const bf16x8_t (&pm)[Cfg<D>::SB][2], const char *Vs,
-                                        const OperandOffsets<D> &oo) {
-    using C = Cfg<D>;
+template <int D, int KS>
+__device__ __forceinline__ void pv_tile(f32x16_t (&oacc)[(Cfg<D, KS>::DB)],
+                                        const bf16x8_t (&pm)[(Cfg<D, KS>::SB)][2], const char *Vs,
+                                        const OperandOffsets<D, KS> &oo) {
+    using C = Cfg<D, KS>;
 #pragma unroll
     for (int kc2 = 0; kc2 < C::KC2; ++kc2)
 #pragma unroll
         for (int db = 0; db < C::DB; ++db)
             oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                v_operand<D>(Vs, oo, kc2, db), pm[kc2 >> 1][kc2 & 1], oacc[db], 0, 0, 0);
+                v_operand<D, KS>(Vs, oo, kc2, db), pm[kc2 >> 1][kc2 & 1], oacc[db], 0, 0, 0);
 }
 
 // The fixed order of one step's MFMAs: pairs of Q.K^T MFMAs alternate with
 // pairs of P.V MFMAs, so consecutive MFMAs never share an accumulator.
-template <int D>
+template <int D, int KS>
 struct Steps {
-    using C = Cfg<D>;
+    using C = Cfg<D, KS>;
     static constexpr int NQ = C::SB * C::KC;             // Q.K^T MFMAs per tile
     static constexpr int NV = C::KC2 * C::DB;            // P.V MFMAs per tile
     static constexpr int N = NQ + NV;
@@ -484,17 +507,17 @@ struct Steps {
     static constexpr int copy_at(int e) { return e * (N / C::DMA_W) + 1; }
 };
 
-template <int D>
+template <int D, int KS>
 __device__ __forceinline__ bf16x8_t step_operand(int i, const char *Kn, const char *Vp,
-                                                 const OperandOffsets<D> &oo) {
-    using C = Cfg<D>;
-    using S = Steps<D>;
+                                                 const OperandOffsets<D, KS> &oo) {
+    using C = Cfg<D, KS>;
+    using S = Steps<D, KS>;
     if (S::is_qk(i)) {
         const int q = S::idx(i);
-        return k_operand<D>(Kn, oo, q / C::SB, q % C::SB);
+        return k_operand<D, KS>(Kn, oo, q / C::SB, q % C::SB);
     }
     const int v = S::idx(i);
-    return v_operand<D>(Vp, oo, v / C::DB, v % C::DB);
+    return v_operand<D, KS>(Vp, oo, v / C::DB, v % C::DB);
 }
 
 // One step's basic block: s_next = K(t+1) Q^T (from Kn), O^T += V(t-1)^T
@@ -506,18 +529,18 @@ __device__ __forceinline__ bf16x8_t step_operand(int i, const char *Kn, const ch
 // brings in this step's first two (read by the previous step) and takes
 // out the next step's first two, read from Kn_next (K(t+2), already
 // published) so they are in flight across the step boundary.
-template <int D>
-__device__ __forceinline__ void region(f32x16_t (&s_next)[Cfg<D>::SB],
-                                       f32x16_t (&oacc)[Cfg<D>::DB],
-                                       bf16x8_t (&p_cur)[Cfg<D>::SB][2], float &l_tile,
-                                       const f32x16_t (&s_cur)[Cfg<D>::SB],
-                                       const bf16x8_t (&p_prev)[Cfg<D>::SB][2],
+template <int D, int KS>
+__device__ __forceinline__ void region(f32x16_t (&s_next)[(Cfg<D, KS>::SB)],
+                                       f32x16_t (&oacc)[(Cfg<D, KS>::DB)],
+                                       bf16x8_t (&p_cur)[(Cfg<D, KS>::SB)][2], float &l_tile,
+                                       const f32x16_t (&s_cur)[(Cfg<D, KS>::SB)],
+                                       const bf16x8_t (&p_prev)[(Cfg<D, KS>::SB)][2],
                                        const char *Kn, const char *Vp, const char *Kn_next,
-                                       bf16x8_t (&carry)[2], const bf16x8_t (&qreg)[Cfg<D>::KC],
-                                       float c, float m_run, const OperandOffsets<D> &oo,
-                                       const TileDma<D> &dma, const CopyJob &job) {
-    using C = Cfg<D>;
-    using S = Steps<D>;
+                                       bf16x8_t (&carry)[2], const bf16x8_t (&qreg)[(Cfg<D, KS>::KC)],
+                                       float c, float m_run, const OperandOffsets<D, KS> &oo,
+                                       const TileDma<D, KS> &dma, const CopyJob &job) {
+    using C = Cfg<D, KS>;
+    using S = Steps<D, KS>;
     const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
     const f32x16_t zero = {};
     bf16x8_t ring[3];
@@ -525,8 +548,8 @@ __device__ __forceinline__ void region(f32x16_t (&s_next)[Cfg<D>::SB],
     ring[1] = carry[1];
 #pragma unroll
     for (int i = 0; i < S::N; ++i) {
-        ring[(i + 2) % 3] = i + 2 < S::N ? step_operand<D>(i + 2, Kn, Vp, oo)
-                                         : step_operand<D>(i + 2 - S::N, Kn_next, Vp, oo);
+        ring[(i + 2) % 3] = i + 2 < S::N ? step_operand<D, KS>(i + 2, Kn, Vp, oo)
+                                         : step_operand<D, KS>(i + 2 - S::N, Kn_next, Vp, oo);
         const bf16x8_t a = ring[i % 3];
         if (S::is_qk(i)) {
             const int q = S::idx(i), kc = q / C::SB, sb = q % C::SB;
@@ -540,7 +563,7 @@ __device__ __forceinline__ void region(f32x16_t (&s_next)[Cfg<D>::SB],
         }
 #pragma unroll
         for (int e = 0; e < C::DMA_W; ++e)
-            if (i == S::copy_at(e)) issue_copy<D>(dma, job, e);
+            if (i == S::copy_at(e)) issue_copy<D, KS>(dma, job, e);
         if (i % S::CHUNK_EVERY == S::CHUNK_EVERY - 1) {
             const int k = i / S::CHUNK_EVERY;      // chunk: two consecutive scores
             const int sb = k / 8, h = (k % 8) / 4, j = (k % 4) * 2;
@@ -561,9 +584,9 @@ __device__ __forceinline__ void region(f32x16_t (&s_next)[Cfg<D>::SB],
         for (int h = 0; h < 2; ++h) asm volatile("" ::"v"(p_cur[sb][h]));
 }
 
-template <int D>
+template <int D, int KS>
 struct State {
-    f32x16_t oacc[Cfg<D>::DB];
+    f32x16_t oacc[(Cfg<D, KS>::DB)];
     float m_run;   // reference max, log2 units (scores * log2(e) * scale)
     float l_run;   // this lane's share of the running sum
 };
@@ -572,11 +595,11 @@ struct State {
 // outgrew the reference).  Raise the reference to the tile max (never
 // lower it), rescale O and l to it and recompute the tile's
 // probabilities.
-template <int D>
+template <int D, int KS>
 __device__ __forceinline__ void raise_reference(
-    State<D> &st, const f32x16_t (&s_cur)[Cfg<D>::SB], bf16x8_t (&p_cur)[Cfg<D>::SB][2],
+    State<D, KS> &st, const f32x16_t (&s_cur)[(Cfg<D, KS>::SB)], bf16x8_t (&p_cur)[(Cfg<D, KS>::SB)][2],
     float &l_tile, float c) {
-    using C = Cfg<D>;
+    using C = Cfg<D, KS>;
     float mx = -INFINITY;
 #pragma unroll
     for (int sb = 0; sb < C::SB; ++sb)
@@ -611,18 +634,18 @@ __device__ __forceinline__ void raise_reference(
 // Split-KV merge, phase 2: each thread owns G 16-byte groups of the query
 // tile and folds NS splits per pass, with all G x NS coherent loads of a
 // pass in flight together (at most 24, to bound registers).
-template <int D>
+template <int D, int KS>
 struct MergeCfg {
-    static constexpr int G = Cfg<D>::BLOCK_M * D / 4 / Cfg<D>::THREADS;
+    static constexpr int G = Cfg<D, KS>::BLOCK_M * D / 4 / Cfg<D, KS>::THREADS;
     static constexpr int NS = 24 / G < 1 ? 1 : (24 / G > 4 ? 4 : 24 / G);
-    static_assert(G * Cfg<D>::THREADS * 4 == Cfg<D>::BLOCK_M * D, "groups tile the query tile");
+    static_assert(G * Cfg<D, KS>::THREADS * 4 == Cfg<D, KS>::BLOCK_M * D, "groups tile the query tile");
 };
 
-template <int D, int N>
-__device__ __forceinline__ void merge_pass(f32x4_t (&acc)[MergeCfg<D>::G], const float *part0,
+template <int D, int KS, int N>
+__device__ __forceinline__ void merge_pass(f32x4_t (&acc)[(MergeCfg<D, KS>::G)], const float *part0,
                                            const float *wts, int s0, int tid) {
-    using C = Cfg<D>;
-    constexpr int G = MergeCfg<D>::G;
+    using C = Cfg<D, KS>;
+    constexpr int G = MergeCfg<D, KS>::G;
     f32x4_t v[N][G];
 #pragma unroll
     for (int j = 0; j < N; ++j) {
@@ -644,10 +667,10 @@ __device__ __forceinline__ void merge_pass(f32x4_t (&acc)[MergeCfg<D>::G], const
         }
 }
 
-template <int D>
+template <int D, int KS>
 struct Smem {
-    char k[Cfg<D>::STAGES][Cfg<D>::K_TILE];
-    char v[Cfg<D>::STAGES][Cfg<D>::V_TILE];
+    char k[(Cfg<D, KS>::STAGES)][(Cfg<D, KS>::K_TILE)];
+    char v[(Cfg<D, KS>::STAGES)][(Cfg<D, KS>::V_TILE)];
 };
 
 // One pipeline step for tile t, r = t - t_begin.  Tile t' of K and of V^T
@@ -659,45 +682,47 @@ struct Smem {
 // V(t-2), freed by the previous barrier; it then waits until only its own
 // copies are in flight and publishes K(t+3), V(t+1) with a barrier.  A tile
 // is thus published one step before it is read and copied two steps ahead.
-template <int D, bool RAGGED, int NF>
-__device__ __forceinline__ void tile_step(int t, const Ctx &x, State<D> &st, Smem<D> &sm,
-                                          const TileDma<D> &dma, const OperandOffsets<D> &oo,
-                                          f32x16_t (&s_cur)[Cfg<D>::SB],
-                                          f32x16_t (&s_next)[Cfg<D>::SB],
-                                          const bf16x8_t (&p_prev)[Cfg<D>::SB][2],
-                                          bf16x8_t (&p_cur)[Cfg<D>::SB][2],
+template <int D, int KS, bool RAGGED, int NF>
+__device__ __forceinline__ void tile_step(int t, const Ctx &x, State<D, KS> &st, Smem<D, KS> &sm,
+                                          const TileDma<D, KS> &dma, const OperandOffsets<D, KS> &oo,
+                                          f32x16_t (&s_cur)[(Cfg<D, KS>::SB)],
+                                          f32x16_t (&s_next)[(Cfg<D, KS>::SB)],
+                                          const bf16x8_t (&p_prev)[(Cfg<D, KS>::SB)][2],
+                                          bf16x8_t (&p_cur)[(Cfg<D, KS>::SB)][2],
                                           bf16x8_t (&carry)[2],
-                                          const bf16x8_t (&qreg)[Cfg<D>::KC]) {
-    using C = Cfg<D>;
+                                          const bf16x8_t (&qreg)[(Cfg<D, KS>::KC)]) {
+    using C = Cfg<D, KS>;
     constexpr int BN = C::BN;
     const int r = t - x.t_begin;
     const int sk1 = (r + 1) & 3, sk2 = (r + 2) & 3, sv_prev = (r + 3) & 3;
     const int j0 = t * BN;
-    if (RAGGED && j0 + BN > x.N_kv) {  // ragged last tile: drop keys past the buffer
+    if (RAGGED && j0 + BN > x.key_end) {   // ragged last tile: drop keys past the range
 #pragma unroll
         for (int sb = 0; sb < C::SB; ++sb)
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const int key = j0 + sb * 32 + score_key(i, x.g);
-                if (key >= x.N_kv) s_cur[sb][i] = -INFINITY;
+                if (key >= x.key_end) s_cur[sb][i] = -INFINITY;
             }
     }
-    const CopyJob job = copy_job<D, NF>(x, dma, t + 4, t + 2, lds_addr(sm.k[r & 3]),
-                                           lds_addr(sm.v[(r + 2) & 3]));
+    const CopyJob job = copy_job<D, KS, NF>(x, dma, t + 4, t + 2, lds_addr(sm.k[r & 3]) + x.goff,
+                                            lds_addr(sm.v[(r + 2) & 3]) + x.goff);
 
     float l_tile = 0.f;
-    region<D>(s_next, st.oacc, p_cur, l_tile, s_cur, p_prev, sm.k[sk1], sm.v[sv_prev], sm.k[sk2],
+    region<D, KS>(s_next, st.oacc, p_cur, l_tile, s_cur, p_prev, sm.k[sk1], sm.v[sv_prev], sm.k[sk2],
               carry, qreg, x.c, st.m_run, oo, dma, job);
     // each probability is at most the tile's row-sum share, so a share
     // within kMaxTileSum proves none outgrew the reference
-    if (__any(!(l_tile <= kMaxTileSum))) raise_reference<D>(st, s_cur, p_cur, l_tile, x.c);
+    if (__any(!(l_tile <= kMaxTileSum))) raise_reference<D, KS>(st, s_cur, p_cur, l_tile, x.c);
     st.l_run += l_tile;
 
-    wait_dma_keep4();                 // K(t+3), V(t+1) have landed
+    wait_dma_keep<C::DMA_W>();                 // K(t+3), V(t+1) have landed
     __syncthreads();
-    if (RAGGED && j0 + 2 * BN > x.N_kv && t + 1 < x.t_end) {   // V(t+1) is the ragged last tile
-        zero_tail_v<D>(sm.v[(r + 1) & 3], j0 + BN, x.N_kv, x.tid);
-        __syncthreads();
+    if (RAGGED) {
+        // V(t+1) is ragged, or a padding step's tile past the range
+        const bool tail = j0 + 2 * BN > x.key_end && t + 1 < x.t_stop;
+        if (tail) zero_tail_v<D, KS>(sm.v[(r + 1) & 3] + x.goff, j0 + BN, x.key_end, x.tid);
+        if (KS > 1 || tail) __syncthreads();   // one barrier count for both key groups
     }
 }
 
@@ -705,20 +730,20 @@ __device__ __forceinline__ void tile_step(int t, const Ctx &x, State<D> &st, Sme
 // compile time (LDS operand addresses become immediates) and copies of full
 // in-range tiles only: fixed buffer resources over the whole (batch, head)
 // (and over its fresh rows) with the tile start as the scalar offset.
-template <int D, int R4, int NF>
-__device__ __forceinline__ void tile_step_static(int t, const Ctx &x, State<D> &st, Smem<D> &sm,
-                                                 const TileDma<D> &dma,
-                                                 const OperandOffsets<D> &oo,
+template <int D, int KS, int R4, int NF>
+__device__ __forceinline__ void tile_step_static(int t, const Ctx &x, State<D, KS> &st, Smem<D, KS> &sm,
+                                                 const TileDma<D, KS> &dma,
+                                                 const OperandOffsets<D, KS> &oo,
                                                  const int32x4_t &rk_all, const int32x4_t &rv_all,
                                                  const int32x4_t (&rk_f)[2],
                                                  const int32x4_t (&rv_f)[2],
-                                                 f32x16_t (&s_cur)[Cfg<D>::SB],
-                                                 f32x16_t (&s_next)[Cfg<D>::SB],
-                                                 const bf16x8_t (&p_prev)[Cfg<D>::SB][2],
-                                                 bf16x8_t (&p_cur)[Cfg<D>::SB][2],
+                                                 f32x16_t (&s_cur)[(Cfg<D, KS>::SB)],
+                                                 f32x16_t (&s_next)[(Cfg<D, KS>::SB)],
+                                                 const bf16x8_t (&p_prev)[(Cfg<D, KS>::SB)][2],
+                                                 bf16x8_t (&p_cur)[(Cfg<D, KS>::SB)][2],
                                                  bf16x8_t (&carry)[2],
-                                                 const bf16x8_t (&qreg)[Cfg<D>::KC]) {
-    using C = Cfg<D>;
+                                                 const bf16x8_t (&qreg)[(Cfg<D, KS>::KC)]) {
+    using C = Cfg<D, KS>;
     constexpr int BN = C::BN;
     constexpr int sk1 = (R4 + 1) & 3, sk2 = (R4 + 2) & 3, sv_prev = (R4 + 3) & 3;
     CopyJob job;
@@ -729,29 +754,29 @@ __device__ __forceinline__ void tile_step_static(int t, const Ctx &x, State<D> &
              (uint32_t)(BN * D * 2);
     job.sv = (uint32_t)(t + 2 - (vr < 0 ? 0 : of_range(vr, x.f_t0[0], x.f_t0[1]))) *
              (uint32_t)(BN * 2);
-    job.lk = lds_addr(sm.k[R4]);
-    job.lv = lds_addr(sm.v[(R4 + 2) & 3]);
+    job.lk = lds_addr(sm.k[R4]) + x.goff;
+    job.lv = lds_addr(sm.v[(R4 + 2) & 3]) + x.goff;
     job.vsel = vr + 1;
     job.vlane = vr < 0 ? 0u : of_range(vr, dma.lane_dp[0], dma.lane_dp[1]);
     job.vpitch = vr < 0 ? 0u : of_range(vr, dma.dpitch[0], dma.dpitch[1]);
     float l_tile = 0.f;
-    region<D>(s_next, st.oacc, p_cur, l_tile, s_cur, p_prev, sm.k[sk1], sm.v[sv_prev], sm.k[sk2],
+    region<D, KS>(s_next, st.oacc, p_cur, l_tile, s_cur, p_prev, sm.k[sk1], sm.v[sv_prev], sm.k[sk2],
               carry, qreg, x.c, st.m_run, oo, dma, job);
-    if (__any(!(l_tile <= kMaxTileSum))) raise_reference<D>(st, s_cur, p_cur, l_tile, x.c);
+    if (__any(!(l_tile <= kMaxTileSum))) raise_reference<D, KS>(st, s_cur, p_cur, l_tile, x.c);
     st.l_run += l_tile;
-    wait_dma_keep4();
+    wait_dma_keep<C::DMA_W>();
     __syncthreads();
 }
 
 // Copy fresh range r into the buffer.
-template <int D>
+template <int D, int KS>
 __device__ __forceinline__ void land_range(const Params &p, int r) {
     // 32-bit vector indices (the launcher checks that they fit)
     constexpr int U = 4;
     const int f_n = r == 1 ? p.f_n[1] : p.f_n[0];
     const int f_row0 = r == 1 ? p.f_row0[1] : p.f_row0[0];
-    const uint32_t stride = (uint32_t)p.land_wg * Cfg<D>::THREADS;
-    const uint32_t first = (uint32_t)((int)blockIdx.x - p.total_wg) * Cfg<D>::THREADS + threadIdx.x;
+    const uint32_t stride = (uint32_t)p.land_wg * Cfg<D, KS>::THREADS;
+    const uint32_t first = (uint32_t)((int)blockIdx.x - p.total_wg) * Cfg<D, KS>::THREADS + threadIdx.x;
     const uint32_t per_bh = (uint32_t)f_n * D / 8;   // vectors of one (b,h)'s fresh K rows
     const uint32_t per_row = (uint32_t)f_n / 8;      // vectors of one fresh V^T channel row
     const uint32_t nk = per_bh * p.BH, nv = per_row * p.BH * D;
@@ -793,26 +818,31 @@ __device__ __forceinline__ void land_range(const Params &p, int r) {
 // buffer (K rows row-major, V^T channel rows), as dfp_kv_scatter would.  No
 // attention workgroup of the launch reads those buffer rows.  Four 16-byte
 // vectors per thread per pass, all loads before the stores.
-template <int D, int NF>
+template <int D, int KS, int NF>
 __device__ __forceinline__ void land_fresh(const Params &p) {
 #pragma unroll
-    for (int r = 0; r < NF; ++r) land_range<D>(p, r);
+    for (int r = 0; r < NF; ++r) land_range<D, KS>(p, r);
 }
 
-template <int D, int NF>
-__global__ __launch_bounds__(Cfg<D>::THREADS, Cfg<D>::WG_PER_CU) void attn_fwd_bf16(Params p) {
-    using C = Cfg<D>;
+template <int D, int KS, int NF>
+__global__ __launch_bounds__((Cfg<D, KS>::THREADS), (Cfg<D, KS>::WG_PER_CU)) void attn_fwd_bf16(Params p) {
+    using C = Cfg<D, KS>;
     constexpr int BN = C::BN;
-    __shared__ __attribute__((aligned(16))) Smem<D> sm;
+    __shared__ __attribute__((aligned(16))) Smem<D, KS> sm_all[KS];   // one ring per key group
     __shared__ int s_last;
+    Smem<D, KS> &sm = sm_all[0];   // stage addresses; a group's offset comes from x.goff
     if (NF > 0 && (int)blockIdx.x >= p.total_wg) {
-        land_fresh<D, NF>(p);
+        land_fresh<D, KS, NF>(p);
         return;
     }
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave_all = tid >> 6;
+    // key group (uniform per wavefront, so its ranges stay in scalar registers)
+    const int gk = KS == 1 ? 0 : __builtin_amdgcn_readfirstlane(wave_all / C::NWQ);
+    const int wave = KS == 1 ? wave_all : wave_all % C::NWQ;   // wavefront within the group
+    const int tid_g = tid - gk * C::NWQ * dfp::kWave;           // thread within the group
     const int ql = lane & 31;   // query column of this lane in every MFMA block
     const int g = lane >> 5;    // which half of the K=16 slice this lane feeds
 
@@ -842,10 +872,20 @@ __global__ __launch_bounds__(Cfg<D>::THREADS, Cfg<D>::WG_PER_CU) void attn_fwd_b
     x.ldv = p.ldv;
     x.N_kv = N_kv;
     const int ntiles = (N_kv + BN - 1) / BN;
-    x.t_begin = split * p.tiles_per_split;
-    x.t_end = min(ntiles, x.t_begin + p.tiles_per_split);
+    const int wg_t0 = split * p.tiles_per_split;
+    const int wg_t1 = min(ntiles, wg_t0 + p.tiles_per_split);
+    // Steps per key group, the same for every wavefront: with two groups the
+    // first takes ceil(n/2) tiles, the second the rest, padded to as many
+    // steps with a masked tile past its range (the range holds >= 2 tiles).
+    const int half = KS == 1 ? wg_t1 - wg_t0 : (wg_t1 - wg_t0 + 1) / 2;
+    const int R = half;
+    x.t_begin = wg_t0 + gk * half;
+    x.t_end = gk == 0 ? wg_t0 + half : wg_t1;
+    x.key_end = min(N_kv, x.t_end * BN);
+    x.t_stop = x.t_begin + R;
+    x.goff = KS == 1 ? 0u : (uint32_t)(gk * sizeof(Smem<D, KS>));
     x.c = p.c_log2;
-    x.tid = tid;
+    x.tid = tid_g;
     x.ql = ql;
     x.g = g;
 
@@ -859,7 +899,7 @@ __global__ __launch_bounds__(Cfg<D>::THREADS, Cfg<D>::WG_PER_CU) void attn_fwd_b
                                            Qh + (int64_t)q_row * D + kc * 16 + g * 8)
                                      : zero4());
 
-    State<D> st;
+    State<D, KS> st;
 #pragma unroll
     for (int db = 0; db < C::DB; ++db)
 #pragma unroll
@@ -870,38 +910,41 @@ __global__ __launch_bounds__(Cfg<D>::THREADS, Cfg<D>::WG_PER_CU) void attn_fwd_b
     // zeroed, since the first step's P.V uses zero probabilities against
     // it; S(t0) and the reference max; the first step's first operands;
     // K(t0+3) and V(t0+1) in flight (the loop's entry state).
-    TileDma<D> dma;
+    TileDma<D, KS> dma;
     dma.init(wave, lane, p.ldv, x.f_n[0], x.f_n[1]);
-    OperandOffsets<D> oo;
-    oo.init(ql, g);
+    OperandOffsets<D, KS> oo;
+    oo.init(ql, g, x.goff);
     const int t0 = x.t_begin;
     {
-        const CopyJob j0 =
-            copy_job<D, NF>(x, dma, t0, t0, lds_addr(sm.k[0]), lds_addr(sm.v[0]));
-        const CopyJob j1 =
-            copy_job<D, NF>(x, dma, t0 + 1, t0 + 1, lds_addr(sm.k[1]), lds_addr(sm.v[1]));
-        const CopyJob j2 =
-            copy_job<D, NF>(x, dma, t0 + 2, t0 + 2, lds_addr(sm.k[2]), lds_addr(sm.v[2]));
+        const uint32_t go = x.goff;
+        const CopyJob j0 = copy_job<D, KS, NF>(x, dma, t0, t0, lds_addr(sm.k[0]) + go,
+                                               lds_addr(sm.v[0]) + go);
+        const CopyJob j1 = copy_job<D, KS, NF>(x, dma, t0 + 1, t0 + 1, lds_addr(sm.k[1]) + go,
+                                               lds_addr(sm.v[1]) + go);
+        const CopyJob j2 = copy_job<D, KS, NF>(x, dma, t0 + 2, t0 + 2, lds_addr(sm.k[2]) + go,
+                                               lds_addr(sm.v[2]) + go);
 #pragma unroll
-        for (int e = 0; e < C::DMA_W; ++e) issue_copy<D>(dma, j0, e);   // K(t0), V(t0)
+        for (int e = 0; e < C::DMA_W; ++e) issue_copy<D, KS>(dma, j0, e);   // K(t0), V(t0)
 #pragma unroll
-        for (int e = 0; e < C::K_DMA_W; ++e) issue_copy<D>(dma, j1, e);   // K(t0+1)
+        for (int e = 0; e < C::K_DMA_W; ++e) issue_copy<D, KS>(dma, j1, e);   // K(t0+1)
 #pragma unroll
-        for (int e = 0; e < C::K_DMA_W; ++e) issue_copy<D>(dma, j2, e);   // K(t0+2)
+        for (int e = 0; e < C::K_DMA_W; ++e) issue_copy<D, KS>(dma, j2, e);   // K(t0+2)
     }
-    for (int e = tid; e < C::V_TILE / 16; e += C::THREADS)
-        reinterpret_cast<uint4 *>(sm.v[3])[e] = zero4();
+    for (int e = tid_g; e < C::V_TILE / 16; e += C::NWQ * dfp::kWave)
+        reinterpret_cast<uint4 *>(sm.v[3] + x.goff)[e] = zero4();
     wait_dma_all();
     __syncthreads();
-    if (t0 * BN + BN > N_kv) zero_tail_v<D>(sm.v[0], t0 * BN, N_kv, tid);   // lone ragged tile
+    if (t0 * BN + BN > x.key_end)   // lone ragged tile
+        zero_tail_v<D, KS>(sm.v[0] + x.goff, t0 * BN, x.key_end, tid_g);
 
     f32x16_t sA[C::SB], sB[C::SB];
     bf16x8_t pA[C::SB][2], pB[C::SB][2];
-    qk_tile<D>(sA, sm.k[0], qreg, oo);
+    qk_tile<D, KS>(sA, sm.k[0], qreg, oo);
     // The reference max is the first tile's max over valid keys; it stays
-    // fixed until a later tile outgrows it (raise_reference).
+    // fixed until a later tile outgrows it (raise_reference).  A key group's
+    // first tile always holds valid keys.
     {
-        const int nvalid = N_kv - t0 * BN;
+        const int nvalid = x.key_end - t0 * BN;
         float mx = -INFINITY;
 #pragma unroll
         for (int sb = 0; sb < C::SB; ++sb)
@@ -919,13 +962,13 @@ __global__ __launch_bounds__(Cfg<D>::THREADS, Cfg<D>::WG_PER_CU) void attn_fwd_b
         for (int h = 0; h < 2; ++h)
 #pragma unroll
             for (int j = 0; j < 8; ++j) pB[sb][h][j] = (__bf16)0.0f;
-    bf16x8_t carry[2] = {step_operand<D>(0, sm.k[1], sm.v[0], oo),
-                         step_operand<D>(1, sm.k[1], sm.v[0], oo)};
+    bf16x8_t carry[2] = {step_operand<D, KS>(0, sm.k[1], sm.v[0], oo),
+                         step_operand<D, KS>(1, sm.k[1], sm.v[0], oo)};
     {
-        const CopyJob j3 =
-            copy_job<D, NF>(x, dma, t0 + 3, t0 + 1, lds_addr(sm.k[3]), lds_addr(sm.v[1]));
+        const CopyJob j3 = copy_job<D, KS, NF>(x, dma, t0 + 3, t0 + 1, lds_addr(sm.k[3]) + x.goff,
+                                               lds_addr(sm.v[1]) + x.goff);
 #pragma unroll
-        for (int e = 0; e < C::DMA_W; ++e) issue_copy<D>(dma, j3, e);   // K(t0+3), V(t0+1)
+        for (int e = 0; e < C::DMA_W; ++e) issue_copy<D, KS>(dma, j3, e);   // K(t0+3), V(t0+1)
     }
     __syncthreads();   // stage 0 of K is free; V(t0)'s zeroed tail is visible
 
@@ -933,40 +976,130 @@ __global__ __launch_bounds__(Cfg<D>::THREADS, Cfg<D>::WG_PER_CU) void attn_fwd_b
     // two steps per trip and never copies scores or probabilities.  Only
     // the last tile can be ragged: the final one or two steps take the path
     // that masks it.
-    int t = t0;
-    {
-        // full tiles only: every copy of a static trip lands tiles below n_full
-        const int n_full = min(x.t_end, N_kv / BN);
+    if constexpr (KS == 1) {
+        int t = t0;
+        {
+            // full tiles only: every copy of a static trip lands tiles below n_full
+            const int n_full = min(x.t_end, N_kv / BN);
+            const int32x4_t rk_all = buffer_rsrc(x.Kh, (uint32_t)N_kv * D * 2);
+            const int32x4_t rv_all = buffer_rsrc(x.Vh, (uint32_t)((int64_t)D * x.ldv * 2));
+            const int32x4_t rk_f[2] = {buffer_rsrc(x.Kf[0], (uint32_t)x.f_n[0] * D * 2),
+                                       buffer_rsrc(x.Kf[1], (uint32_t)x.f_n[1] * D * 2)};
+            const int32x4_t rv_f[2] = {
+                buffer_rsrc(x.Vf[0], (uint32_t)((int64_t)D * x.f_n[0] * 2)),
+                buffer_rsrc(x.Vf[1], (uint32_t)((int64_t)D * x.f_n[1] * 2))};
+            for (; t + 8 <= n_full; t += 4) {
+                tile_step_static<D, KS, 0, NF>(t, x, st, sm, dma, oo, rk_all, rv_all, rk_f, rv_f,
+                                               sA, sB, pB, pA, carry, qreg);
+                tile_step_static<D, KS, 1, NF>(t + 1, x, st, sm, dma, oo, rk_all, rv_all, rk_f,
+                                               rv_f, sB, sA, pA, pB, carry, qreg);
+                tile_step_static<D, KS, 2, NF>(t + 2, x, st, sm, dma, oo, rk_all, rv_all, rk_f,
+                                               rv_f, sA, sB, pB, pA, carry, qreg);
+                tile_step_static<D, KS, 3, NF>(t + 3, x, st, sm, dma, oo, rk_all, rv_all, rk_f,
+                                               rv_f, sB, sA, pA, pB, carry, qreg);
+            }
+        }
+        for (; t + 2 < x.t_end; t += 2) {
+            tile_step<D, KS, false, NF>(t, x, st, sm, dma, oo, sA, sB, pB, pA, carry, qreg);
+            tile_step<D, KS, false, NF>(t + 1, x, st, sm, dma, oo, sB, sA, pA, pB, carry, qreg);
+        }
+        if (t + 1 < x.t_end) {
+            tile_step<D, KS, true, NF>(t, x, st, sm, dma, oo, sA, sB, pB, pA, carry, qreg);
+            tile_step<D, KS, true, NF>(t + 1, x, st, sm, dma, oo, sB, sA, pA, pB, carry, qreg);
+            pv_tile<D, KS>(st.oacc, pB, sm.v[(t + 1 - t0) & 3], oo);
+        } else {
+            // a ragged last tile after an unmasked step: V(t) has landed and
+            // is first read after this step's barrier
+            if (t > t0 && (t + 1) * BN > x.key_end)
+                zero_tail_v<D, KS>(sm.v[(t - t0) & 3], t * BN, x.key_end, x.tid);
+            tile_step<D, KS, true, NF>(t, x, st, sm, dma, oo, sA, sB, pB, pA, carry, qreg);
+            pv_tile<D, KS>(st.oacc, pA, sm.v[(t - t0) & 3], oo);
+        }
+    } else {
+        // Two key groups step in lockstep (the same barriers every step), so
+        // every loop bound is the same for all wavefronts: r counts steps
+        // from the group's first tile.  The second group's range can be one
+        // tile shorter; its last real tile and the masked padding step fall
+        // in the masked steps at the end.
+        const int h1 = wg_t1 - (wg_t0 + half);   // tiles of the second group (half or half-1)
+        const int full = N_kv / BN;
+        const int r_full = min(min(wg_t0 + half, full) - wg_t0, min(wg_t1, full) - (wg_t0 + half));
         const int32x4_t rk_all = buffer_rsrc(x.Kh, (uint32_t)N_kv * D * 2);
         const int32x4_t rv_all = buffer_rsrc(x.Vh, (uint32_t)((int64_t)D * x.ldv * 2));
         const int32x4_t rk_f[2] = {buffer_rsrc(x.Kf[0], (uint32_t)x.f_n[0] * D * 2),
                                    buffer_rsrc(x.Kf[1], (uint32_t)x.f_n[1] * D * 2)};
         const int32x4_t rv_f[2] = {buffer_rsrc(x.Vf[0], (uint32_t)((int64_t)D * x.f_n[0] * 2)),
                                    buffer_rsrc(x.Vf[1], (uint32_t)((int64_t)D * x.f_n[1] * 2))};
-        for (; t + 8 <= n_full; t += 4) {
-            tile_step_static<D, 0, NF>(t, x, st, sm, dma, oo, rk_all, rv_all, rk_f, rv_f, sA,
-                                          sB, pB, pA, carry, qreg);
-            tile_step_static<D, 1, NF>(t + 1, x, st, sm, dma, oo, rk_all, rv_all, rk_f, rv_f,
-                                          sB, sA, pA, pB, carry, qreg);
-            tile_step_static<D, 2, NF>(t + 2, x, st, sm, dma, oo, rk_all, rv_all, rk_f, rv_f,
-                                          sA, sB, pB, pA, carry, qreg);
-            tile_step_static<D, 3, NF>(t + 3, x, st, sm, dma, oo, rk_all, rv_all, rk_f, rv_f,
-                                          sB, sA, pA, pB, carry, qreg);
+        int r = 0;
+        // Unrolled four-step trips only for long ranges: a short range runs
+        // each copy of the step code about once, and after other kernels
+        // every copy is an instruction-cache miss (fewer copies, fewer misses).
+        const int r_static = r_full >= kStaticMinSteps ? r_full : 0;
+        for (; r + 8 <= r_static; r += 4) {
+            const int t = x.t_begin + r;
+            tile_step_static<D, KS, 0, NF>(t, x, st, sm, dma, oo, rk_all, rv_all, rk_f, rv_f, sA,
+                                           sB, pB, pA, carry, qreg);
+            tile_step_static<D, KS, 1, NF>(t + 1, x, st, sm, dma, oo, rk_all, rv_all, rk_f, rv_f,
+                                           sB, sA, pA, pB, carry, qreg);
+            tile_step_static<D, KS, 2, NF>(t + 2, x, st, sm, dma, oo, rk_all, rv_all, rk_f, rv_f,
+                                           sA, sB, pB, pA, carry, qreg);
+            tile_step_static<D, KS, 3, NF>(t + 3, x, st, sm, dma, oo, rk_all, rv_all, rk_f, rv_f,
+                                           sB, sA, pA, pB, carry, qreg);
+        }
+        for (; r + 2 < h1; r += 2) {
+            const int t = x.t_begin + r;
+            tile_step<D, KS, false, NF>(t, x, st, sm, dma, oo, sA, sB, pB, pA, carry, qreg);
+            tile_step<D, KS, false, NF>(t + 1, x, st, sm, dma, oo, sB, sA, pA, pB, carry, qreg);
+        }
+        // a ragged tile right after an unmasked step: V(t) has landed and is
+        // first read after the next step's barrier
+        if (r > 0 && (x.t_begin + r + 1) * BN > x.key_end)
+            zero_tail_v<D, KS>(sm.v[r & 3] + x.goff, (x.t_begin + r) * BN, x.key_end, x.tid);
+        for (; r + 1 < R; r += 2) {
+            const int t = x.t_begin + r;
+            tile_step<D, KS, true, NF>(t, x, st, sm, dma, oo, sA, sB, pB, pA, carry, qreg);
+            tile_step<D, KS, true, NF>(t + 1, x, st, sm, dma, oo, sB, sA, pA, pB, carry, qreg);
+        }
+        if (r < R) {
+            tile_step<D, KS, true, NF>(x.t_begin + r, x, st, sm, dma, oo, sA, sB, pB, pA, carry,
+                                       qreg);
+            pv_tile<D, KS>(st.oacc, pA, sm.v[r & 3], oo);
+        } else {
+            pv_tile<D, KS>(st.oacc, pB, sm.v[(r - 1) & 3], oo);
         }
     }
-    for (; t + 2 < x.t_end; t += 2) {
-        tile_step<D, false, NF>(t, x, st, sm, dma, oo, sA, sB, pB, pA, carry, qreg);
-        tile_step<D, false, NF>(t + 1, x, st, sm, dma, oo, sB, sA, pA, pB, carry, qreg);
-    }
-    if (t + 1 < x.t_end) {
-        tile_step<D, true, NF>(t, x, st, sm, dma, oo, sA, sB, pB, pA, carry, qreg);
-        tile_step<D, true, NF>(t + 1, x, st, sm, dma, oo, sB, sA, pA, pB, carry, qreg);
-        pv_tile<D>(st.oacc, pB, sm.v[(t + 1 - t0) & 3], oo);
-    } else {
-        tile_step<D, true, NF>(t, x, st, sm, dma, oo, sA, sB, pB, pA, carry, qreg);
-        pv_tile<D>(st.oacc, pA, sm.v[(t - t0) & 3], oo);
-    }
     wait_dma_all();   // no copy may outlive the workgroup's LDS
+
+    if constexpr (KS == 2) {
+        // The second key group hands its (O, m, l) to the first through LDS
+        // (its own ring, now idle); the first merges them into its
+        // registers, lane for lane in the same accumulator layout.
+        constexpr int PER = C::DB * 16 + 2;   // floats per lane
+        static_assert(C::NWQ * dfp::kWave * PER * 4 <= (int)sizeof(Smem<D, KS>), "fits a ring");
+        float *xch = reinterpret_cast<float *>(&sm_all[1]) + (wave * dfp::kWave + lane) * PER;
+        __syncthreads();   // both groups are done with their rings
+        if (gk == 1) {
+#pragma unroll
+            for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) xch[db * 16 + i] = st.oacc[db][i];
+            xch[C::DB * 16] = st.m_run;
+            xch[C::DB * 16 + 1] = st.l_run;
+        }
+        __syncthreads();
+        if (gk == 1) return;
+        const float m1 = xch[C::DB * 16], l1 = xch[C::DB * 16 + 1];
+        const float mstar = fmaxf(st.m_run, m1);
+        const float a0 = __builtin_amdgcn_exp2f(st.m_run - mstar);
+        const float a1 = __builtin_amdgcn_exp2f(m1 - mstar);
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                st.oacc[db][i] = fmaf(a0, st.oacc[db][i], a1 * xch[db * 16 + i]);
+        st.l_run = fmaf(a0, st.l_run, a1 * l1);
+        st.m_run = mstar;
+    }
 
     const float l_tot = pair_sum(st.l_run);
 
@@ -1054,18 +1187,18 @@ __global__ __launch_bounds__(Cfg<D>::THREADS, Cfg<D>::WG_PER_CU) void attn_fwd_b
             if (s < p.splits) wts[tid * kMaxSplits + s] = ms[s] * inv;
     }
     __syncthreads();
-    constexpr int G = MergeCfg<D>::G;
-    constexpr int NS = MergeCfg<D>::NS;
+    constexpr int G = MergeCfg<D, KS>::G;
+    constexpr int NS = MergeCfg<D, KS>::NS;
     f32x4_t acc[G];
 #pragma unroll
     for (int k = 0; k < G; ++k) acc[k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     const float *part0 = p.part_o + base * C::BLOCK_M * D;
     for (int s0 = 0; s0 < p.splits; s0 += NS) {
         switch (min(NS, p.splits - s0)) {
-            case 1: merge_pass<D, 1>(acc, part0, wts, s0, tid); break;
-            case 2: merge_pass<D, (NS >= 2 ? 2 : 1)>(acc, part0, wts, s0, tid); break;
-            case 3: merge_pass<D, (NS >= 3 ? 3 : 1)>(acc, part0, wts, s0, tid); break;
-            default: merge_pass<D, NS>(acc, part0, wts, s0, tid); break;
+            case 1: merge_pass<D, KS, 1>(acc, part0, wts, s0, tid); break;
+            case 2: merge_pass<D, KS, (NS >= 2 ? 2 : 1)>(acc, part0, wts, s0, tid); break;
+            case 3: merge_pass<D, KS, (NS >= 3 ? 3 : 1)>(acc, part0, wts, s0, tid); break;
+            default: merge_pass<D, KS, NS>(acc, part0, wts, s0, tid); break;
         }
     }
 #pragma unroll
@@ -1087,6 +1220,7 @@ __global__ __launch_bounds__(Cfg<D>::THREADS, Cfg<D>::WG_PER_CU) void attn_fwd_b
 constexpr int kCus = 256;
 
 struct Plan {
+    int ks;   // key groups per workgroup (1, or 2 at d=64)
     int block_m, q_tiles, ntiles, splits, tiles_per_split;
 };
 
@@ -1097,16 +1231,20 @@ struct Plan {
 // one).  Workgroups beyond the resident slots run in later rounds.  Every
 // workgroup pays a fixed prologue/epilogue; a split adds the hand-off
 // latency and moves each fp32 partial through memory twice (publish, merge).
+// At d=64 a grid too small to fill the GPU can instead use two key groups
+// per workgroup (64 queries, one workgroup per CU, half the steps, an LDS
+// merge): chosen when its estimate beats the best split.
 Plan make_plan(int BH, int n_q, int N_kv, int d, bool can_split) {
     Plan pl;
-    pl.block_m = d == 64 ? Cfg<64>::BLOCK_M : Cfg<128>::BLOCK_M;
+    pl.ks = 1;
+    pl.block_m = d == 64 ? Cfg<64, 1>::BLOCK_M : Cfg<128, 1>::BLOCK_M;
     const int bn = 64;
     pl.q_tiles = (n_q + pl.block_m - 1) / pl.block_m;
     pl.ntiles = (N_kv + bn - 1) / bn;
     pl.splits = 1;
     pl.tiles_per_split = pl.ntiles;
     if (!can_split) return pl;
-    const int per_cu = d == 64 ? Cfg<64>::WG_PER_CU : Cfg<128>::WG_PER_CU;
+    const int per_cu = d == 64 ? Cfg<64, 1>::WG_PER_CU : Cfg<128, 1>::WG_PER_CU;
     const double t_alone = d == 64 ? 0.62e-6 : 1.7e-6;   // s per step, CU to itself
     const double t_shared = 1.09e-6;                     // s per step, two per CU (d=64)
     const double t_fixed = 3e-6;                         // prologue + epilogue
@@ -1139,6 +1277,21 @@ Plan make_plan(int BH, int n_q, int N_kv, int d, bool can_split) {
         }
         if (forced > 0 && s == forced) break;
     }
+    const char *env_ks = std::getenv("DFP_ATTN_KS");
+    const int forced_ks = env_ks ? std::atoi(env_ks) : 0;
+    if (d == 64 && pl.ntiles >= 2 && forced <= 1 && forced_ks != 1) {
+        const int q_tiles2 = (n_q + Cfg<64, 2>::BLOCK_M - 1) / Cfg<64, 2>::BLOCK_M;
+        const double wgs2 = (double)BH * q_tiles2;   // one workgroup per CU
+        const double t2 = std::ceil(wgs2 / kCus) * ((pl.ntiles + 1) / 2) * t_alone + t_fixed +
+                          0.5e-6;   // LDS merge
+        if (forced_ks == 2 || (forced <= 0 && t2 < best * 0.98)) {
+            pl.ks = 2;
+            pl.block_m = Cfg<64, 2>::BLOCK_M;
+            pl.q_tiles = q_tiles2;
+            pl.splits = 1;
+            pl.tiles_per_split = pl.ntiles;
+        }
+    }
     return pl;
 }
 
@@ -1161,6 +1314,14 @@ size_t dfp_attn_workspace_bytes(int B, int H, int n_q, int N_kv, int d) {
     return need_bytes(BH, d, make_plan(BH, n_q, N_kv, d, true));
 }
 
+void dfp_attn_bf16_plan(int BH, int n_q, int N_kv, int d, bool can_split, int *key_groups,
+                        int *splits, int64_t *workgroups) {
+    const Plan pl = make_plan(BH, n_q, N_kv, d, can_split);
+    *key_groups = pl.ks;
+    *splits = pl.splits;
+    *workgroups = (int64_t)pl.q_tiles * BH * pl.splits;
+}
+
 dfp_status dfp_attn_bf16_launch(void *o, const void *q, const void *k, const void *vt, int BH,
                                 int n_q, int N_kv, int d, float scale, void *ws, size_t ws_bytes,
                                 const dfp_fresh_launch *fresh, hipStream_t stream) {
@@ -1177,7 +1338,8 @@ dfp_status dfp_attn_bf16_launch(void *o, const void *q, const void *k, const voi
     // free in its last round (at least 16, at most 64)
     int land_wg = 0;
     if (fresh && fresh->land) {
-        const int64_t slots = (int64_t)kCus * (d == 64 ? Cfg<64>::WG_PER_CU : Cfg<128>::WG_PER_CU);
+        const int64_t slots =
+            (int64_t)kCus * (d == 64 && pl.ks == 1 ? Cfg<64, 1>::WG_PER_CU : 1);
         const int64_t free = (slots - blocks % slots) % slots;
         land_wg = (int)(free < 16 ? 16 : (free > 64 ? 64 : free));
     }
@@ -1229,18 +1391,26 @@ dfp_status dfp_attn_bf16_launch(void *o, const void *q, const void *k, const voi
     }
     const dim3 grid((unsigned)(blocks + land_wg));
     const int nf = fresh ? fresh->count : 0;
-    if (d == 64 && nf == 0)
-        hipLaunchKernelGGL((attn_fwd_bf16<64, 0>), grid, dim3(Cfg<64>::THREADS), 0, stream, p);
+    if (d == 64 && pl.ks == 2) {
+        const dim3 block(Cfg<64, 2>::THREADS);
+        if (nf == 0) hipLaunchKernelGGL((attn_fwd_bf16<64, 2, 0>), grid, block, 0, stream, p);
+        else if (nf == 1) hipLaunchKernelGGL((attn_fwd_bf16<64, 2, 1>), grid, block, 0, stream, p);
+        else hipLaunchKernelGGL((attn_fwd_bf16<64, 2, 2>), grid, block, 0, stream, p);
+    } else if (d == 64 && nf == 0)
+        hipLaunchKernelGGL((attn_fwd_bf16<64, 1, 0>), grid, dim3(Cfg<64, 1>::THREADS), 0, stream, p);
     else if (d == 64 && nf == 1)
-        hipLaunchKernelGGL((attn_fwd_bf16<64, 1>), grid, dim3(Cfg<64>::THREADS), 0, stream, p);
+        hipLaunchKernelGGL((attn_fwd_bf16<64, 1, 1>), grid, dim3(Cfg<64, 1>::THREADS), 0, stream, p);
     else if (d == 64 && nf == 2)
-        hipLaunchKernelGGL((attn_fwd_bf16<64, 2>), grid, dim3(Cfg<64>::THREADS), 0, stream, p);
+        hipLaunchKernelGGL((attn_fwd_bf16<64, 1, 2>), grid, dim3(Cfg<64, 1>::THREADS), 0, stream, p);
     else if (d == 128 && nf == 0)
-        hipLaunchKernelGGL((attn_fwd_bf16<128, 0>), grid, dim3(Cfg<128>::THREADS), 0, stream, p);
+        hipLaunchKernelGGL((attn_fwd_bf16<128, 1, 0>), grid, dim3(Cfg<128, 1>::THREADS), 0, stream,
+                           p);
     else if (d == 128 && nf == 1)
-        hipLaunchKernelGGL((attn_fwd_bf16<128, 1>), grid, dim3(Cfg<128>::THREADS), 0, stream, p);
+        hipLaunchKernelGGL((attn_fwd_bf16<128, 1, 1>), grid, dim3(Cfg<128, 1>::THREADS), 0, stream,
+                           p);
     else if (d == 128 && nf == 2)
-        hipLaunchKernelGGL((attn_fwd_bf16<128, 2>), grid, dim3(Cfg<128>::THREADS), 0, stream, p);
+        hipLaunchKernelGGL((attn_fwd_bf16<128, 1, 2>), grid, dim3(Cfg<128, 1>::THREADS), 0, stream,
+                           p);
     else
         return DFP_ERR_UNSUPPORTED;
     return dfp::launch_status();

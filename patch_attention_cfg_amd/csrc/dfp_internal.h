@@ -7,6 +7,10 @@
 
 size_t dfp_cfg_workspace_bytes(int64_t n_per_image, int batch);
 size_t dfp_attn_workspace_bytes(int B, int H, int n_q, int N_kv, int d);
+// The bf16 launcher's plan for these sizes (attention_bf16.hip): key groups
+// per workgroup, workgroups per query tile, attention workgroups.
+void dfp_attn_bf16_plan(int BH, int n_q, int N_kv, int d, bool can_split, int *key_groups,
+                        int *splits, int64_t *workgroups);
 
 #include "dfp.h"
 

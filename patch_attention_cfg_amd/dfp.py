@@ -33,6 +33,7 @@ SIGNATURES = {
     "dfp_cfg_step_noise": (_I, [_P, _P, _P, _P, _I64, _I, _F, _D, _D, _D, _P, _P, _SZ, _P]),
     "dfp_relmae": (_I, [_P, _P, _I64, _I, _P, _P, _SZ, _P]),
     "dfp_workspace_bytes": (_SZ, [_I, _I64, _I, _I, _I, _I, _I, _I]),
+    "dfp_attention_plan": (_I, [_I, _I, _I, _I, _I, _I, _P, _P, _P]),
     "dfp_ddim_coeffs": (_I, [_D, _D, _P, _P]),
     "dfp_ddim_eta_coeffs": (_I, [_D, _D, _D, _P, _P, _P]),
     "dfp_euler_coeffs": (_I, [_D, _D, _P, _P]),
@@ -124,6 +125,16 @@ def v_ld(N_buf: int, dtype_code: int) -> int:
 def workspace_bytes(op: int, n_per_image: int = 0, batch: int = 0, B: int = 0, H: int = 0,
                     n_q: int = 0, N_kv: int = 0, d: int = 0) -> int:
     return int(lib().dfp_workspace_bytes(op, n_per_image, batch, B, H, n_q, N_kv, d))
+
+
+def attention_plan(B: int, H: int, n_q: int, N_kv: int, d: int, with_workspace: bool = True):
+    """(key_groups, splits, workgroups) of a bf16 attention call of these
+    sizes (dfp_attention_plan; host only)."""
+    ks, sp, wg = ctypes.c_int(), ctypes.c_int(), ctypes.c_int64()
+    _check(lib().dfp_attention_plan(B, H, n_q, N_kv, d, 1 if with_workspace else 0,
+                                    ctypes.byref(ks), ctypes.byref(sp), ctypes.byref(wg)),
+           "dfp_attention_plan")
+    return ks.value, sp.value, wg.value
 
 
 def ddim_coeffs(abar_t: float, abar_prev: float):

@@ -187,6 +187,37 @@ def test_workspace_sizes_grow_with_batch(L):
     assert dfp.workspace_bytes(99) == 0
 
 
+def test_attention_plan(L, monkeypatch):
+    """The bf16 launch plan: two key groups only for d=64 grids far too small
+    to fill the GPU, a key-range split only with a workspace, and the
+    environment overrides honoured."""
+    monkeypatch.delenv("DFP_ATTN_KS", raising=False)
+    monkeypatch.delenv("DFP_ATTN_SPLITS", raising=False)
+    # SDXL-1024 32x32 level: 40 (batch, head) pairs x 256 queries
+    assert dfp.attention_plan(2, 20, 256, 1024, 64) == (2, 1, 160)
+    # SDXL-1024 64x64 level: one key group, key range split across workgroups
+    ks, sp, wg = dfp.attention_plan(2, 10, 1024, 4096, 64)
+    assert ks == 1 and sp > 1 and wg == 160 * sp
+    assert dfp.attention_plan(2, 10, 1024, 4096, 64, with_workspace=False) == (1, 1, 160)
+    # grids that fill the GPU, d=128, a single key tile: one key group
+    assert dfp.attention_plan(2, 10, 2048, 16384, 64)[0] == 1
+    assert dfp.attention_plan(2, 20, 256, 1024, 128)[0] == 1
+    assert dfp.attention_plan(1, 1, 64, 64, 64) == (1, 1, 1)
+    monkeypatch.setenv("DFP_ATTN_KS", "1")
+    assert dfp.attention_plan(2, 20, 256, 1024, 64)[0] == 1
+    monkeypatch.setenv("DFP_ATTN_KS", "2")
+    assert dfp.attention_plan(2, 10, 2048, 16384, 64) == (2, 1, 20 * 32)
+    monkeypatch.delenv("DFP_ATTN_KS")
+    monkeypatch.setenv("DFP_ATTN_SPLITS", "4")
+    assert dfp.attention_plan(2, 20, 256, 1024, 64) == (1, 4, 320)
+    out = ctypes.c_int(7)
+    assert L.dfp_attention_plan(0, 1, 1, 1, 64, 1, ctypes.byref(out), None, None) == \
+        dfp.ERR_INVALID_ARG
+    assert L.dfp_attention_plan(1, 1, 0, 1, 64, 1, None, None, None) == dfp.ERR_INVALID_ARG
+    assert L.dfp_attention_plan(1, 1, 1, 1, 96, 1, None, None, None) == dfp.ERR_UNSUPPORTED
+    assert out.value == 7
+
+
 # ------------------------------------------------- host helpers vs oracle
 def test_schedule_matches_oracle(L):
     ours = dfp.scaled_linear_abar(1000, 0.00085, 0.012)

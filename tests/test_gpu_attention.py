@@ -86,10 +86,20 @@ def test_large_patch_sampled_rows(name, p, per_bh):
     (1, 3, 33, 65, 128),     # d=128 ragged
     (2, 2, 256, 64, 128),    # exactly one key tile
     (1, 1, 64, 1000, 64),    # ragged long key range
+    (1, 2, 40, 150, 64),     # 3 tiles, ragged: an odd step count ends the loop
+    (1, 1, 64, 266, 64),     # 5 tiles, ragged
+    (1, 1, 33, 300, 128),    # 5 tiles, ragged, d=128
 ])
-def test_edge_shapes_every_element(kind, B, H, nq, N, d):
+@pytest.mark.parametrize("ks", [None, "1"])
+def test_edge_shapes_every_element(monkeypatch, kind, B, H, nq, N, d, ks):
+    """Every element at ragged and tiny shapes, with the planner's own choice
+    and with one key group per workgroup forced."""
     G.require_gpu()
-    G.announce(f"attention edge {kind} B{B} H{H} nq{nq} N{N} d{d}")
+    if ks is not None:
+        if kind != "bf16" or d != 64:
+            pytest.skip("key groups are a bf16 d=64 choice")
+        monkeypatch.setenv("DFP_ATTN_KS", ks)
+    G.announce(f"attention edge {kind} B{B} H{H} nq{nq} N{N} d{d} ks{ks}")
     torch = G.torch_mod()
     q, k, v = inputs.random_attention_arrays(B, H, nq, N, d, seed=nq * 7 + N, dtype=kind)
     k_buf, v_buf = dfp.alloc_kv_buffer(B, H, N, d, G.dtype_of(kind))
@@ -225,6 +235,73 @@ def test_fresh_landing_only(d):
     np.testing.assert_array_equal(G.down(k_buf), k_eff)
     np.testing.assert_array_equal(G.v_buffer_to_rows(v_buf, N), v_eff)
     assert torch.isnan(v_buf[..., N:]).all()   # padding columns untouched
+
+
+@pytest.mark.parametrize("B,H,nq,N,d", [
+    (1, 2, 100, 1000, 64),    # 16 tiles (8 + 8), ragged last tile, ragged query tile
+    (2, 1, 64, 960, 64),      # 15 tiles: the second group pads its last step
+    (1, 1, 64, 128, 64),      # 2 tiles: one each
+    (1, 1, 40, 150, 64),      # 3 tiles: 2 + 1 (ragged) + padding step
+    (1, 3, 256, 1024, 64),    # the SDXL 32x32 shape per head group
+    (1, 1, 64, 4100, 64),     # 65 tiles through the four-step loop, ragged
+])
+def test_two_key_groups_every_element(monkeypatch, B, H, nq, N, d):
+    """Two key groups per workgroup (forced): each half of the key range in
+    its own wavefronts and LDS ring, merged through LDS; every element against
+    the oracle, bitwise repeatable, and (fresh call) the same bits as scatter
+    + attention."""
+    G.require_gpu()
+    G.announce(f"attention two key groups B{B} H{H} nq{nq} N{N} d{d}")
+    monkeypatch.setenv("DFP_ATTN_KS", "2")
+    torch = G.torch_mod()
+    q, k, v = inputs.random_attention_arrays(B, H, nq, N, d, seed=nq * 13 + N)
+    k_buf, v_buf = dfp.alloc_kv_buffer(B, H, N, d, torch.bfloat16)
+    v_buf.fill_(float("nan"))   # padding columns past N must not leak in
+    dfp.kv_scatter(k_buf, v_buf, G.up(k, "bf16"), G.up(v, "bf16"), 0)
+    qd = G.up(q, "bf16")
+    o = torch.empty_like(qd)
+    assert dfp.attention_workspace(B, H, nq, N, d) is None   # no split across workgroups
+    dfp.patch_attention(o, qd, k_buf, v_buf)
+    torch.cuda.synchronize()
+    first = G.down(o)
+    _check(first, oracle.attention(q, k, v, 1.0 / d ** 0.5), "bf16", "two key groups")
+    dfp.patch_attention(o, qd, k_buf, v_buf)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(G.down(o), first)
+    if N >= 256:   # the fused call over a fresh range gives the same bits
+        row0, n = 64, 128
+        kf = k_buf[:, :, row0:row0 + n].clone()
+        vtf = v_buf[:, :, :, row0:row0 + n].clone().contiguous()
+        v_before = G.down(v_buf)
+        k_buf[:, :, row0:row0 + n] = float("nan")
+        v_buf[:, :, :, row0:row0 + n] = float("nan")
+        o2 = torch.empty_like(qd)
+        dfp.patch_attention_fresh(o2, qd, k_buf, v_buf, [(kf, vtf, row0)], True)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(G.down(o2), first)
+        np.testing.assert_array_equal(G.down(k_buf), k)
+        np.testing.assert_array_equal(G.down(v_buf), v_before)
+
+
+@pytest.mark.parametrize("growth", [6.0, 40.0])
+def test_two_key_groups_scores_outgrow_first_tile(monkeypatch, growth):
+    """The rare rescale path inside each key group, and a merge of two groups
+    whose references differ widely."""
+    G.require_gpu()
+    G.announce(f"attention two key groups, growing scores x{growth}")
+    monkeypatch.setenv("DFP_ATTN_KS", "2")
+    torch = G.torch_mod()
+    B, H, nq, N, d = 1, 2, 96, 1100, 64
+    q, k, v = inputs.random_attention_arrays(B, H, nq, N, d, seed=int(growth) + 500)
+    ramp = np.linspace(0.0, growth, N, dtype=np.float32)[None, None, :, None]
+    k = inputs.round_bf16(k * (1.0 + ramp) / 4.0)
+    k_buf, v_buf = dfp.alloc_kv_buffer(B, H, N, d, torch.bfloat16)
+    dfp.kv_scatter(k_buf, v_buf, G.up(k, "bf16"), G.up(v, "bf16"), 0)
+    qd = G.up(q, "bf16")
+    o = torch.empty_like(qd)
+    dfp.patch_attention(o, qd, k_buf, v_buf)
+    torch.cuda.synchronize()
+    _check(G.down(o), oracle.attention(q, k, v, 1.0 / d ** 0.5), "bf16", f"grow{growth}")
 
 
 def test_constant_values_and_single_key_properties():
