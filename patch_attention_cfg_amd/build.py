@@ -21,7 +21,13 @@ SOURCES = ["host.cpp", "kv_scatter.hip", "cfg_step.hip", "attention.hip", "atten
 
 ARCH = "gfx950"
 # Packed-FP32 VALU instructions are kept out of the device code on purpose.
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# MFMA results go to ordinary VGPRs: a kernel whose LDS allows one
+# workgroup per CU (the two-key-group attention) otherwise gets a
+# 512-register budget, and the allocator then places MFMA results in AGPRs
+# and copies them to VGPRs for the softmax every step (about 100 extra
+# moves per step).  Kernels that fit 256 registers compile identically.
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                "-mllvm", "-amdgpu-mfma-vgpr-form=1"]
 CFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
           "-Wall", "-Wno-unused-command-line-argument"] + DEVICE_FLAGS
 

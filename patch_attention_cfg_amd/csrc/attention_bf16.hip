@@ -908,8 +908,8 @@ __global__ __launch_bounds__((Cfg<D, KS>::THREADS), (Cfg<D, KS>::WG_PER_CU)) voi
 
     // Prologue: K(t0..t0+2) and V(t0) landed, V "tile t0-1" (stage 3)
     // zeroed, since the first step's P.V uses zero probabilities against
-    // it; S(t0) and the reference max; the first step's first operands;
-    // K(t0+3) and V(t0+1) in flight (the loop's entry state).
+    // it; K(t0+3) and V(t0+1) in flight (the loop's entry state) while S(t0),
+    // the reference max and the first step's first operands are computed.
     TileDma<D, KS> dma;
     dma.init(wave, lane, p.ldv, x.f_n[0], x.f_n[1]);
     OperandOffsets<D, KS> oo;
@@ -934,6 +934,24 @@ __global__ __launch_bounds__((Cfg<D, KS>::THREADS), (Cfg<D, KS>::WG_PER_CU)) voi
         reinterpret_cast<uint4 *>(sm.v[3] + x.goff)[e] = zero4();
     wait_dma_all();
     __syncthreads();
+    // K(t0+3), V(t0+1) go out now, before S(t0) (stages K3 and V1 are
+    // untouched by the prologue), at d=64; at d=128, whose registers are
+    // full, their copy job would stay live across S(t0) and spill inside
+    // the main loop, so they go out after it.
+    auto copy_k3_v1 = [&]() {
+        const CopyJob j3 = copy_job<D, KS, NF>(x, dma, t0 + 3, t0 + 1, lds_addr(sm.k[3]) + x.goff,
+                                               lds_addr(sm.v[1]) + x.goff);
+#pragma unroll
+        for (int e = 0; e < C::DMA_W; ++e) issue_copy<D, KS>(dma, j3, e);
+    };
+    if constexpr (D == 64) {
+        // The compiler does not count the copies: its wait for Q's loads (an
+        // in-order counter) must come before this copy, or it would hold the
+        // first product until the copy lands.  An empty use here places it.
+#pragma unroll
+        for (int kc = 0; kc < C::KC; ++kc) asm volatile("" ::"v"(qreg[kc]));
+        copy_k3_v1();
+    }
     if (t0 * BN + BN > x.key_end)   // lone ragged tile
         zero_tail_v<D, KS>(sm.v[0] + x.goff, t0 * BN, x.key_end, tid_g);
 
@@ -964,12 +982,7 @@ __global__ __launch_bounds__((Cfg<D, KS>::THREADS), (Cfg<D, KS>::WG_PER_CU)) voi
             for (int j = 0; j < 8; ++j) pB[sb][h][j] = (__bf16)0.0f;
     bf16x8_t carry[2] = {step_operand<D, KS>(0, sm.k[1], sm.v[0], oo),
                          step_operand<D, KS>(1, sm.k[1], sm.v[0], oo)};
-    {
-        const CopyJob j3 = copy_job<D, KS, NF>(x, dma, t0 + 3, t0 + 1, lds_addr(sm.k[3]) + x.goff,
-                                               lds_addr(sm.v[1]) + x.goff);
-#pragma unroll
-        for (int e = 0; e < C::DMA_W; ++e) issue_copy<D, KS>(dma, j3, e);   // K(t0+3), V(t0+1)
-    }
+    if constexpr (D != 64) copy_k3_v1();
     __syncthreads();   // stage 0 of K is free; V(t0)'s zeroed tail is visible
 
     // Two register sets alternate roles from step to step, so the loop runs
@@ -1243,7 +1256,6 @@ Plan make_plan(int BH, int n_q, int N_kv, int d, bool can_split) {
     pl.ntiles = (N_kv + bn - 1) / bn;
     pl.splits = 1;
     pl.tiles_per_split = pl.ntiles;
-    if (!can_split) return pl;
     const int per_cu = d == 64 ? Cfg<64, 1>::WG_PER_CU : Cfg<128, 1>::WG_PER_CU;
     const double t_alone = d == 64 ? 0.62e-6 : 1.7e-6;   // s per step, CU to itself
     const double t_shared = 1.09e-6;                     // s per step, two per CU (d=64)
@@ -1254,7 +1266,7 @@ Plan make_plan(int BH, int n_q, int N_kv, int d, bool can_split) {
     double best = 1e300;
     const char *env = std::getenv("DFP_ATTN_SPLITS");
     const int forced = env ? std::atoi(env) : 0;
-    for (int s = 1; s <= kMaxSplits && s <= pl.ntiles; ++s) {
+    for (int s = 1; s <= (can_split ? kMaxSplits : 1) && s <= pl.ntiles; ++s) {
         const int tps = (pl.ntiles + s - 1) / s;
         const int s_eff = (pl.ntiles + tps - 1) / tps;
         if (s_eff != s) continue;
@@ -1270,7 +1282,7 @@ Plan make_plan(int BH, int n_q, int N_kv, int d, bool can_split) {
         }
         t += t_fixed;
         if (s > 1) t += t_handoff + 2.0 * wgs * pl.block_m * d * 4.0 / merge_bw;
-        if (forced > 0 ? s == forced : t < best * 0.98) {
+        if (s == 1 || (forced > 0 ? s == forced : t < best * 0.98)) {
             best = t;
             pl.splits = s;
             pl.tiles_per_split = tps;

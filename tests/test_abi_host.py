@@ -195,6 +195,8 @@ def test_attention_plan(L, monkeypatch):
     monkeypatch.delenv("DFP_ATTN_SPLITS", raising=False)
     # SDXL-1024 32x32 level: 40 (batch, head) pairs x 256 queries
     assert dfp.attention_plan(2, 20, 256, 1024, 64) == (2, 1, 160)
+    # two key groups need no workspace
+    assert dfp.attention_plan(2, 20, 256, 1024, 64, with_workspace=False) == (2, 1, 160)
     # SDXL-1024 64x64 level: one key group, key range split across workgroups
     ks, sp, wg = dfp.attention_plan(2, 10, 1024, 4096, 64)
     assert ks == 1 and sp > 1 and wg == 160 * sp
