@@ -160,6 +160,12 @@ def test_forced_split_kv_every_element(monkeypatch, splits, B, H, nq, N, d):
     (1, 2, 200, 1344, 64, [(768, 512), (0, 256)], 3),    # the same, listed the other way
     (1, 2, 200, 1344, 64, [(0, 256), (256, 512)], 0),    # adjacent ranges
     (1, 2, 300, 1300, 128, [(0, 256), (768, 256)], 2),   # d=128, ragged last tile
+    # two key groups per workgroup (forced)
+    (1, 2, 200, 1000, 64, [(256, 512)], "ks2"),          # ragged last tile
+    (1, 2, 300, 1024, 64, [(64, 768)], "ks2"),           # the range spans both groups
+    (1, 2, 200, 1344, 64, [(0, 256), (768, 512)], "ks2"),   # two ranges
+    (1, 1, 64, 192, 64, [(128, 64)], "ks2"),             # 3 tiles: fresh tile + padding step
+    (2, 1, 130, 1024, 64, [(768, 256)], "ks2"),          # fresh rows last
 ])
 def test_fresh_rows_every_element(monkeypatch, B, H, nq, N, d, ranges, splits, land):
     """dfp_patch_attention_fresh with one or two fresh ranges: the buffer's
@@ -170,9 +176,13 @@ def test_fresh_rows_every_element(monkeypatch, B, H, nq, N, d, ranges, splits, l
     G.require_gpu()
     G.announce(f"attention fresh rows land={land} B{B} H{H} nq{nq} N{N} d{d} "
                f"ranges={ranges} splits={splits}")
-    if splits:
+    if splits == "ks2":
+        monkeypatch.setenv("DFP_ATTN_KS", "2")
+    elif splits:
         monkeypatch.setenv("DFP_ATTN_SPLITS", str(splits))
     torch = G.torch_mod()
+    if splits == "ks2":
+        assert dfp.attention_plan(B, H, nq, N, d)[0] == 2
     seed = N + d + sum(r0 + n for r0, n in ranges)
     q, k_st, v_st = inputs.random_attention_arrays(B, H, nq, N, d, seed=seed)
     k_buf, v_buf = dfp.alloc_kv_buffer(B, H, N, d, torch.bfloat16)
