@@ -62,6 +62,8 @@ def _load():
         "oracle_euler_step": (None, [D, D, i64, dbl, dbl]),
         "oracle_relmae": (dbl, [D, D, i64]),
         "oracle_num_threads": (cint, []),
+        "oracle_displaced_group_norm": (None, [D, D, D, D, i64, i64, i64, i64, i64, i64, dbl,
+                                               D, D]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
@@ -327,3 +329,33 @@ def switch_points(relmae_series, L: int, g_slope: float, k: int = 5):
                                     _pi(t2)) != 0:
         raise ValueError("need a non-empty series and L >= 1")
     return int(t1[0]), int(t2[0])
+
+
+# --------------------------------------------------------------------------
+# Displaced GroupNorm ([DT] corrected_async_gn; reading in dfp_oracle.c)
+# --------------------------------------------------------------------------
+def displaced_group_norm(x, stats, G: int, p: int, eps: float, gamma=None, beta=None):
+    """GroupNorm of one patch x [B, C, n] whose statistics combine the other
+    patches' previous-step sums stats [B, G, P, 2] with this patch's fresh
+    ones.  Returns (y [B, C, n], fresh sums [B, G, 2])."""
+    x = _f64(x)
+    stats = _f64(stats)
+    B, C, n = x.shape
+    if C % G != 0:
+        raise ValueError("C must be a multiple of G")
+    if stats.shape[:2] != (B, G) or stats.shape[3] != 2:
+        raise ValueError("stats must be [B, G, P, 2]")
+    P = stats.shape[2]
+    if not 0 <= p < P:
+        raise ValueError("patch index out of range")
+    ga = None if gamma is None else _f64(gamma)
+    be = None if beta is None else _f64(beta)
+    for a in (ga, be):
+        if a is not None and a.shape != (C,):
+            raise ValueError("gamma and beta must be [C]")
+    y = np.empty_like(x)
+    fresh = np.empty((B, G, 2), dtype=np.float64)
+    _load().oracle_displaced_group_norm(_pd(x), _pd(stats), None if ga is None else _pd(ga),
+                                        None if be is None else _pd(be), B, C, G, n, P, p,
+                                        float(eps), _pd(y), _pd(fresh))
+    return y, fresh

@@ -22,13 +22,22 @@
  *         below) and 损失函数/训练策略 (flow matching: swap eps for v).
  *   [AI]  "AIGC 文生图系统如何优化扩散模型推理速度", section 1 (x_T drawn
  *         from N(0,1)) and section 3 (DDIM with eta; eta = 0 deterministic).
+ *   [DT]  "DistriFusion高级教程：自定义并行配置实现超高清图像生成的完整指南",
+ *         sections 多设备配置优化 and 速度与质量平衡: a communication mode
+ *         named corrected_async_gn (an asynchronous GroupNorm with a
+ *         correction), given by name only.
  *
  * Readings taken where the pages are silent:
  *   - attention is plain softmax(Q K^T * scale) V with no mask or bias;
  *   - the CFG combine is g = g_u + w (g_c - g_u)  (not printed on [XD]/[HY]);
  *   - DDIM's undefined sigma_t in x0_hat is sqrt(1 - abar_t);
  *   - "scaled linear" betas are linear in sqrt(beta);
- *   - the flow sampler is plain Euler on sigma_i = 1 - i/S.
+ *   - the flow sampler is plain Euler on sigma_i = 1 - i/S;
+ *   - corrected_async_gn: GroupNorm whose per-group statistics come from
+ *     every other patch's partial sums of the previous step (stale, as [DF]
+ *     reuses activations) plus this patch's own sums of this step (fresh:
+ *     the correction), over equal-size patches; statistics are the plain
+ *     mean and biased variance of the group, eps inside the square root.
  */
 #include <math.h>
 #include <stdint.h>
@@ -336,4 +345,56 @@ int oracle_switch_points(const double *M, int64_t S, int64_t L, double g_slope, 
     *tau1 = t1;
     *tau2 = t2;
     return 0;
+}
+
+
+/* ------------------------------------------------------------------------ */
+/* Displaced GroupNorm of one patch ([DT] corrected_async_gn, with the        */
+/* reading in the header; [DF] 革命性突破 for stale reuse).                   */
+/* x:      [B][C][n]  this patch's activations, this step (fresh).           */
+/* stats:  [B][G][P][2] per-patch (sum, sum of squares) of the previous step. */
+/* gamma, beta: [C] affine parameters, or NULL for none.                      */
+/* For each (b, g), with the group's channels c in [g C/G, (g+1) C/G):        */
+/*   f1 = sum_{c, i} x[b,c,i],  f2 = sum_{c, i} x[b,c,i]^2   (fresh, local)    */
+/*   S1 = f1 + sum_{q != p} stats[b,g,q,0],  S2 = f2 + sum_{q != p} stats[..,1]*/
+/*   N  = P * n * C/G;  mean = S1 / N;  var = S2 / N - mean^2                 */
+/*   y[b,c,i] = (x[b,c,i] - mean) / sqrt(var + eps) * gamma[c] + beta[c]      */
+/* fresh_out: [B][G][2] receives (f1, f2), this patch's sums for the next     */
+/* step.                                                                      */
+/* ------------------------------------------------------------------------ */
+void oracle_displaced_group_norm(const double *x, const double *stats, const double *gamma,
+                                 const double *beta, int64_t B, int64_t C, int64_t G,
+                                 int64_t n, int64_t P, int64_t p, double eps, double *y,
+                                 double *fresh_out)
+{
+    const int64_t cg = C / G;
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t g = 0; g < G; ++g) {
+            double f1 = 0.0, f2 = 0.0;
+            for (int64_t c = g * cg; c < (g + 1) * cg; ++c)
+                for (int64_t i = 0; i < n; ++i) {
+                    const double v = x[(b * C + c) * n + i];
+                    f1 += v;
+                    f2 += v * v;
+                }
+            double s1 = f1, s2 = f2;
+            for (int64_t q = 0; q < P; ++q)
+                if (q != p) {
+                    s1 += stats[((b * G + g) * P + q) * 2];
+                    s2 += stats[((b * G + g) * P + q) * 2 + 1];
+                }
+            const double N = (double)(P * n * cg);
+            const double mean = s1 / N;
+            const double var = s2 / N - mean * mean;
+            const double rstd = 1.0 / sqrt(var + eps);
+            for (int64_t c = g * cg; c < (g + 1) * cg; ++c) {
+                const double ga = gamma ? gamma[c] : 1.0, be = beta ? beta[c] : 0.0;
+                for (int64_t i = 0; i < n; ++i) {
+                    const int64_t k = (b * C + c) * n + i;
+                    y[k] = (x[k] - mean) * rstd * ga + be;
+                }
+            }
+            fresh_out[(b * G + g) * 2] = f1;
+            fresh_out[(b * G + g) * 2 + 1] = f2;
+        }
 }
