@@ -357,6 +357,27 @@ def main():
                         "frac_hbm_peak": sampler.bytes / (mean * 1e-6) / 1e9 / PEAK_HBM_GBPS,
                         "bytes": sampler.bytes}
 
+    # displaced GroupNorm (the corrected_async_gn mode) on the workload's
+    # first U-Net level: 320 channels in 32 groups over the latent grid, one
+    # patch's row band; a DiT has no GroupNorm
+    if wl.name.startswith("sdxl") or wl.name == "tiny-f32":
+        _, _, hl, wdl = wl.latent
+        pg = wl.levels[0].P
+        gi = inputs.group_norm_inputs(2, 320, 32, (hl // pg) * wdl, pg, 1, wl.seed + 300)
+        gx = torch.from_numpy(gi.x).cuda()
+        gy = torch.empty_like(gx)
+        gst = torch.from_numpy(gi.stats).cuda()
+        gga, gbe = torch.from_numpy(gi.gamma).cuda(), torch.from_numpy(gi.beta).cuda()
+        gws = dfp.group_norm_workspace(2, 320, 32, (hl // pg) * wdl)
+        mean, mn = time_kernel(torch, lambda: dfp.displaced_group_norm(
+            gy, gx, gst, 32, 1, 1e-5, gga, gbe, True, gws), reps)
+        gb = 8 * gx.numel()   # x read, y written; the per-group sums are 0.02%
+        kern["displaced_group_norm"] = {
+            "us_mean": mean, "us_min": mn, "gbps": gb / (mean * 1e-6) / 1e9,
+            "frac_hbm_peak": gb / (mean * 1e-6) / 1e9 / PEAK_HBM_GBPS, "bytes": gb,
+            "shape": f"x [2, 320, {(hl // pg) * wdl}] (patch 1 of {pg}), 32 groups"}
+        del gx, gy, gst, gws
+
     # the same fused step streaming a batch of 32 latents in one call: the
     # kernel's bandwidth once the per-call latency (launch, reduction tail)
     # is amortised

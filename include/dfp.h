@@ -249,6 +249,51 @@ dfp_status dfp_relmae(const float *g_c, const float *g_u, int64_t n_per_image,
                       int batch, float *out, void *workspace, size_t ws_bytes,
                       hipStream_t stream);
 
+/* (f4) Displaced GroupNorm of one patch: the corrected_async_gn mode that
+ * [DT] 多设备配置优化 names (an asynchronous GroupNorm with a correction;
+ * the page gives only the name).  Reading, after [DF] 革命性突破's reuse of
+ * the previous step's activations: each group's statistics sum every other
+ * patch's partial sums from the previous step (stale) and this patch's own
+ * sums from this step (fresh, the correction); all P patches have n
+ * positions.  Per image b and group g (channels g*C/G .. (g+1)*C/G - 1):
+ *   f1 = sum x, f2 = sum x^2 over the patch's group   (fp64)
+ *   S1 = f1 + sum_{q != p} stats[b][g][q][0],  S2 likewise with [1]
+ *   N = P * n * C/G,  mean = S1/N,  var = S2/N - mean^2 (biased)
+ *   y = (x - mean) / sqrt(var + eps) * gamma[c] + beta[c]
+ *
+ *   y      [B][C][n]     fp32 output; may equal x (in place), must not
+ *                        otherwise overlap it.
+ *   x      [B][C][n]     fp32, this patch's activations (NCHW with the
+ *                        patch's rows contiguous: n = rows * width).
+ *   stats  [B][G][P][2]  fp64 device buffer, 8-byte aligned: each patch's
+ *                        (sum, sum of squares) of the previous step.  Slot
+ *                        p is ignored on input; with land != 0 it receives
+ *                        (f1, f2) for the next step.
+ *   gamma, beta  [C] fp32, or NULL (1 and 0).
+ *   workspace/ws_bytes  optional device scratch (may be NULL/0), 256-byte
+ *           aligned.  Groups of up to 64 Ki floats of the patch (C/G * n)
+ *           need none.  For longer groups, with at least
+ *           dfp_group_norm_workspace_bytes(B, C, G, n) bytes the work is
+ *           spread over the whole GPU in two launches; without it one
+ *           workgroup per (image, group) does it.  The workspace starts
+ *           with one arrival counter per (image, group) that must be zero
+ *           before the first call (allocate it zeroed); every call leaves
+ *           them zero.  Calls that share a workspace must not run
+ *           concurrently.
+ * The statistics are bitwise reproducible (fixed-order fp64 sums).
+ * Errors: INVALID_ARG for null y/x/stats, non-positive B/C/G/n/P, C not a
+ * multiple of G, p outside [0, P), negative or non-finite eps, misaligned
+ * stats, y partially overlapping x; UNSUPPORTED for B > 65535. */
+dfp_status dfp_displaced_group_norm(float *y, const float *x, double *stats,
+                                    const float *gamma, const float *beta, int B,
+                                    int C, int G, int64_t n, int P, int p,
+                                    float eps, int land, void *workspace,
+                                    size_t ws_bytes, hipStream_t stream);
+
+/* Workspace bytes dfp_displaced_group_norm uses for these sizes to spread
+ * long groups over the GPU (0: none needed, or invalid sizes). */
+size_t dfp_group_norm_workspace_bytes(int B, int C, int G, int64_t n);
+
 /* Device scratch, in bytes, that `op` needs for the given sizes.  Arguments
  * that do not apply to `op` are ignored.  Returns 0 if the op needs none. */
 size_t dfp_workspace_bytes(int op, int64_t n_per_image, int batch, int B, int H,

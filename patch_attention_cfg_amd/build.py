@@ -17,7 +17,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdfp.so")
 
-SOURCES = ["host.cpp", "kv_scatter.hip", "cfg_step.hip", "attention.hip", "attention_bf16.hip"]
+SOURCES = ["host.cpp", "kv_scatter.hip", "cfg_step.hip", "attention.hip", "attention_bf16.hip",
+           "group_norm.hip"]
 
 ARCH = "gfx950"
 # Packed-FP32 VALU instructions are kept out of the device code on purpose.

@@ -34,6 +34,9 @@ SIGNATURES = {
     "dfp_relmae": (_I, [_P, _P, _I64, _I, _P, _P, _SZ, _P]),
     "dfp_workspace_bytes": (_SZ, [_I, _I64, _I, _I, _I, _I, _I, _I]),
     "dfp_attention_plan": (_I, [_I, _I, _I, _I, _I, _I, _P, _P, _P]),
+    "dfp_displaced_group_norm": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I64, _I, _I, _F, _I,
+                                      _P, _SZ, _P]),
+    "dfp_group_norm_workspace_bytes": (_SZ, [_I, _I, _I, _I64]),
     "dfp_ddim_coeffs": (_I, [_D, _D, _P, _P]),
     "dfp_ddim_eta_coeffs": (_I, [_D, _D, _D, _P, _P, _P]),
     "dfp_euler_coeffs": (_I, [_D, _D, _P, _P]),
@@ -255,6 +258,33 @@ def patch_attention_fresh(o, q, k_buf, v_buf_t, fresh, land: bool = True,
                                          n_q, N_kv, d, 1 if land else 0, float(scale),
                                          _dtype_code(q), ws_ptr, ws_bytes, _stream(stream))
     _check(st, "dfp_patch_attention_fresh")
+
+
+def displaced_group_norm(y, x, stats, G: int, p: int, eps: float = 1e-5, gamma=None,
+                         beta=None, land: bool = True, workspace=None, stream=None) -> None:
+    """dfp_displaced_group_norm: y [B,C,n] = GroupNorm of the patch x [B,C,n]
+    with statistics from the other patches' previous-step sums in stats
+    [B,G,P,2] (float64) and this patch's fresh sums, which land in slot p."""
+    B, C, n = x.shape
+    P = stats.shape[2]
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib().dfp_displaced_group_norm(_ptr(y), _ptr(x), _ptr(stats),
+                                        _ptr(gamma) if gamma is not None else None,
+                                        _ptr(beta) if beta is not None else None, B, C, G, n,
+                                        P, p, float(eps), 1 if land else 0,
+                                        _ptr(workspace) if workspace is not None else None,
+                                        ws_bytes, _stream(stream))
+    _check(st, "dfp_displaced_group_norm")
+
+
+def group_norm_workspace(B: int, C: int, G: int, n: int, device="cuda"):
+    """A zero-filled workspace for dfp_displaced_group_norm (None when the
+    sizes need none)."""
+    torch = _torch()
+    nbytes = int(lib().dfp_group_norm_workspace_bytes(B, C, G, n))
+    if nbytes == 0:
+        return None
+    return torch.zeros(nbytes, dtype=torch.uint8, device=device)
 
 
 def attention_workspace(B: int, H: int, n_q: int, N_kv: int, d: int, device="cuda"):

@@ -31,6 +31,18 @@ Sampler stream (seed + 200): x_T [1,C,H,W], then per step g_c and g_u;
 sampler noise z for DDIM with eta > 0 comes from its own stream (seed + 300).
 Seeds: per workload (1001 ... 1005 in the order above); a workload's second
 attention level adds 100.
+
+Displaced GroupNorm (the corrected_async_gn mode), one patch of a U-Net
+feature map [B, C, H, W] cut into P row bands, n = (H/P) * W:
+  x      [B,C,n]    per-channel N(mu_c, sigma_c), mu_c ~ N(0, 0.5),
+                    sigma_c ~ U(0.5, 2) (activations differ per channel)
+  stats  [B,G,P,2]  each other patch's (sum, sum of squares) of the previous
+                    step, from drawn per-(image, group, patch) moments
+                    m ~ N(0, 0.5), s ~ U(0.5, 2): (cnt m, cnt (s^2 + m^2)),
+                    cnt = (C/G) n; the patch's own slot holds NaN (unused)
+  gamma  [C] 1 + 0.1 N(0,1);  beta [C] 0.1 N(0,1)
+SDXL-1024's first U-Net level stands in for the workload: C=320, G=32,
+128x128, P=4, B=2.
 """
 from __future__ import annotations
 
@@ -225,3 +237,29 @@ def sampler_stream(workload: Workload, seed: int | None = None) -> SamplerStream
     rng = np.random.Generator(np.random.PCG64(s))
     x_T = rng.standard_normal(workload.latent, dtype=np.float32)
     return SamplerStream(workload, rng, x_T, np.random.Generator(np.random.PCG64(s + 100)))
+
+
+@dataclass(frozen=True)
+class GroupNormInputs:
+    x: np.ndarray       # [B, C, n] float32
+    stats: np.ndarray   # [B, G, P, 2] float64
+    gamma: np.ndarray   # [C] float32
+    beta: np.ndarray    # [C] float32
+
+
+def group_norm_inputs(B: int, C: int, G: int, n: int, P: int, p: int,
+                      seed: int) -> GroupNormInputs:
+    """Seeded inputs of one displaced GroupNorm call (recipe in the module
+    docstring)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    mu = rng.normal(0.0, 0.5, size=(B, C, 1)).astype(np.float32)
+    sd = rng.uniform(0.5, 2.0, size=(B, C, 1)).astype(np.float32)
+    x = (rng.standard_normal((B, C, n), dtype=np.float32) * sd + mu).astype(np.float32)
+    cnt = float((C // G) * n)
+    m = rng.normal(0.0, 0.5, size=(B, G, P))
+    s = rng.uniform(0.5, 2.0, size=(B, G, P))
+    stats = np.stack([cnt * m, cnt * (s * s + m * m)], axis=-1)
+    stats[:, :, p, :] = np.nan
+    gamma = (1.0 + 0.1 * rng.standard_normal(C)).astype(np.float32)
+    beta = (0.1 * rng.standard_normal(C)).astype(np.float32)
+    return GroupNormInputs(x, stats, gamma, beta)

@@ -187,6 +187,42 @@ def test_workspace_sizes_grow_with_batch(L):
     assert dfp.workspace_bytes(99) == 0
 
 
+def test_group_norm_validation(L):
+    """dfp_displaced_group_norm rejects bad arguments before any launch."""
+    X = ctypes.c_void_p(0x200000)
+    Y = ctypes.c_void_p(0x400000)
+    ST = ctypes.c_void_p(0x600000)
+    f = L.dfp_displaced_group_norm
+
+    def call(y=Y, x=X, st=ST, B=2, C=8, G=4, n=16, P=3, p=1, eps=1e-5):
+        return f(y, x, st, NULL, NULL, B, C, G, n, P, p, eps, 1, NULL, 0, S0)
+
+    E = dfp.ERR_INVALID_ARG
+    assert call(y=NULL) == E
+    assert call(x=NULL) == E
+    assert call(st=NULL) == E
+    assert call(st=ctypes.c_void_p(0x600004)) == E     # stats not 8-byte aligned
+    assert call(y=ctypes.c_void_p(0x200004)) == E      # y partly overlaps x
+    assert call(C=10) == E                             # C not a multiple of G
+    assert call(G=0) == E
+    assert call(B=0) == E
+    assert call(n=0) == E
+    assert call(P=0) == E
+    assert call(p=3) == E
+    assert call(p=-1) == E
+    assert call(eps=-1.0) == E
+    assert call(eps=float("nan")) == E
+    assert call(eps=float("inf")) == E
+    assert call(B=65536) == dfp.ERR_UNSUPPORTED
+    # groups of up to 64 Ki floats need no workspace; longer ones one counter
+    # per group (256-byte padded), fp64 sums per 16 Ki-float chunk, (mean, rstd)
+    ws = L.dfp_group_norm_workspace_bytes
+    assert ws(2, 320, 32, 4096) == 0               # 40 Ki floats per group
+    assert ws(2, 320, 32, 28800) == 256 + 64 * 18 * 16 + 64 * 8
+    assert ws(2, 320, 30, 28800) == 0              # C not a multiple of G
+    assert ws(0, 320, 32, 28800) == 0
+
+
 def test_attention_plan(L, monkeypatch):
     """The bf16 launch plan: two key groups only for d=64 grids far too small
     to fill the GPU, a key-range split only with a workspace, and the
