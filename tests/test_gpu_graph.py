@@ -83,3 +83,51 @@ def test_graph_replays_match_eager(monkeypatch):
         dfp.patch_attention(other, qd, k_buf, v_buf, None, ws)
         torch.cuda.synchronize()
         np.testing.assert_array_equal(G.down(other), want_o)
+
+
+def test_group_norm_graph_replays_match_eager():
+    """The chunked displaced GroupNorm (two launches, published chunk sums,
+    last-arrival statistics) captured in a HIP graph: every replay gives the
+    eager call's bits, lands the same sums and leaves the counters at zero,
+    with an eager call on the same workspace between replays."""
+    G.require_gpu()
+    G.announce("graph replay: chunked displaced GroupNorm, 4 replays")
+    torch = G.torch_mod()
+    B, C, G_, n, P, p = 2, 64, 4, 8192, 4, 2        # groups of 128 Ki floats: chunked
+    a = inputs.group_norm_inputs(B, C, G_, n, P, p, seed=44)
+    x = torch.from_numpy(a.x).cuda()
+    ga, be = torch.from_numpy(a.gamma).cuda(), torch.from_numpy(a.beta).cuda()
+    ws = dfp.group_norm_workspace(B, C, G_, n)
+    assert ws is not None
+
+    st_e = torch.from_numpy(a.stats).cuda()
+    y_e = torch.empty_like(x)
+    dfp.displaced_group_norm(y_e, x, st_e, G_, p, 1e-5, ga, be, True, ws)
+    torch.cuda.synchronize()
+    want_y, want_st = G.down(y_e), st_e.cpu().numpy()
+
+    st_g = torch.from_numpy(a.stats).cuda()
+    y_g = torch.empty_like(x)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):            # warm-up outside capture
+        dfp.displaced_group_norm(y_g, x, st_g, G_, p, 1e-5, ga, be, True, ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        dfp.displaced_group_norm(y_g, x, st_g, G_, p, 1e-5, ga, be, True, ws)
+    torch.cuda.synchronize()
+
+    other = torch.empty_like(x)
+    for i in range(4):
+        y_g.zero_()
+        st_g.copy_(torch.from_numpy(a.stats))
+        graph.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(G.down(y_g), want_y, err_msg=f"replay {i} output")
+        np.testing.assert_array_equal(st_g.cpu().numpy(), want_st, err_msg=f"replay {i} sums")
+        assert int(ws[:B * G_ * 4].sum().item()) == 0
+        dfp.displaced_group_norm(other, x, st_e, G_, p, 1e-5, ga, be, True, ws)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(G.down(other), want_y)
