@@ -1167,10 +1167,32 @@ __global__ __launch_bounds__((Cfg<D, KS>::THREADS), (Cfg<D, KS>::WG_PER_CU)) voi
     if (!s_last) return;
 
     // merge: O = sum_s w_s O_s with w_s = 2^(m_s - m*) / sum_s' 2^(m_s' - m*) l_s',
-    // in split order.  Row weights first (into LDS, reusing the K ring),
-    // then every thread streams its 16-byte groups, one batch of loads per
-    // split in flight together.
+    // in split order.  Row weights into LDS (reusing the K ring); every
+    // thread streams its 16-byte groups, one batch of loads per split in
+    // flight together.
     const int64_t base = (int64_t)qtile_id * p.splits;
+    constexpr int G = MergeCfg<D, KS>::G;
+    constexpr int NS = MergeCfg<D, KS>::NS;
+    const float *part0 = p.part_o + base * C::BLOCK_M * D;
+    // With at most NS splits every partial's loads go out before the row
+    // weights' loads, so the two round trips overlap (same arithmetic).
+    // d=64 only: at d=128 the registers are needed elsewhere.
+    const bool early = D == 64 && p.splits <= NS;
+    f32x4_t pre[NS][G];
+    if (early) {
+#pragma unroll
+        for (int j = 0; j < NS; ++j)
+            if (j < p.splits) {
+                const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+                    const_cast<float *>(part0) + (int64_t)j * C::BLOCK_M * D, 0,
+                    C::BLOCK_M * D * 4, 0x00020000);
+#pragma unroll
+                for (int k = 0; k < G; ++k)
+                    pre[j][k] = __builtin_bit_cast(
+                        f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                     ro, (tid + k * C::THREADS) * 16, 0, kCoherent));
+            }
+    }
     float *wts = reinterpret_cast<float *>(sm.k[0]);   // [BLOCK_M][kMaxSplits]
     static_assert(C::BLOCK_M * kMaxSplits * 4 <= C::K_TILE, "row weights fit one K stage");
     if (tid < C::BLOCK_M) {
@@ -1200,13 +1222,20 @@ __global__ __launch_bounds__((Cfg<D, KS>::THREADS), (Cfg<D, KS>::WG_PER_CU)) voi
             if (s < p.splits) wts[tid * kMaxSplits + s] = ms[s] * inv;
     }
     __syncthreads();
-    constexpr int G = MergeCfg<D, KS>::G;
-    constexpr int NS = MergeCfg<D, KS>::NS;
     f32x4_t acc[G];
 #pragma unroll
     for (int k = 0; k < G; ++k) acc[k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    const float *part0 = p.part_o + base * C::BLOCK_M * D;
-    for (int s0 = 0; s0 < p.splits; s0 += NS) {
+    if (early) {
+#pragma unroll
+        for (int j = 0; j < NS; ++j)
+            if (j < p.splits)
+#pragma unroll
+                for (int k = 0; k < G; ++k) {
+                    const int rr = (tid + k * C::THREADS) * 4 / D;
+                    acc[k] += wts[rr * kMaxSplits + j] * pre[j][k];
+                }
+    }
+    for (int s0 = early ? p.splits : 0; s0 < p.splits; s0 += NS) {
         switch (min(NS, p.splits - s0)) {
             case 1: merge_pass<D, KS, 1>(acc, part0, wts, s0, tid); break;
             case 2: merge_pass<D, KS, (NS >= 2 ? 2 : 1)>(acc, part0, wts, s0, tid); break;
