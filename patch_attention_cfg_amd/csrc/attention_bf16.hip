@@ -1289,7 +1289,10 @@ Plan make_plan(int BH, int n_q, int N_kv, int d, bool can_split) {
     const double t_alone = d == 64 ? 0.62e-6 : 1.7e-6;   // s per step, CU to itself
     const double t_shared = 1.09e-6;                     // s per step, two per CU (d=64)
     const double t_fixed = 3e-6;                         // prologue + epilogue
-    const double t_handoff = 3e-6;                       // publish, arrive, row weights
+    // publish, arrive and row weights, then one memory round trip per batch
+    // of partials the merge loads together (measured: 3 splits ~3.5 us,
+    // 8 splits ~6.5 us at d=64)
+    const int merge_batch = d == 64 ? MergeCfg<64, 1>::NS : MergeCfg<128, 1>::NS;
     const double merge_bw = 5e12;                        // partial bytes/s, written and read
     const double base = (double)BH * pl.q_tiles;
     double best = 1e300;
@@ -1310,7 +1313,9 @@ Plan make_plan(int BH, int n_q, int N_kv, int d, bool can_split) {
                 (rem <= 0 ? 0.0 : tps * (rem <= kCus ? t_alone : t_shared));
         }
         t += t_fixed;
-        if (s > 1) t += t_handoff + 2.0 * wgs * pl.block_m * d * 4.0 / merge_bw;
+        if (s > 1)
+            t += 2e-6 + std::ceil((double)s / merge_batch) * 1.5e-6 +
+                 2.0 * wgs * pl.block_m * d * 4.0 / merge_bw;
         if (s == 1 || (forced > 0 ? s == forced : t < best * 0.98)) {
             best = t;
             pl.splits = s;
@@ -1323,7 +1328,11 @@ Plan make_plan(int BH, int n_q, int N_kv, int d, bool can_split) {
     if (d == 64 && pl.ntiles >= 2 && forced <= 1 && forced_ks != 1) {
         const int q_tiles2 = (n_q + Cfg<64, 2>::BLOCK_M - 1) / Cfg<64, 2>::BLOCK_M;
         const double wgs2 = (double)BH * q_tiles2;   // one workgroup per CU
-        const double t2 = std::ceil(wgs2 / kCus) * ((pl.ntiles + 1) / 2) * t_alone + t_fixed +
+        // measured step times of this variant: 0.65 us in unrolled trips,
+        // 0.80 us in short loops (run-time stages)
+        const int steps2 = (pl.ntiles + 1) / 2;
+        const double t_step2 = steps2 >= kStaticMinSteps ? 0.65e-6 : 0.80e-6;
+        const double t2 = std::ceil(wgs2 / kCus) * steps2 * t_step2 + t_fixed +
                           0.5e-6;   // LDS merge
         if (forced_ks == 2 || (forced <= 0 && t2 < best * 0.98)) {
             pl.ks = 2;
