@@ -56,6 +56,12 @@
 //     (unnormalised O, running max, running sum) to the workspace, and the
 //     last workgroup of a query tile to finish (integer counter) merges the
 //     partials in split order, so the result is bitwise reproducible.
+//   * Two key groups (the KS = 2 instantiations, d=64) for grids far too
+//     small to fill the GPU: a workgroup of four wavefronts takes 64
+//     queries, two query wavefronts per key group, each group streaming one
+//     half of the key range through its own four-stage ring; at the end the
+//     second group hands its (O, m, l) to the first through LDS.  Half the
+//     steps per workgroup, no workspace, no cross-workgroup hand-off.
 //   * Workgroups are mapped to XCDs so that each XCD streams a contiguous
 //     range of (batch, head) buffers, keeping their K/V in that XCD's L2.
 //   * Fresh rows (the NF = 1, 2 instantiations): key tiles of up to two
