@@ -125,3 +125,30 @@ def test_landed_sums_feed_the_next_step():
                                           eps=1e-5).numpy()
     got = np.concatenate(outs, axis=-1)
     assert np.abs(got - want).max() <= MAX_ABS
+
+
+def _random_case(i):
+    rng = np.random.Generator(np.random.PCG64(7000 + i))
+    G_ = int(rng.choice([1, 2, 4, 8, 32]))
+    C = G_ * int(rng.integers(1, 9))
+    n = int(rng.choice([int(rng.integers(1, 200)), int(rng.integers(1000, 40000))]))
+    B = int(rng.integers(1, 4))
+    P = int(rng.integers(1, 9))
+    return dict(B=B, C=C, G_=G_, n=n, P=P, p=int(rng.integers(0, P)),
+                affine=bool(rng.integers(0, 2)), in_place=bool(rng.integers(0, 4) == 0),
+                land=bool(rng.integers(0, 4) != 0), offset=int(rng.choice([0, 0, 0, 1, 3])),
+                ws=bool(rng.integers(0, 4) != 0))
+
+
+@pytest.mark.parametrize("i", range(32))
+def test_random_shape(i):
+    """Seeded draws across the register, chunked and single-workgroup paths:
+    group runs from a few floats to over 300 Ki, n with and without a
+    multiple of 4, x and y on and off the 16-byte grid, in place, with and
+    without gamma/beta, landing and workspace."""
+    c = _random_case(i)
+    G.require_gpu()
+    G.announce(f"group norm random case {i}: {c}")
+    kw = dict(c)
+    B, C, G_, n, P, p = (kw.pop(k) for k in ("B", "C", "G_", "n", "P", "p"))
+    _run(B, C, G_, n, P, p, seed=7100 + i, **kw)
