@@ -10,7 +10,10 @@
  *   - once per step, the conditional and unconditional predictions are
  *     combined (classifier-free guidance), the latent is advanced by one
  *     DDIM (eta = 0) or flow-matching Euler step, and the rel-MAE between the
- *     two predictions is reduced.
+ *     two predictions is reduced;
+ *   - a patch's GroupNorm takes its statistics from the other patches'
+ *     previous-step partial sums and its own fresh ones (displaced GroupNorm,
+ *     the corrected_async_gn mode).
  *
  * Sources (page title, section):
  *   [DF] "终极性能对比：DistriFusion vs 传统推理方案" -- "DistriFusion的革命性突破":
@@ -28,6 +31,10 @@
  *   [AI] "AIGC 文生图系统如何优化扩散模型推理速度" -- section 3 (DDIM with
  *        eta; eta = 0 is deterministic) and section 6 (operator fusion to cut
  *        data movement).
+ *   [DT] "DistriFusion高级教程：自定义并行配置实现超高清图像生成的完整指南" --
+ *        多设备配置优化 and 速度与质量平衡: a communication mode named
+ *        corrected_async_gn (an asynchronous GroupNorm with a correction),
+ *        given by name only.
  *
  * Conventions shared by every entry point:
  *   - Pointers are DEVICE pointers unless the parameter says "host".  The
