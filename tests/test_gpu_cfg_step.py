@@ -213,3 +213,71 @@ def test_no_reduction_and_degenerate_ratios():
     dfp.relmae(ones, zeros, out, ws)
     torch.cuda.synchronize()
     assert math.isinf(out[0].item()) and out[0].item() > 0
+
+
+def _random_case(i):
+    rng = np.random.Generator(np.random.PCG64(8000 + i))
+    n = int(rng.choice([int(rng.integers(1, 300)), int(rng.integers(300, 70000)),
+                        int(rng.integers(70000, 600000))]))
+    a_t = float(rng.uniform(0.01, 0.9))
+    s0 = float(rng.uniform(0.05, 1.0))
+    return dict(batch=int(rng.integers(1, 6)), n=n,
+                kind=str(rng.choice(["ddim", "ddim_last", "euler", "eta"])),
+                w=float(rng.uniform(0.0, 10.0)), offset=int(rng.choice([0, 0, 1, 2, 3])),
+                with_relmae=bool(rng.integers(0, 4) != 0), a_t=a_t,
+                a_prev=float(rng.uniform(a_t, 0.999)), eta=float(rng.uniform(0.0, 1.0)),
+                s0=s0, s1=float(rng.uniform(0.0, s0)))
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_random_shape(i):
+    """Seeded draws over latent sizes (a few floats to over half a million
+    per image, 1-5 images per call), x and the predictions on and off the
+    16-byte grid, DDIM (also its last step and eta > 0) and Euler updates,
+    any guidance weight, with and without the rel-MAE output: every image's
+    step and rel-MAE against the oracle, the counters back at zero."""
+    c = _random_case(i)
+    G.require_gpu()
+    G.announce(f"cfg step random case {i}: {c}")
+    torch = G.torch_mod()
+    B, n, off = c["batch"], c["n"], c["offset"]
+    r = np.random.Generator(np.random.PCG64(8100 + i))
+    x0, g_c, g_u, z = (r.standard_normal((B, n), dtype=np.float32) for _ in range(4))
+
+    def dev(a):
+        t = torch.full((B * n + off + 16,), float("nan"), dtype=torch.float32, device="cuda")
+        t[off:off + B * n] = torch.from_numpy(a.ravel()).cuda()
+        return t, t[off:off + B * n].view(B, n)
+
+    xs, x = dev(x0)
+    out = torch.full((B,), float("nan"), dtype=torch.float32, device="cuda") \
+        if c["with_relmae"] else None
+    ws = dfp.cfg_workspace(n, B) if c["with_relmae"] else None
+    args = (dev(g_c)[1], dev(g_u)[1])
+    kind = c["kind"]
+    if kind == "eta":
+        c_x, c_e, c_z = dfp.ddim_eta_coeffs(c["a_t"], c["a_prev"], c["eta"])
+        dfp.cfg_step_noise(x, *args, dev(z)[1], c["w"], c_x, c_e, c_z, out, ws)
+    else:
+        if kind == "euler":
+            c_x, c_e = dfp.euler_coeffs(c["s0"], c["s1"])
+        else:
+            c_x, c_e = dfp.ddim_coeffs(c["a_t"], 1.0 if kind == "ddim_last" else c["a_prev"])
+        dfp.cfg_step(x, *args, c["w"], c_x, c_e, out, ws)
+    torch.cuda.synchronize()
+    got = x.cpu().numpy()
+    for b in range(B):
+        g = oracle.cfg_combine(g_c[b], g_u[b], c["w"])
+        if kind == "eta":
+            want = oracle.ddim_step_eta(x0[b], g, z[b], c["a_t"], c["a_prev"], c["eta"], False)
+        elif kind == "euler":
+            want = oracle.euler_step(x0[b], g, c["s0"], c["s1"])
+        else:
+            want = oracle.ddim_step(x0[b], g, c["a_t"], c["a_prev"], kind == "ddim_last")
+        assert G.rel_l2(got[b], want) <= STEP_REL_L2, f"image {b}"
+        if out is not None:
+            rw = oracle.relmae(g_c[b], g_u[b])
+            assert abs(out[b].item() - rw) / rw <= RELMAE_REL, f"image {b}"
+    assert torch.isnan(xs[off + B * n:]).all() and torch.isnan(xs[:off]).all()
+    if ws is not None:
+        assert int(ws[:B * 4].sum().item()) == 0
