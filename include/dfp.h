@@ -141,8 +141,11 @@ dfp_status dfp_kv_scatter(void *k_buf, void *v_buf_t, const void *k_new,
  *           when the query grid alone is too small to fill the GPU; without
  *           it, it never splits.  The workspace starts with per-query-tile
  *           arrival counters that must be zero before the first call (e.g.
- *           allocate it zeroed); every call leaves them zero again.  The
- *           split partials are merged in a fixed order, so results are
+ *           allocate it zeroed); every call leaves them zero again.  How
+ *           many counters there are, and so where the partials begin,
+ *           depends on the sizes and the plan: zero the workspace again
+ *           before it serves calls of other sizes, or keep one per size.
+ *           The split partials are merged in a fixed order, so results are
  *           bitwise reproducible for a given shape.  Calls that share a
  *           workspace must not run concurrently (one stream, or streams
  *           ordered by events).
@@ -221,7 +224,9 @@ dfp_status dfp_patch_attention_fresh(void *o, const void *q, void *k_buf,
  *              (4 bytes each, padded to a multiple of 256 bytes) that must
  *              be zero before the first call (e.g. allocate it zeroed);
  *              every call leaves them zero again.  The rest holds
- *              per-workgroup partial sums.  Calls that share a workspace
+ *              per-workgroup partial sums; as the counters' extent depends
+ *              on batch, zero the workspace again before it serves calls
+ *              with another batch, or keep one per batch.  Calls that share a workspace
  *              must not run concurrently.  The cross-workgroup sum runs
  *              in a fixed order in double precision, so results are
  *              bitwise reproducible.
@@ -285,7 +290,9 @@ dfp_status dfp_relmae(const float *g_c, const float *g_u, int64_t n_per_image,
  *           workgroup per (image, group) does it.  The workspace starts
  *           with one arrival counter per (image, group) that must be zero
  *           before the first call (allocate it zeroed); every call leaves
- *           them zero.  Calls that share a workspace must not run
+ *           them zero.  As their extent depends on B and G, zero the
+ *           workspace again before it serves calls of other sizes, or keep
+ *           one per size.  Calls that share a workspace must not run
  *           concurrently.
  * The statistics are bitwise reproducible (fixed-order fp64 sums).
  * Errors: INVALID_ARG for null y/x/stats, non-positive B/C/G/n/P, C not a
