@@ -45,6 +45,8 @@ def _load():
     lib = ctypes.CDLL(_LIB_PATH)
     D = ctypes.POINTER(ctypes.c_double)
     I = ctypes.POINTER(ctypes.c_int64)
+    U = ctypes.POINTER(ctypes.c_uint64)
+    u64 = ctypes.c_uint64
     i64, dbl, cint = ctypes.c_int64, ctypes.c_double, ctypes.c_int
     sigs = {
         "oracle_effective_kv": (None, [D, D, i64, i64, i64, i64, i64]),
@@ -55,8 +57,11 @@ def _load():
         "oracle_alphas_cumprod": (None, [i64, D, D]),
         "oracle_ddim_timesteps": (None, [i64, i64, I]),
         "oracle_cfg_combine": (None, [D, D, i64, dbl, D]),
-        "oracle_ddim_step": (None, [D, D, i64, dbl, dbl, cint]),
-        "oracle_ddim_step_eta": (None, [D, D, D, i64, dbl, dbl, dbl, cint]),
+        "oracle_ddim_sigma": (dbl, [dbl, dbl, dbl]),
+        "oracle_ddim_update": (None, [D, D, D, i64, dbl, dbl, dbl]),
+        "oracle_philox4x64_10": (None, [U, U, U]),
+        "oracle_philox_normals": (None, [D, i64, u64, u64, u64]),
+        "oracle_set_threads": (None, [cint]),
         "oracle_switch_points": (cint, [D, i64, i64, dbl, i64, I, I]),
         "oracle_flow_sigmas": (None, [i64, D]),
         "oracle_euler_step": (None, [D, D, i64, dbl, dbl]),
@@ -236,22 +241,59 @@ def cfg_combine(g_c, g_u, w: float) -> np.ndarray:
     return g
 
 
-def ddim_step(x, eps, abar_t: float, abar_prev: float, last: bool) -> np.ndarray:
+def ddim_sigma(abar_t: float, abar_prev: float, eta: float) -> float:
+    """Noise scale of a DDIM step with parameter eta."""
+    return float(_load().oracle_ddim_sigma(float(abar_t), float(abar_prev), float(eta)))
+
+
+def _ddim(x, eps, z, abar_t, abar_prev, eta, last):
     x = _f64(x).copy()
     eps = _f64(eps)
-    _load().oracle_ddim_step(_pd(x), _pd(eps), x.size, float(abar_t), float(abar_prev), int(bool(last)))
+    if eps.shape != x.shape or (z is not None and z.shape != x.shape):
+        raise ValueError("x, eps and z shapes differ")
+    a_prev = 1.0 if last else float(abar_prev)   # the last step returns the x0 estimate
+    sigma = ddim_sigma(abar_t, a_prev, eta) if eta else 0.0
+    _load().oracle_ddim_update(_pd(x), _pd(eps), None if z is None else _pd(_f64(z)), x.size,
+                               float(abar_t), a_prev, sigma)
     return x
+
+
+def ddim_step(x, eps, abar_t: float, abar_prev: float, last: bool) -> np.ndarray:
+    """DDIM with eta = 0: x_t -> the previous sampled timestep (abar_prev),
+    or -> the x0 estimate on the last step."""
+    return _ddim(x, eps, None, abar_t, abar_prev, 0.0, last)
 
 
 def ddim_step_eta(x, eps, z, abar_t: float, abar_prev: float, eta: float,
                   last: bool) -> np.ndarray:
-    x = _f64(x).copy()
-    eps, z = _f64(eps), _f64(z)
-    if eps.shape != x.shape or z.shape != x.shape:
-        raise ValueError("x, eps and z shapes differ")
-    _load().oracle_ddim_step_eta(_pd(x), _pd(eps), _pd(z), x.size, float(abar_t),
-                                 float(abar_prev), float(eta), int(bool(last)))
-    return x
+    """DDIM with noise scale eta and the standard-normal draw z."""
+    return _ddim(x, eps, _f64(z), abar_t, abar_prev, eta, last)
+
+
+def philox4x64_10(counter, key) -> np.ndarray:
+    """One Philox4x64-10 block: counter (4 uint64), key (2 uint64) -> 4 uint64."""
+    c = np.ascontiguousarray(np.asarray(counter, dtype=np.uint64))
+    k = np.ascontiguousarray(np.asarray(key, dtype=np.uint64))
+    if c.shape != (4,) or k.shape != (2,):
+        raise ValueError("counter must hold 4 words and key 2")
+    out = np.empty(4, dtype=np.uint64)
+    P = ctypes.POINTER(ctypes.c_uint64)
+    _load().oracle_philox4x64_10(c.ctypes.data_as(P), k.ctypes.data_as(P), out.ctypes.data_as(P))
+    return out
+
+
+def philox_normals(n: int, seed: int, step: int, image: int = 0) -> np.ndarray:
+    """The standard-normal draw z[0..n) of one image at one sampler step
+    (Philox4x64-10 + Box-Muller; mapping in dfp_oracle.c)."""
+    z = np.empty(int(n), dtype=np.float64)
+    _load().oracle_philox_normals(_pd(z), int(n), int(seed) & (2**64 - 1),
+                                  int(step) & (2**64 - 1), int(image) & (2**64 - 1))
+    return z
+
+
+def set_threads(threads: int) -> None:
+    """Threads the oracle's parallel loops use from now on (timing only)."""
+    _load().oracle_set_threads(int(threads))
 
 
 def euler_step(x, v, sigma: float, sigma_next: float) -> np.ndarray:

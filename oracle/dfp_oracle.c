@@ -42,6 +42,9 @@
 #include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 /* ------------------------------------------------------------------------ */
 /* The persistent K/V buffer after the fresh patch rows have landed.          */
@@ -225,51 +228,109 @@ void oracle_cfg_combine(const double *g_c, const double *g_u, int64_t n,
         g[i] = g_u[i] + w * (g_c[i] - g_u[i]);
 }
 
-/* [AI] section 3, DDIM with eta = 0, in its own two-stage form:
- *   x0_hat = (x_t - sigma_t * eps) / sqrt(abar_t),  sigma_t = sqrt(1 - abar_t)
- *   not last:  x_{t-1} = sqrt(abar_prev) x0_hat
- *                       + sqrt(1 - abar_prev - sigma_eta^2) eps,  sigma_eta = 0
- *   last:      x_{t-1} = x0_hat                                               */
-void oracle_ddim_step(double *x, const double *eps, int64_t n, double abar_t,
-                      double abar_prev, int last)
+/* [AI] section 3, DDIM.  The DDIM update moves x_t to the previous sampled
+ * timestep in three parts, all read off the noise prediction eps:
+ *   the predicted clean latent   x0  = (x_t - sqrt(1 - abar_t) eps) / sqrt(abar_t)
+ *     (the page's undefined sigma_t is read as sqrt(1 - abar_t));
+ *   the direction back to x_t    dir = sqrt(1 - abar_prev - sigma^2) eps;
+ *   fresh noise                  sigma z,  z ~ N(0, 1);
+ * and x_{t-1} = sqrt(abar_prev) x0 + dir + sigma z.  The page's final step
+ * returns x0 itself, which is this update with abar_prev = 1 (then sigma = 0
+ * and dir = 0).  sigma is the step's noise scale, see oracle_ddim_sigma. */
+double oracle_ddim_sigma(double abar_t, double abar_prev, double eta)
 {
-    double sigma_t = sqrt(1.0 - abar_t);
-    double sqrt_abar_t = sqrt(abar_t);
-    double sigma_eta = 0.0;
+    /* [AI] section 3: eta scales the standard deviation of the DDPM
+     * posterior q(x_{t-1} | x_t, x0); eta = 0 is deterministic DDIM. */
+    double posterior_var = (1.0 - abar_prev) / (1.0 - abar_t) * (1.0 - abar_t / abar_prev);
+    return eta * sqrt(posterior_var);
+}
+
+void oracle_ddim_update(double *x, const double *eps, const double *z, int64_t n,
+                        double abar_t, double abar_prev, double sigma)
+{
+    const double keep = sqrt(abar_prev);                           /* on x0  */
+    const double toward = sqrt(1.0 - abar_prev - sigma * sigma);   /* on eps */
     for (int64_t i = 0; i < n; ++i) {
-        double x0_hat = (x[i] - sigma_t * eps[i]) / sqrt_abar_t;
-        if (last)
-            x[i] = x0_hat;
-        else
-            x[i] = sqrt(abar_prev) * x0_hat +
-                   sqrt(1.0 - abar_prev - sigma_eta * sigma_eta) * eps[i];
+        double pred_x0 = (x[i] - sqrt(1.0 - abar_t) * eps[i]) / sqrt(abar_t);
+        double noise = (z != NULL) ? sigma * z[i] : 0.0;
+        x[i] = keep * pred_x0 + toward * eps[i] + noise;
     }
 }
 
-/* [AI] section 3, DDIM with a general eta (the same listing): the noise
- * scale of the step is
- *   sigma_eta = eta * sqrt((1 - abar_prev) / (1 - abar_t) * (1 - abar_t / abar_prev))
- * and the step adds sigma_eta * z for a standard-normal draw z (passed in):
- *   x0_hat  = (x_t - sigma_t * eps) / sqrt(abar_t)
- *   not last: x_{t-1} = sqrt(abar_prev) x0_hat
- *                      + sqrt(1 - abar_prev - sigma_eta^2) eps + sigma_eta z
- *   last:     x_{t-1} = x0_hat                                            */
-void oracle_ddim_step_eta(double *x, const double *eps, const double *z, int64_t n,
-                          double abar_t, double abar_prev, double eta, int last)
+/* ------------------------------------------------------------------------ */
+/* The standard-normal draw z of a DDIM step with eta > 0 ([AI] section 3    */
+/* draws it with randn_like).  To draw the same z on any device it comes     */
+/* from a counter-based generator: Philox4x64 with 10 rounds (J. Salmon,     */
+/* M. Moraes, R. Dror, D. Shaw, "Parallel Random Numbers: As Easy as 1, 2,   */
+/* 3", SC'11), followed by the Box-Muller transform (G. Box, M. Muller, "A   */
+/* Note on the Generation of Random Normal Deviates", 1958).                 */
+/* ------------------------------------------------------------------------ */
+
+/* One Philox4x64-10 block.  Each round multiplies counter words 0 and 2 by
+ * the round constants (full 128-bit products), and the new counter is
+ * (hi(M1*c2) ^ c1 ^ k0, lo(M1*c2), hi(M0*c0) ^ c3 ^ k1, lo(M0*c0)); between
+ * rounds the key is advanced by the two Weyl constants. */
+void oracle_philox4x64_10(const uint64_t ctr[4], const uint64_t key[2], uint64_t out[4])
 {
-    double sigma_t = sqrt(1.0 - abar_t);
-    double sqrt_abar_t = sqrt(abar_t);
-    double sigma_eta =
-        eta * sqrt((1.0 - abar_prev) / (1.0 - abar_t) * (1.0 - abar_t / abar_prev));
-    for (int64_t i = 0; i < n; ++i) {
-        double x0_hat = (x[i] - sigma_t * eps[i]) / sqrt_abar_t;
-        if (last)
-            x[i] = x0_hat;
-        else
-            x[i] = sqrt(abar_prev) * x0_hat +
-                   sqrt(1.0 - abar_prev - sigma_eta * sigma_eta) * eps[i] +
-                   sigma_eta * z[i];
+    const uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
+    const uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
+    uint64_t c0 = ctr[0], c1 = ctr[1], c2 = ctr[2], c3 = ctr[3];
+    uint64_t k0 = key[0], k1 = key[1];
+    for (int round = 0; round < 10; ++round) {
+        if (round > 0) {
+            k0 += W0;
+            k1 += W1;
+        }
+        unsigned __int128 p0 = (unsigned __int128)M0 * c0;
+        unsigned __int128 p1 = (unsigned __int128)M1 * c2;
+        uint64_t n0 = (uint64_t)(p1 >> 64) ^ c1 ^ k0;
+        uint64_t n1 = (uint64_t)p1;
+        uint64_t n2 = (uint64_t)(p0 >> 64) ^ c3 ^ k1;
+        uint64_t n3 = (uint64_t)p0;
+        c0 = n0; c1 = n1; c2 = n2; c3 = n3;
     }
+    out[0] = c0; out[1] = c1; out[2] = c2; out[3] = c3;
+}
+
+/* z[0..n) of image `image` at sampler step `step` under `seed`.  Block j
+ * (elements 8j .. 8j+7) is Philox4x64-10 of counter (j, image, 0, 0) under
+ * key (seed, step).  Its four 64-bit words give eight 32-bit halves h_0..h_7
+ * (h_{2k} the low half of word k, h_{2k+1} the high half), each mapped to a
+ * uniform u = (h + 1/2) / 2^32 in (0, 1).  Pair k turns (u_{2k}, u_{2k+1})
+ * into two normals by Box-Muller:
+ *   z[8j+2k]   = sqrt(-2 ln u_{2k}) cos(2 pi u_{2k+1})
+ *   z[8j+2k+1] = sqrt(-2 ln u_{2k}) sin(2 pi u_{2k+1}). */
+void oracle_philox_normals(double *z, int64_t n, uint64_t seed, uint64_t step, uint64_t image)
+{
+    const double two_pi = 6.283185307179586476925286766559;
+    const uint64_t key[2] = {seed, step};
+    for (int64_t j = 0; 8 * j < n; ++j) {
+        const uint64_t ctr[4] = {(uint64_t)j, image, 0, 0};
+        uint64_t w[4];
+        oracle_philox4x64_10(ctr, key, w);
+        double u[8];
+        for (int k = 0; k < 4; ++k) {
+            u[2 * k] = ((double)(w[k] & 0xFFFFFFFFull) + 0.5) / 4294967296.0;
+            u[2 * k + 1] = ((double)(w[k] >> 32) + 0.5) / 4294967296.0;
+        }
+        for (int k = 0; k < 4; ++k) {
+            double r = sqrt(-2.0 * log(u[2 * k]));
+            double a = two_pi * u[2 * k + 1];
+            if (8 * j + 2 * k < n) z[8 * j + 2 * k] = r * cos(a);
+            if (8 * j + 2 * k + 1 < n) z[8 * j + 2 * k + 1] = r * sin(a);
+        }
+    }
+}
+
+/* Run a parallel region of this library on `threads` threads from now on
+ * (harness plumbing for timing the oracle on one core; no arithmetic). */
+void oracle_set_threads(int threads)
+{
+#ifdef _OPENMP
+    if (threads > 0) omp_set_num_threads(threads);
+#else
+    (void)threads;
+#endif
 }
 
 /* [HY] 损失函数/训练策略: flow-matching models predict a velocity v in place
@@ -303,9 +364,6 @@ double oracle_relmae(const double *g_c, const double *g_u, int64_t n)
 }
 
 /* Number of OpenMP threads a parallel region of this library uses. */
-#ifdef _OPENMP
-#include <omp.h>
-#endif
 int oracle_num_threads(void)
 {
 #ifdef _OPENMP

@@ -64,6 +64,35 @@ def test_two_keys_logistic_closed_form():
                                rtol=0, atol=1e-15)
 
 
+def _numpy_probs(q, k, scale):
+    """The probability matrix of _numpy_attention, on its own."""
+    s = np.einsum("...id,...jd->...ij", q, k) * scale
+    p = np.exp(s - s.max(axis=-1, keepdims=True))
+    return p / p.sum(axis=-1, keepdims=True)
+
+
+@pytest.mark.parametrize("shape,scale", [((2, 2, 6, 16, 33), 0.25), ((1, 3, 4, 8, 1), 1.0),
+                                         ((1, 1, 9, 5, 70), 3.0)])
+def test_probability_matrix_matches_numpy(shape, scale):
+    B, H, nq, d, N = shape
+    r = _rng(nq * 31 + N)
+    q = r.standard_normal((B, H, nq, d))
+    k = r.standard_normal((B, H, N, d))
+    np.testing.assert_allclose(oracle.attention_probs(q, k, scale), _numpy_probs(q, k, scale),
+                               rtol=1e-13, atol=1e-15)
+
+
+def test_probability_matrix_two_keys_and_order():
+    # two keys: logistic weights of the score gap, in key order
+    q = np.array([[[[1.0, 2.0], [0.0, 0.0]]]])
+    k = np.array([[[[0.5, -1.0], [2.0, 0.25]]]])
+    p = oracle.attention_probs(q, k, 0.7)
+    s0, s1 = 0.7 * (0.5 - 2.0), 0.7 * (2.0 + 0.5)
+    w0 = 1.0 / (1.0 + math.exp(s1 - s0))
+    np.testing.assert_allclose(p[0, 0, 0], [w0, 1 - w0], rtol=0, atol=1e-15)
+    np.testing.assert_allclose(p[0, 0, 1], [0.5, 0.5], rtol=0, atol=0)   # q = 0: uniform
+
+
 def test_probability_rows_sum_to_one():
     r = _rng(3)
     q = r.standard_normal((2, 2, 6, 16)) * 3
