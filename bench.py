@@ -1,23 +1,27 @@
 #!/usr/bin/env python3
 """Benchmark of one GPU's share of a patch-parallel diffusion step on MI355X.
 
-One timed "step" is the whole hot path once, at the SDXL-1024-shaped workload
-(64x64 level: 4096 tokens, 10 heads x 64, P=4; 32x32 level: 1024 tokens,
-20 heads x 64, P=4; batch 2 = cond/uncond; latent 1x4x128x128, DDIM-50,
-w=7.5):
-  patch attention (64x64 level), reading the patch's fresh K/V from this
-      step's tensors and landing them in the persistent buffer in the same
-      launch (dfp_patch_attention_fresh)
-  the same for the 32x32 level
-  fused CFG + DDIM update + rel-MAE on the latent.
-A DiT level passes its always-fresh text rows as a second fresh range.  A
-level whose patch rows are not whole 64-key tiles (SDXL-3840) lands its K/V
-with dfp_kv_scatter and then runs dfp_patch_attention; `--no-fresh` times
-that path everywhere.
+The headline workload is the largest one that fits one GPU, SDXL-3840-shaped:
+the 240x240 attention level (57600 tokens, 10 heads x 64, P=8, so one patch
+is 7200 query rows against the 57600-row displaced K/V buffer; batch 2 =
+cond/uncond) and the fused CFG + DDIM-50 + rel-MAE step on the 1x4x480x480
+latent (w=7.5).  One timed "step" is the whole hot path once:
+  landing of the patch's fresh K/V in the persistent buffer
+      (dfp_kv_scatter: the patch's 7200 rows are not whole 64-key tiles) or,
+      where the rows are whole tiles, inside the attention launch
+      (dfp_patch_attention_fresh; a DiT passes its text rows as a second
+      fresh range)
+  patch attention over the buffer
+  fused CFG + sampler update + rel-MAE on the latent.
 All inputs are seeded synthetic arrays resident in HBM before timing starts.
-The timed steps replay one HIP graph of the step (falls back to eager
-launches if capture is refused).  Per-kernel durations for the roofline come
-from HIP events on the launch stream around batches of back-to-back launches.
+The timed steps replay one HIP graph of the step (eager launches if capture
+is refused).  Per-kernel durations come from HIP events on the launch stream
+around batches of back-to-back launches.
+
+The same run also times the other configurations' kernels (SDXL-1024's two
+levels, SDXL-2048, DiT-1024) and reports them under "configs", and times
+the fp64 oracle on the host on a bounded, seeded sample of the headline
+workload ("cpu_baseline").
 
 Prints ONE JSON line.  `--gpus N` with N > 1 is refused: this library is the
 single-GPU share of the work.
@@ -37,21 +41,29 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = ("patch-attn TFLOP/s (% bf16 MFMA peak); CFG+sampler step GB/s (% HBM peak)")
-PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA (vendor figure, 2.4 GHz)
+PEAK_CLOCK_GHZ = 2.4
 PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
+NAMES = {"sdxl1024": "SDXL-1024-shaped", "sdxl2048": "SDXL-2048-shaped",
+         "sdxl3840": "SDXL-3840-shaped", "dit1024": "DiT/flow-shaped"}
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="sdxl1024",
-                    choices=["sdxl1024", "sdxl2048", "sdxl3840", "dit1024"],
-                    help="sdxl1024 is the reported workload; the others are for exploration")
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="sdxl3840", choices=sorted(NAMES),
+                    help="headline workload (default: the largest single-GPU one)")
+    ap.add_argument("--configs", default="sdxl1024,sdxl2048,dit1024",
+                    help="other workloads whose kernels are timed in the same run "
+                         "(comma list; empty for none)")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--kernel-reps", type=int, default=50)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="host time budget of the oracle on all cores (the 1-core run "
+                         "gets half of it)")
+    ap.add_argument("--kernel-reps", type=int, default=20)
     ap.add_argument("--sweep", action="store_true",
                     help="time the one-device patch sweep: every patch of each level in order "
                          "(each landing its fresh K/V for the patches after it), instead of one "
@@ -61,31 +73,47 @@ def parse():
                          "of the fused dfp_patch_attention_fresh")
     ap.add_argument("--eta", type=float, default=0.0,
                     help="DDIM noise scale (DDIM workloads): > 0 runs the fused step with the "
-                         "sampler-noise term (dfp_cfg_step_noise)")
+                         "sampler-noise term drawn in the kernel (dfp_cfg_step_philox)")
+    ap.add_argument("--noise-array", action="store_true",
+                    help="with --eta: read the noise from a caller array (dfp_cfg_step_noise) "
+                         "instead of drawing it in the kernel")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run one plain device-to-device copy of this many MiB, the "
                          "reference kernel that scales FETCH_SIZE/WRITE_SIZE counter runs")
     return ap.parse_args()
 
 
-def measured_traffic(kernel_source: str, level_name: str):
-    """HBM bytes per launch of the attention kernel on `level_name`, from the
-    committed rocprofv3 counter summary -- only while the kernel source still
-    hashes to the one the counters were taken on (else None)."""
-    path = os.path.join(ROOT, "profiles", f"attn_bf16_{level_name}_hbm_traffic.txt")
+def profile_fields(path: str, section: str | None = None) -> dict:
+    """key: value lines of a committed rocprofv3 summary (of one [section]
+    when given)."""
+    fields, cur = {}, None
     if not os.path.exists(path):
-        return None
-    fields = {}
+        return fields
     with open(path) as fh:
         for line in fh:
-            if ":" in line and not line.startswith("#"):
-                k, v = line.split(":", 1)
+            s = line.strip()
+            if s.startswith("[") and s.endswith("]"):
+                cur = s[1:-1]
+                continue
+            if ":" in s and not s.startswith("#") and (section is None or cur == section
+                                                       or cur is None):
+                k, v = s.split(":", 1)
                 fields[k.strip()] = v.strip()
-    with open(kernel_source, "rb") as fh:
-        sha = hashlib.sha256(fh.read()).hexdigest()
-    if fields.get("source_sha256") != sha or "traffic_bytes" not in fields:
+    return fields
+
+
+def source_sha(rel: str) -> str:
+    with open(os.path.join(ROOT, rel), "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()
+
+
+def counted(path: str, source: str, key: str, section: str | None = None):
+    """A figure from a committed counter summary, only while the kernel
+    source still hashes to the one the counters were taken on (else None)."""
+    f = profile_fields(path, section)
+    if f.get("source_sha256") != source_sha(source) or key not in f:
         return None
-    return float(fields["traffic_bytes"])
+    return float(f[key])
 
 
 class Level:
@@ -119,12 +147,15 @@ class Level:
         if level.n_text:
             kt, vt = x.text_rows()
             self.text = (up(kt), up(np.swapaxes(vt, -1, -2) if self.fused else vt))
+        del x
         self.ws = dfp.attention_workspace(level.B, level.H, level.n, level.N_kv, level.d)
         self.scale = 1.0 / level.d ** 0.5
         self.flops = level.flops() * len(self.patches)
         self.fresh_bytes = 2 * 2 * self.fresh[0][0].numel() * 2   # K and V, read + write
         if self.text:
             self.fresh_bytes += 2 * 2 * self.text[0].numel() * 2
+        self.plan = dfp.attention_plan(level.B, level.H, level.n, level.N_kv, level.d,
+                                       self.ws is not None)
 
     def scatter(self, dfp, i=0):
         if self.text and i == 0:
@@ -148,21 +179,29 @@ class Level:
                 self.scatter(dfp, i)
                 self.attend(dfp, i)
 
+    def kernel_name(self):
+        ks = self.plan[0]
+        nf = (2 if self.text else 1) if self.fused else 0   # fresh ranges the launch reads
+        return f"attn_fwd_bf16<{self.level.d}, {ks}, {nf}>"
+
 
 class Sampler:
-    """Latent, per-step prediction pairs (and sampler noise when eta > 0) and
-    coefficients, all in HBM."""
+    """Latent, per-step prediction pairs (and caller noise when eta > 0 with
+    --noise-array) and coefficients, all in HBM.  The pairs of every step
+    stay resident, so consecutive timed steps read different predictions."""
 
-    def __init__(self, wl, dfp, torch, inputs, eta=0.0):
+    def __init__(self, wl, dfp, torch, inputs, eta=0.0, noise_array=False):
         st = inputs.sampler_stream(wl)
         self.wl = wl
         self.eta = eta if wl.sampler == "ddim" else 0.0
+        self.noise_array = noise_array and self.eta > 0
+        self.seed = inputs.noise_seed(wl)
         self.x = torch.from_numpy(st.x_T).cuda()
         pairs = [st.next_pair() for _ in range(wl.steps)]
         self.g_c = [torch.from_numpy(a).cuda() for a, _ in pairs]
         self.g_u = [torch.from_numpy(b).cuda() for _, b in pairs]
         self.z = ([torch.from_numpy(st.next_noise()).cuda() for _ in range(wl.steps)]
-                  if self.eta > 0 else None)
+                  if self.noise_array else None)
         self.coeffs = []
         if wl.sampler == "ddim":
             abar = dfp.scaled_linear_abar(1000, 0.00085, 0.012)
@@ -178,14 +217,19 @@ class Sampler:
         batch = wl.latent[0]
         self.ws = dfp.cfg_workspace(wl.n_latent, batch)
         self.r = torch.empty((wl.steps, batch), dtype=torch.float32, device="cuda")
-        self.bytes = (20 if self.z else 16) * self.x.numel()
+        self.bytes = (20 if self.noise_array else 16) * self.x.numel()
+        self.entry = ("dfp_cfg_step_noise" if self.noise_array else
+                      "dfp_cfg_step_philox" if self.eta > 0 else "dfp_cfg_step")
 
     def step(self, dfp, i):
         k = i % self.wl.steps
         c_x, c_e, c_z = self.coeffs[k]
-        if self.z:
+        if self.noise_array:
             dfp.cfg_step_noise(self.x, self.g_c[k], self.g_u[k], self.z[k], self.wl.w, c_x, c_e,
                                c_z, self.r[k], self.ws)
+        elif self.eta > 0:
+            dfp.cfg_step_philox(self.x, self.g_c[k], self.g_u[k], self.wl.w, c_x, c_e, c_z,
+                                self.seed, k, self.r[k], self.ws)
         else:
             dfp.cfg_step(self.x, self.g_c[k], self.g_u[k], self.wl.w, c_x, c_e, self.r[k],
                          self.ws)
@@ -215,11 +259,64 @@ def time_kernel(torch, fn, reps, batches=3):
     return float(np.mean(per)), float(np.min(per))
 
 
-def cpu_baseline(wl, inputs):
-    """The fp64 oracle, as it stands, on the same workload: one whole step
-    (every attention level's patch attention over its displaced buffer, then
-    the guided sampler step with rel-MAE), repeated until about 10 s of host
-    work; reported like `value` (attention FLOP of the step / step time)."""
+def attn_reps(flops: float, reps: int) -> int:
+    """Fewer back-to-back launches for long kernels (about 50 ms per batch)."""
+    per = flops / 1e15   # seconds at ~1 PFLOP/s
+    return max(3, min(reps, int(0.05 / max(per, 1e-9))))
+
+
+def time_levels(levels, sampler, dfp, torch, reps):
+    kern = {}
+    for L in levels:
+        # the attention launch the step runs: fused with the landing, or plain
+        fn = (lambda L=L: L.attend_fresh(dfp)) if L.fused else (lambda L=L: L.attend(dfp))
+        mean, mn = time_kernel(torch, fn, attn_reps(L.level.flops(), reps))
+        tf = L.level.flops() / (mean * 1e-6) / 1e12
+        kern[f"attn_{L.level.name}"] = {
+            "us_mean": mean, "us_min": mn, "tflops": tf,
+            "frac_bf16_peak": tf / PEAK_BF16_TFLOPS, "flop": L.level.flops(),
+            "kernel": L.kernel_name(),
+            "plan": {"key_groups": L.plan[0], "splits": L.plan[1], "workgroups": L.plan[2]},
+            "launch": "dfp_patch_attention_fresh (attention + landing of the fresh K/V)"
+                      if L.fused else "dfp_patch_attention"}
+        if not L.fused:
+            mean, mn = time_kernel(torch, lambda L=L: L.scatter(dfp), reps)
+            kern[f"scatter_{L.level.name}"] = {
+                "us_mean": mean, "us_min": mn,
+                "gbps": L.fresh_bytes / (mean * 1e-6) / 1e9,
+                "frac_hbm_peak": L.fresh_bytes / (mean * 1e-6) / 1e9 / PEAK_HBM_GBPS,
+                "bytes": L.fresh_bytes}
+    ctr = [0]
+
+    def cfg():
+        sampler.step(dfp, ctr[0])
+        ctr[0] += 1
+    mean, mn = time_kernel(torch, cfg, max(reps, 50))
+    kern["cfg_step"] = {"us_mean": mean, "us_min": mn,
+                        "gbps": sampler.bytes / (mean * 1e-6) / 1e9,
+                        "frac_hbm_peak": sampler.bytes / (mean * 1e-6) / 1e9 / PEAK_HBM_GBPS,
+                        "bytes": sampler.bytes, "entry": sampler.entry}
+    return kern
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(wl, inputs, budget_s: float):
+    """The fp64 oracle, as it stands, on the headline workload: the patch
+    attention of seeded random (batch*head, query row) pairs of patch 1 of
+    every level over its displaced buffer, in rounds of 256 rows until the
+    time budget is spent -- once on every host core the oracle's OpenMP
+    loops use, once on one core.  Reported like `value` (attention FLOP of
+    the rows timed / host time)."""
     import oracle
     levels = []
     for lv in wl.levels:
@@ -230,25 +327,37 @@ def cpu_baseline(wl, inputs):
         if lv.n_text:
             k_eff = oracle.effective_kv(k_eff, x.text_rows()[0], 0)
             v_eff = oracle.effective_kv(v_eff, x.text_rows()[1], 0)
-        levels.append((x.q_patch(p), k_eff, v_eff, 1.0 / lv.d ** 0.5, lv.flops()))
-    st = inputs.sampler_stream(wl)
-    g_c, g_u = st.next_pair()
-    sched = oracle.DDIMSchedule(wl.steps) if wl.sampler == "ddim" else oracle.EulerSchedule(wl.steps)
-    flops = sum(lv[4] for lv in levels)
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        for q, k, v, scale, _ in levels:
-            oracle.attention(q, k, v, scale)
-        sched.step(st.x_T, g_c, g_u, wl.w, reps % wl.steps)
-        reps += 1
-        dt = time.perf_counter() - t0
-        if dt >= 10.0 or reps >= 200:
-            break
-    return {"value": reps * flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
-            "sample": f"{reps} whole steps of the {wl.name} workload: patch attention of every "
-                      f"level ({flops / 1e9:.2f} GFLOP per step, fp64) and the guided "
-                      f"{wl.sampler} step with rel-MAE on the latent, {dt:.1f} s"}
+        q = np.ascontiguousarray(x.q_patch(p), dtype=np.float64)
+        del x
+        levels.append((lv, q, k_eff, v_eff))
+    rng = np.random.Generator(np.random.PCG64(wl.seed + 900))
+
+    def run(seconds):
+        rows, flop, t0 = 0, 0.0, time.perf_counter()
+        while True:
+            for lv, q, k, v in levels:
+                bh = rng.integers(0, lv.B * lv.H, size=256)
+                ri = rng.integers(0, lv.n, size=256)
+                oracle.attention_rows(q, k, v, 1.0 / lv.d ** 0.5, bh, ri)
+                rows += 256
+                flop += 256 * 4.0 * lv.N_kv * lv.d
+            dt = time.perf_counter() - t0
+            if dt >= seconds:
+                return rows, flop, dt
+
+    cores = oracle.num_threads()
+    rows, flop, dt = run(budget_s)
+    oracle.set_threads(1)
+    rows1, flop1, dt1 = run(budget_s / 2)
+    oracle.set_threads(cores)
+    lv_desc = ", ".join(f"{lv.name} (N_kv {lv.N_kv}, d {lv.d})" for lv, *_ in levels)
+    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{rows} seeded random (batch*head, query row) pairs of patch 1 of "
+                      f"{lv_desc}, fp64 two-pass attention over the displaced buffer, "
+                      f"{flop / 1e9:.1f} GFLOP in {dt:.1f} s on {cores} threads",
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
+            "value_1core": flop1 / dt1 / 1e12,
+            "sample_1core": f"{rows1} pairs, {flop1 / 1e9:.1f} GFLOP in {dt1:.1f} s on 1 thread"}
 
 
 def main():
@@ -276,8 +385,9 @@ def main():
         del src, dst
     wl = inputs.WORKLOADS[args.workload]
     levels = [Level(lv, dfp, torch, inputs, args.sweep, not args.no_fresh) for lv in wl.levels]
-    sampler = Sampler(wl, dfp, torch, inputs, args.eta)
+    sampler = Sampler(wl, dfp, torch, inputs, args.eta, args.noise_array)
     torch.cuda.synchronize()
+    print(f"[bench] {wl.name}: inputs resident", file=sys.stderr, flush=True)
 
     def one_step(i):
         for L in levels:
@@ -326,92 +436,63 @@ def main():
     wall = time.perf_counter() - t0
     ms_per_step = max(ev0.elapsed_time(ev1), 1e-9) / args.steps
     attn_flops = sum(L.flops for L in levels)
+    print(f"[bench] {wl.name}: {args.steps} steps timed, {ms_per_step:.3f} ms/step",
+          file=sys.stderr, flush=True)
 
     # ---- per-kernel durations (HIP events on the launch stream)
-    reps = args.kernel_reps
-    kern = {}
-    for L in levels:
-        # the attention launch the step runs: fused with the landing, or plain
-        fn = (lambda L=L: L.attend_fresh(dfp)) if L.fused else (lambda L=L: L.attend(dfp))
-        mean, mn = time_kernel(torch, fn, reps)
-        kern[f"attn_{L.level.name}"] = {
-            "us_mean": mean, "us_min": mn,
-            "tflops": L.level.flops() / (mean * 1e-6) / 1e12,
-            "frac_bf16_peak": L.level.flops() / (mean * 1e-6) / 1e12 / PEAK_BF16_TFLOPS,
-            "flop": L.level.flops(),
-            "launch": "dfp_patch_attention_fresh (attention + landing of the fresh K/V)"
-                      if L.fused else "dfp_patch_attention"}
-        if not L.fused:
-            mean, mn = time_kernel(torch, lambda L=L: L.scatter(dfp), reps)
-            kern[f"scatter_{L.level.name}"] = {
-                "us_mean": mean, "us_min": mn,
-                "gbps": L.fresh_bytes / (mean * 1e-6) / 1e9, "bytes": L.fresh_bytes}
-    ctr = [0]
-
-    def cfg():
-        sampler.step(dfp, ctr[0])
-        ctr[0] += 1
-    mean, mn = time_kernel(torch, cfg, reps)
-    kern["cfg_step"] = {"us_mean": mean, "us_min": mn,
-                        "gbps": sampler.bytes / (mean * 1e-6) / 1e9,
-                        "frac_hbm_peak": sampler.bytes / (mean * 1e-6) / 1e9 / PEAK_HBM_GBPS,
-                        "bytes": sampler.bytes}
-
-    # displaced GroupNorm (the corrected_async_gn mode) on the workload's
-    # first U-Net level: 320 channels in 32 groups over the latent grid, one
-    # patch's row band; a DiT has no GroupNorm
-    if wl.name.startswith("sdxl") or wl.name == "tiny-f32":
-        _, _, hl, wdl = wl.latent
-        pg = wl.levels[0].P
-        gi = inputs.group_norm_inputs(2, 320, 32, (hl // pg) * wdl, pg, 1, wl.seed + 300)
-        gx = torch.from_numpy(gi.x).cuda()
-        gy = torch.empty_like(gx)
-        gst = torch.from_numpy(gi.stats).cuda()
-        gga, gbe = torch.from_numpy(gi.gamma).cuda(), torch.from_numpy(gi.beta).cuda()
-        gws = dfp.group_norm_workspace(2, 320, 32, (hl // pg) * wdl)
-        mean, mn = time_kernel(torch, lambda: dfp.displaced_group_norm(
-            gy, gx, gst, 32, 1, 1e-5, gga, gbe, True, gws), reps)
-        gb = 8 * gx.numel()   # x read, y written; the per-group sums are 0.02%
-        kern["displaced_group_norm"] = {
-            "us_mean": mean, "us_min": mn, "gbps": gb / (mean * 1e-6) / 1e9,
-            "frac_hbm_peak": gb / (mean * 1e-6) / 1e9 / PEAK_HBM_GBPS, "bytes": gb,
-            "shape": f"x [2, 320, {(hl // pg) * wdl}] (patch 1 of {pg}), 32 groups"}
-        del gx, gy, gst, gws
-
-    # the same fused step streaming a batch of 32 latents in one call: the
-    # kernel's bandwidth once the per-call latency (launch, reduction tail)
-    # is amortised
-    nb = 32
-    xs = torch.randn((nb, wl.n_latent), device="cuda")
-    gcs, gus = torch.randn_like(xs), torch.randn_like(xs)
-    rs = torch.empty(nb, device="cuda")
-    wss = dfp.cfg_workspace(wl.n_latent, nb)
-    c_x, c_e, _ = sampler.coeffs[-1]   # the last step's: c_x ~ 1, so repeats stay bounded
-    mean, mn = time_kernel(torch, lambda: dfp.cfg_step(xs, gcs, gus, wl.w, c_x, c_e, rs, wss),
-                           max(reps // 4, 5))
-    sb = 16 * xs.numel()
-    kern["cfg_step_batch32"] = {"us_mean": mean, "us_min": mn, "gbps": sb / (mean * 1e-6) / 1e9,
-                                "frac_hbm_peak": sb / (mean * 1e-6) / 1e9 / PEAK_HBM_GBPS,
-                                "bytes": sb}
-    del xs, gcs, gus
+    kern = time_levels(levels, sampler, dfp, torch, args.kernel_reps)
 
     dom = max(levels, key=lambda L: L.level.flops())
-    lv = dom.level
-    dom_ks = dfp.attention_plan(lv.B, lv.H, lv.n, lv.N_kv, lv.d, dom.ws is not None)[0]
-    dom_nf = (2 if dom.text else 1) if dom.fused else 0   # fresh ranges the launch reads
     dk = kern[f"attn_{dom.level.name}"]
-    traffic = measured_traffic(
-        os.path.join(ROOT, "patch_attention_cfg_amd", "csrc", "attention_bf16.hip"),
-        dom.level.name)
+    attn_src = "patch_attention_cfg_amd/csrc/attention_bf16.hip"
+    prof = os.path.join(ROOT, "profiles")
+    traffic = counted(os.path.join(prof, f"attn_bf16_{dom.level.name}_hbm_traffic.txt"),
+                      attn_src, "traffic_bytes")
+    clock = counted(os.path.join(prof, f"attn_bf16_{dom.level.name}_sq_counters.txt"),
+                    attn_src, "clock_ghz")
     roofline = {"bound": "mfma", "achieved": dk["tflops"], "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": dk["tflops"] / PEAK_BF16_TFLOPS, "traffic": traffic,
-                "kernel": f"attn_fwd_bf16<{dom.level.d}, {dom_ks}, {dom_nf}> "
-                          f"({dom.level.name}, "
+                "kernel": f"{dom.kernel_name()} ({dom.level.name}, "
                           f"{dom.level.flops() / 1e9:.2f} GFLOP per launch)"}
+    if clock:
+        pc = PEAK_BF16_TFLOPS * clock / PEAK_CLOCK_GHZ
+        roofline.update({"clock_ghz_measured": clock, "peak_at_measured_clock": pc,
+                         "frac_at_measured_clock": dk["tflops"] / pc})
+    ck = kern["cfg_step"]
+    cfg_src = "patch_attention_cfg_amd/csrc/cfg_step.hip"
+    cfg_prof = os.path.join(prof, f"cfg_step_{wl.name}_hbm_traffic.txt")
+    rd = counted(cfg_prof, cfg_src, "read_bytes")
+    wr = counted(cfg_prof, cfg_src, "write_bytes")
+    cfg_roofline = {"bound": "hbm", "achieved": ck["gbps"], "peak": PEAK_HBM_GBPS,
+                    "unit": "GB/s", "frac": ck["frac_hbm_peak"],
+                    "traffic": (rd + wr) if rd is not None and wr is not None else None,
+                    "kernel": f"cfg_step_kernel ({sampler.entry}, latent "
+                              f"{'x'.join(map(str, wl.latent))}, {sampler.bytes} B per launch)"}
+    del graph
+    keep = {"attn": [(L.level.name, L.kernel_name()) for L in levels]}
+    del levels, sampler
+    torch.cuda.empty_cache()
+
+    # ---- the other configurations' kernels, same run
+    configs = {}
+    for name in [c for c in args.configs.split(",") if c and c != wl.name]:
+        cw = inputs.WORKLOADS[name]
+        clv = [Level(lv, dfp, torch, inputs, False, not args.no_fresh) for lv in cw.levels]
+        csm = Sampler(cw, dfp, torch, inputs, args.eta, args.noise_array)
+        torch.cuda.synchronize()
+        for _ in range(2):
+            for L in clv:
+                L.run(dfp)
+            csm.step(dfp, 0)
+        ckern = time_levels(clv, csm, dfp, torch, args.kernel_reps)
+        configs[name] = {"workload": NAMES[name], "kernels": ckern}
+        print(f"[bench] {name}: kernels timed", file=sys.stderr, flush=True)
+        del clv, csm
+        torch.cuda.empty_cache()
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, inputs)
+        cpu = cpu_baseline(wl, inputs, args.cpu_seconds)
 
     out = {
         "metric": METRIC,
@@ -427,23 +508,23 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": {"sdxl1024": "SDXL-1024-shaped", "sdxl2048": "SDXL-2048-shaped",
-                         "sdxl3840": "SDXL-3840-shaped", "dit1024": "DiT/flow-shaped"}[wl.name]
+            "workload": NAMES[wl.name]
                         + (" one-device patch sweep: every patch of each attention level in order"
                            " + fused CFG step" if args.sweep else
                            " patch-parallel step: one patch per attention level + fused CFG step"),
-            "kv_landing": {L.level.name: "fused into the attention launch" if L.fused
-                           else "dfp_kv_scatter before the attention" for L in levels},
-            "attention": [f"{L.level.name}: B{L.level.B} H{L.level.H} n_q{L.level.n} "
-                          f"N_kv{L.level.N_kv} d{L.level.d} bf16" for L in levels],
+            "attention": [f"{lv.name}: B{lv.B} H{lv.H} n_q{lv.n} N_kv{lv.N_kv} d{lv.d} bf16"
+                          for lv in wl.levels],
+            "attention_kernels": dict(keep["attn"]),
             "latent": list(wl.latent), "sampler": f"{wl.sampler}{wl.steps} fp32"
-            + (f" eta={sampler.eta}" if sampler.eta > 0 else ""), "w": wl.w,
-            "launch": launch},
-        "cfg_step_gbps": kern["cfg_step"]["gbps"],
-        "cfg_step_frac_hbm_peak": kern["cfg_step"]["frac_hbm_peak"],
+            + (f" eta={args.eta}" if args.eta > 0 and wl.sampler == "ddim" else ""),
+            "w": wl.w, "launch": launch},
+        "cfg_step_gbps": ck["gbps"],
+        "cfg_step_frac_hbm_peak": ck["frac_hbm_peak"],
         "wall_s_timed": wall,
         "kernels": kern,
         "roofline": roofline,
+        "cfg_step_roofline": cfg_roofline,
+        "configs": configs,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out))

@@ -47,7 +47,8 @@
  *   - A launch error reported by the HIP runtime returns DFP_ERR_HIP.
  *     Faults inside a kernel surface at the caller's next synchronisation.
  *   - No entry point throws; none keeps state between calls except where a
- *     workspace is documented to (see dfp_cfg_step).
+ *     workspace is documented to (attention split-KV arrival counters,
+ *     displaced GroupNorm arrival counters).
  *   - bf16 tensors hold raw bfloat16 bit patterns (uint16_t).
  *   - Tensors are dense and row-major in the order their shape is written.
  *   - Calls that share a workspace must not overlap in time.
@@ -219,17 +220,13 @@ dfp_status dfp_patch_attention_fresh(void *o, const void *q, void *k_buf,
  *   g_c, g_u   [batch][n_per_image] fp32.
  *   relmae_out [batch] fp32 device memory, or NULL to skip the reduction.
  *   workspace  device scratch of >= dfp_workspace_bytes(DFP_OP_CFG_STEP,
- *              n_per_image, batch, ...) bytes, required when relmae_out is
- *              non-NULL.  It starts with one completion counter per image
- *              (4 bytes each, padded to a multiple of 256 bytes) that must
- *              be zero before the first call (e.g. allocate it zeroed);
- *              every call leaves them zero again.  The rest holds
- *              per-workgroup partial sums; as the counters' extent depends
- *              on batch, zero the workspace again before it serves calls
- *              with another batch, or keep one per batch.  Calls that share a workspace
- *              must not run concurrently.  The cross-workgroup sum runs
- *              in a fixed order in double precision, so results are
- *              bitwise reproducible.
+ *              n_per_image, batch, ...) bytes, 8-byte aligned, required when
+ *              relmae_out is non-NULL; its initial contents do not matter.
+ *              It receives one fp64 (sum, sum) pair per workgroup, which a
+ *              second launch of the call sums per image in a fixed order in
+ *              double precision, so results are bitwise reproducible for a
+ *              given size and entry point.  Calls that share a workspace
+ *              must not run concurrently.
  * Degenerate rel-MAE follows IEEE division (0/0 = NaN, x/0 = +Inf).
  * Errors: INVALID_ARG for null x/g_c/g_u, n_per_image <= 0, batch <= 0,
  * a missing or short workspace when relmae_out is non-NULL, non-finite
@@ -253,6 +250,44 @@ dfp_status dfp_cfg_step_noise(float *x, const float *g_c, const float *g_u,
                               float w, double c_x, double c_e, double c_z,
                               float *relmae_out, void *workspace,
                               size_t ws_bytes, hipStream_t stream);
+
+/* Fused step with the noise term drawn inside the kernel: DDIM with eta > 0
+ * ([AI] section 3, the sigma_eta * z term with z drawn by randn_like) at the
+ * 16 bytes per element of dfp_cfg_step.  Per element:
+ *   x <- c_x * x + c_e * g + c_z * z
+ * with z the standard-normal draw of this image and step from a counter-based
+ * generator, so any device (or the host) draws the same z:
+ *   elements 8j .. 8j+7 of image b (b = batch index of this call) come from
+ *   the Philox4x64-10 block (J. Salmon et al., "Parallel Random Numbers: As
+ *   Easy as 1, 2, 3", SC'11) of counter (j, b, 0, 0) under key (seed, step);
+ *   its four 64-bit words' 32-bit halves h_0..h_7 (h_2k the low half of word
+ *   k) become u_m = (h_m + 1/2) / 2^32, and Box-Muller gives
+ *     z[8j+2k]   = sqrt(-2 ln u_2k) cos(2 pi u_2k+1)
+ *     z[8j+2k+1] = sqrt(-2 ln u_2k) sin(2 pi u_2k+1).
+ * The device evaluates the transform in fp32 (|z - z_exact| stays within a
+ * few fp32 ulps of |z|).  seed, step: any 64-bit values; a sampler passes
+ * its seed and the step index.  rel-MAE, workspace rules and errors are
+ * those of dfp_cfg_step, plus INVALID_ARG for a non-finite c_z.  Reads 12
+ * bytes and writes 4 per element. */
+dfp_status dfp_cfg_step_philox(float *x, const float *g_c, const float *g_u,
+                               int64_t n_per_image, int batch, float w, double c_x,
+                               double c_e, double c_z, uint64_t seed, uint64_t step,
+                               float *relmae_out, void *workspace, size_t ws_bytes,
+                               hipStream_t stream);
+
+/* The draw z that dfp_cfg_step_philox adds, written out (same device code):
+ *   z  [batch][n_per_image] fp32 device output.
+ * Errors: INVALID_ARG for a null z, n_per_image <= 0, batch outside
+ * [1, 65535]. */
+dfp_status dfp_philox_normal(float *z, int64_t n_per_image, int batch, uint64_t seed,
+                             uint64_t step, hipStream_t stream);
+
+/* Raw Philox4x64-10 blocks (the generator under dfp_cfg_step_philox):
+ *   out [blocks][4] uint64 device output; block j is the generator applied to
+ *   counter (j, counter1, 0, 0) under key (key0, key1).
+ * blocks == 0 is a no-op.  Errors: INVALID_ARG for blocks < 0 or a null out. */
+dfp_status dfp_philox4x64_10(uint64_t *out, int64_t blocks, uint64_t counter1, uint64_t key0,
+                             uint64_t key1, hipStream_t stream);
 
 /* (a7) rel-MAE alone ([HY] 关键设计 2):
  *   out[b] = sum |g_c - g_u| / sum |g_u|  over image b's n_per_image values.

@@ -28,7 +28,9 @@ Draw recipe (numpy PCG64, standard_normal in float32), per attention level:
   nk, nv [B,H,N_kv,d]    noise;  stale = fresh + 0.05 * noise
 then every array is rounded to bf16 (nearest-even) for the bf16 workloads.
 Sampler stream (seed + 200): x_T [1,C,H,W], then per step g_c and g_u;
-sampler noise z for DDIM with eta > 0 comes from its own stream (seed + 300).
+sampler noise z for DDIM with eta > 0 comes from its own stream (seed + 300)
+when the caller draws it, or from the counter-based generator keyed by
+(seed + 300, step index) when the step draws it (noise_seed).
 Seeds: per workload (1001 ... 1005 in the order above); a workload's second
 attention level adds 100.
 
@@ -230,6 +232,12 @@ class SamplerStream:
         float32 N(0,1), from its own stream so the prediction draws do not
         depend on whether noise is drawn."""
         return self.noise_rng.standard_normal(self.workload.latent, dtype=np.float32)
+
+
+def noise_seed(workload: Workload) -> int:
+    """Seed of the sampler noise the fused step draws itself (the generator's
+    key is (noise_seed, step index))."""
+    return workload.seed + 300
 
 
 def sampler_stream(workload: Workload, seed: int | None = None) -> SamplerStream:

@@ -91,19 +91,31 @@ def assert_counters_zero(ws, BH: int, n_q: int, d: int = 64) -> None:
     assert int(ws[:n].sum().item()) == 0
 
 
-def sample_rows(n: int, BH: int, per_bh: int, seed: int):
-    """(bh, row) pairs: the first and last rows of every 32/128-row tile edge
-    near both ends, plus seeded random rows, for every (batch, head)."""
+def sample_rows(n: int, BH: int, block_m: int, total: int, seed: int):
+    """(bh, row) pairs for every (batch, head): the first and last rows of
+    the 32-, 64- and block_m-row tiles at both ends of the patch, every row
+    of the last (possibly partial) block_m tile, plus seeded random rows
+    spread over the (batch, head) slices until `total` random pairs."""
     rng = np.random.Generator(np.random.PCG64(seed))
-    fixed = {0, 1, 31, 32, 127, 128, n - 1, n - 2, n - 33, n - 129}
+    fixed = {0, 1, 31, 32, 63, 64, 127, 128, block_m - 1, block_m,
+             n - 1, n - 2, n - 33, n - 65, n - 129}
+    tail0 = (n - 1) // block_m * block_m          # first row of the last tile
+    fixed |= set(range(tail0, n))
+    fixed |= {tail0 - 1, tail0 - 2}
     fixed = sorted(r for r in fixed if 0 <= r < n)
-    bhs, rows = [], []
-    for bh in range(BH):
-        extra = rng.choice(n, size=min(per_bh, n), replace=False)
-        rr = sorted(set(fixed) | set(int(v) for v in extra))
-        bhs += [bh] * len(rr)
-        rows += rr
-    return np.array(bhs, dtype=np.int64), np.array(rows, dtype=np.int64)
+    extra_bh = rng.integers(0, BH, size=total)
+    extra_row = rng.integers(0, n, size=total)
+    pairs = {(bh, r) for bh in range(BH) for r in fixed}
+    pairs |= {(int(b), int(r)) for b, r in zip(extra_bh, extra_row)}
+    pairs = sorted(pairs)
+    return (np.array([b for b, _ in pairs], dtype=np.int64),
+            np.array([r for _, r in pairs], dtype=np.int64))
+
+
+def block_m_of(level, with_workspace: bool = True) -> int:
+    """Query rows per workgroup of the planner's launch for this level."""
+    ks = dfp.attention_plan(level.B, level.H, level.n, level.N_kv, level.d, with_workspace)[0]
+    return (128 if level.d == 64 else 256) // ks
 
 
 def rel_l2(a: np.ndarray, b: np.ndarray) -> float:

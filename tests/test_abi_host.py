@@ -158,7 +158,7 @@ def test_fresh_attention_null_range_array(L):
 
 def test_cfg_step_validation(L):
     ws_need = dfp.workspace_bytes(dfp.OP_CFG_STEP, 4096, 1)
-    assert ws_need > 256
+    assert ws_need >= 16   # one fp64 pair per workgroup
     cases = [
         ((NULL, FAKE, FAKE, 4096, 1, 7.5, 1.0, -0.5, NULL, NULL, 0), dfp.ERR_INVALID_ARG),
         ((FAKE, NULL, FAKE, 4096, 1, 7.5, 1.0, -0.5, NULL, NULL, 0), dfp.ERR_INVALID_ARG),
@@ -179,10 +179,26 @@ def test_cfg_step_validation(L):
     assert L.dfp_relmae(FAKE, FAKE, 4096, 1, FAKE, NULL, 0, S0) == dfp.ERR_INVALID_ARG
 
 
+def test_philox_entry_validation(L):
+    ws_need = dfp.workspace_bytes(dfp.OP_CFG_STEP, 4096, 1)
+    base = (FAKE, FAKE, FAKE, 4096, 1, 7.5, 1.0, -0.5, 0.1, 5, 3)
+    assert L.dfp_cfg_step_philox(*base, FAKE, NULL, 0, S0) == dfp.ERR_INVALID_ARG
+    assert L.dfp_cfg_step_philox(*base[:8], float("nan"), 5, 3, NULL, NULL, 0,
+                                 S0) == dfp.ERR_INVALID_ARG
+    assert L.dfp_cfg_step_philox(NULL, *base[1:], NULL, NULL, 0, S0) == dfp.ERR_INVALID_ARG
+    assert L.dfp_cfg_step_philox(*base, FAKE, FAKE, ws_need - 1, S0) == dfp.ERR_INVALID_ARG
+    assert L.dfp_philox_normal(NULL, 16, 1, 0, 0, S0) == dfp.ERR_INVALID_ARG
+    assert L.dfp_philox_normal(FAKE, 0, 1, 0, 0, S0) == dfp.ERR_INVALID_ARG
+    assert L.dfp_philox_normal(FAKE, 16, 0, 0, 0, S0) == dfp.ERR_INVALID_ARG
+    assert L.dfp_philox4x64_10(NULL, 4, 0, 0, 0, S0) == dfp.ERR_INVALID_ARG
+    assert L.dfp_philox4x64_10(FAKE, -1, 0, 0, 0, S0) == dfp.ERR_INVALID_ARG
+    assert L.dfp_philox4x64_10(NULL, 0, 0, 0, 0, S0) == dfp.OK   # nothing to do
+
+
 def test_workspace_sizes_grow_with_batch(L):
     a = dfp.workspace_bytes(dfp.OP_CFG_STEP, 921600, 1)
     b = dfp.workspace_bytes(dfp.OP_CFG_STEP, 921600, 2)
-    assert b > a > 256
+    assert b == 2 * a and a > 256
     assert dfp.workspace_bytes(dfp.OP_RELMAE, 921600, 1) == a
     assert dfp.workspace_bytes(99) == 0
 

@@ -2,9 +2,9 @@
 
 Bars: fp32 path max-abs <= 1e-4; bf16 path relative L2 <= 1e-2 and max-abs
 <= 2e-2 (over every checked element).  Small workloads are checked on every
-output element; the SDXL-2048/3840 and DiT workloads on seeded samples of
-rows that include the first and last rows of the tiles at both ends of the
-patch, with every (batch, head).
+output element; the SDXL-2048/3840 and DiT workloads on at least 2048 seeded
+(batch*head, row) pairs per patch plus, for every (batch, head), the tile
+edge rows at both ends and every row of the last query tile.
 """
 import numpy as np
 import pytest
@@ -57,25 +57,60 @@ def test_full_patch_every_element(name, p):
     _check(got, want, level.dtype, f"{name} p{p}")
 
 
-@pytest.mark.parametrize("name,p,per_bh", [("sdxl2048", 0, 24), ("sdxl2048", 7, 24), ("sdxl3840", 3, 12),
-                                           ("sdxl3840", 7, 8), ("dit1024", 0, 24), ("dit1024", 2, 24)])
-def test_large_patch_sampled_rows(name, p, per_bh):
+SAMPLE_PAIRS = 2048   # seeded random (batch*head, row) pairs per patch, beyond the tile edges
+
+
+@pytest.mark.parametrize("name,p", [("sdxl2048", 0), ("sdxl2048", 7), ("sdxl3840", 0),
+                                    ("sdxl3840", 3), ("sdxl3840", 7), ("dit1024", 0),
+                                    ("dit1024", 2), ("dit1024", 3)])
+def test_large_patch_sampled_rows(name, p):
+    """Every (batch, head) of the patch in the launch the benchmark runs: at
+    least 2048 seeded random (batch*head, row) pairs plus, for every (batch,
+    head), the edge rows of the 32/64/128-row tiles at both ends and every
+    row of the last query tile of the planner's launch (SDXL-3840: rows
+    7168-7199), against the oracle.  Where the patch's rows are whole 64-key
+    tiles (SDXL-2048, DiT-1024) the fused call (reading the fresh rows from
+    this step's tensors and landing them) is also run and must equal
+    scatter + attention bit for bit on every element of every head."""
     G.require_gpu()
+    torch = G.torch_mod()
     level = inputs.LEVELS[name]
-    G.announce(f"attention {name} patch {p} (sampled rows)")
     x = _inputs(name)
+    block_m = G.block_m_of(level)
+    BH = level.B * level.H
+    bh, rows = G.sample_rows(level.n, BH, block_m, SAMPLE_PAIRS, seed=7 + p)
+    G.announce(f"attention {name} patch {p}: {bh.size} sampled (bh, row) pairs, "
+               f"block_m {block_m}")
     got = G.run_patch(level, x, p)
     k_eff = oracle.effective_kv(x.k_stale, x.fresh_rows(p)[0], level.row0(p))
     v_eff = oracle.effective_kv(x.v_stale, x.fresh_rows(p)[1], level.row0(p))
     if level.n_text:
         k_eff = oracle.effective_kv(k_eff, x.text_rows()[0], 0)
         v_eff = oracle.effective_kv(v_eff, x.text_rows()[1], 0)
-    BH = level.B * level.H
-    bh, rows = G.sample_rows(level.n, BH, per_bh, seed=7 + p)
     want = oracle.attention_rows(x.q_patch(p), k_eff, v_eff, 1.0 / level.d ** 0.5, bh, rows)
     got_rows = got.reshape(BH, level.n, level.d)[bh, rows]
     _check(got_rows, want, "bf16", f"{name} p{p} sampled")
     assert np.isfinite(got).all()
+    if level.n % 64 == 0 and level.row0(p) % 64 == 0 and level.n_text % 64 == 0:
+        G.announce(f"attention {name} patch {p}: fused call, every element vs scatter path")
+        k_buf, v_buf = dfp.alloc_kv_buffer(level.B, level.H, level.N_kv, level.d,
+                                           torch.bfloat16)
+        dfp.kv_scatter(k_buf, v_buf, G.up(x.k_stale, "bf16"), G.up(x.v_stale, "bf16"), 0)
+        kf, vf = x.fresh_rows(p)
+        ranges = []
+        if level.n_text:
+            kt, vt = x.text_rows()
+            ranges.append((G.up(kt, "bf16"), G.up(np.swapaxes(vt, -1, -2), "bf16"), 0))
+        ranges.append((G.up(kf, "bf16"), G.up(np.swapaxes(vf, -1, -2), "bf16"), level.row0(p)))
+        q = G.up(x.q_patch(p), "bf16")
+        o = torch.empty_like(q)
+        ws = dfp.attention_workspace(level.B, level.H, level.n, level.N_kv, level.d)
+        dfp.patch_attention_fresh(o, q, k_buf, v_buf, ranges, True, 1.0 / level.d ** 0.5, ws)
+        torch.cuda.synchronize()
+        fused = G.down(o)
+        np.testing.assert_array_equal(fused.view(np.uint32), got.view(np.uint32))
+        if ws is not None:
+            G.assert_counters_zero(ws, BH, level.n, level.d)
 
 
 @pytest.mark.parametrize("kind", ["bf16", "f32"])

@@ -47,7 +47,7 @@ def test_sampler_run_step_by_step(name):
     sch = _schedule(wl)
     batch = wl.latent[0]
     n = wl.n_latent
-    ws = dfp.cfg_workspace(n, batch)
+    ws = dfp.cfg_workspace(n, batch).fill_(255)   # initial contents must not matter
     r_dev = torch.empty(batch, dtype=torch.float32, device="cuda")
     x_host = stream.x_T.astype(np.float32)
     x_ref_traj = x_host.astype(np.float64)
@@ -71,7 +71,6 @@ def test_sampler_run_step_by_step(name):
         assert rerr <= RELMAE_REL, f"{name} step {i}: rel-MAE {r_got} vs {r_want}"
         x_ref_traj, _ = sch.step(x_ref_traj, g_c, g_u, wl.w, i)
         x_host = got
-    assert int(ws[:4].view(torch.int32)[0].item()) == 0   # counter left at zero
     traj = G.rel_l2(x_host, x_ref_traj)
     G.announce(f"{name}: worst step relL2 {worst_step:.2e}, worst rel-MAE err {worst_r:.2e}, "
                f"full-trajectory relL2 {traj:.2e}")
@@ -136,12 +135,11 @@ def test_relmae_alone_batch_and_determinism():
     dfp.relmae(dc, du, out, ws)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(out.cpu().numpy(), a)
-    assert int(ws[:3 * 4].sum().item()) == 0      # every image's counter left at zero
 
 
 def test_relmae_many_images_one_call():
-    """Batch 70 in one call (one completion counter per image, several
-    256-byte counter blocks): every image's ratio against the oracle."""
+    """Batch 70 in one call (one merge workgroup per image): every image's
+    ratio against the oracle."""
     G.require_gpu()
     G.announce("relmae batch=70")
     torch = G.torch_mod()
@@ -158,7 +156,6 @@ def test_relmae_many_images_one_call():
     for b in range(batch):
         want = oracle.relmae(g_c[b], g_u[b])
         assert abs(got[b] - want) / want <= RELMAE_REL, f"image {b}"
-    assert int(ws[:batch * 4].sum().item()) == 0
 
 
 @pytest.mark.parametrize("n,offset", [(1001, 0), (4096, 1), (3, 0), (1, 0)])
@@ -235,7 +232,7 @@ def test_random_shape(i):
     per image, 1-5 images per call), x and the predictions on and off the
     16-byte grid, DDIM (also its last step and eta > 0) and Euler updates,
     any guidance weight, with and without the rel-MAE output: every image's
-    step and rel-MAE against the oracle, the counters back at zero."""
+    step and rel-MAE against the oracle, from a workspace of arbitrary bytes."""
     c = _random_case(i)
     G.require_gpu()
     G.announce(f"cfg step random case {i}: {c}")
@@ -252,7 +249,7 @@ def test_random_shape(i):
     xs, x = dev(x0)
     out = torch.full((B,), float("nan"), dtype=torch.float32, device="cuda") \
         if c["with_relmae"] else None
-    ws = dfp.cfg_workspace(n, B) if c["with_relmae"] else None
+    ws = dfp.cfg_workspace(n, B).fill_(0xA5) if c["with_relmae"] else None
     args = (dev(g_c)[1], dev(g_u)[1])
     kind = c["kind"]
     if kind == "eta":
@@ -279,5 +276,3 @@ def test_random_shape(i):
             rw = oracle.relmae(g_c[b], g_u[b])
             assert abs(out[b].item() - rw) / rw <= RELMAE_REL, f"image {b}"
     assert torch.isnan(xs[off + B * n:]).all() and torch.isnan(xs[:off]).all()
-    if ws is not None:
-        assert int(ws[:B * 4].sum().item()) == 0

@@ -78,7 +78,6 @@ def test_graph_replays_match_eager(monkeypatch):
         np.testing.assert_array_equal(x_g.cpu().numpy(), want_x[i], err_msg=f"replay {i} latent")
         np.testing.assert_array_equal(r_g.cpu().numpy(), want_r[i], err_msg=f"replay {i} rel-MAE")
         G.assert_counters_zero(ws, B * H, nq, d)
-        assert int(cws[:4].view(torch.int32)[0].item()) == 0
         # eager work on the same workspace between replays
         dfp.patch_attention(other, qd, k_buf, v_buf, None, ws)
         torch.cuda.synchronize()
