@@ -220,12 +220,12 @@ dfp_status dfp_patch_attention_fresh(void *o, const void *q, void *k_buf,
  *   g_c, g_u   [batch][n_per_image] fp32.
  *   relmae_out [batch] fp32 device memory, or NULL to skip the reduction.
  *   workspace  device scratch of >= dfp_workspace_bytes(DFP_OP_CFG_STEP,
- *              n_per_image, batch, ...) bytes, 8-byte aligned, required when
+ *              n_per_image, batch, ...) bytes, 16-byte aligned, required when
  *              relmae_out is non-NULL; its initial contents do not matter.
  *              It receives one fp64 (sum, sum) pair per workgroup, which a
- *              second launch of the call sums per image in a fixed order in
- *              double precision, so results are bitwise reproducible for a
- *              given size and entry point.  Calls that share a workspace
+ *              second launch of the call (one wavefront per image) sums in
+ *              a fixed order in double precision, so results are bitwise
+ *              reproducible for a given size and entry point.  Calls that share a workspace
  *              must not run concurrently.
  * Degenerate rel-MAE follows IEEE division (0/0 = NaN, x/0 = +Inf).
  * Errors: INVALID_ARG for null x/g_c/g_u, n_per_image <= 0, batch <= 0,

@@ -331,30 +331,33 @@ __global__ __launch_bounds__(kThreads) void cfg_step_kernel(
     if (UPDATE && last >= 0) update_pass(last);
 }
 
-// Second launch: one workgroup per image sums the image's workgroup partials
+// Second launch: one wavefront per image sums the image's workgroup partials
 // in a fixed order (fp64) and writes the ratio.  The launch boundary orders
-// it after every partial store of the first launch.
-__global__ __launch_bounds__(kThreads) void cfg_merge_kernel(const double *__restrict__ partials,
-                                                             int nblk, float *__restrict__ out) {
-    const int img = blockIdx.x, tid = threadIdx.x;
-    __shared__ double snum[kThreads], sden[kThreads];
+// it after every partial store of the first launch.  Lane l adds partials
+// l, l + 64, ... in order, with up to kMergeLoads of them loaded at once,
+// then a fixed butterfly combines the lanes.
+constexpr int kMergeLoads = 8;
+__global__ __launch_bounds__(dfp::kWave) void cfg_merge_kernel(const double *__restrict__ partials,
+                                                               int nblk, float *__restrict__ out) {
+    const int img = blockIdx.x, lane = threadIdx.x;
+    const double2 *p = reinterpret_cast<const double2 *>(partials) + (int64_t)img * nblk;
     double a = 0.0, b = 0.0;
-    const double *p = partials + 2 * (int64_t)img * nblk;
-    for (int k = tid; k < nblk; k += kThreads) {
-        a += p[2 * k];
-        b += p[2 * k + 1];
-    }
-    snum[tid] = a;
-    sden[tid] = b;
-    __syncthreads();
-    for (int s = kThreads / 2; s > 0; s >>= 1) {
-        if (tid < s) {
-            snum[tid] += snum[tid + s];
-            sden[tid] += sden[tid + s];
+    for (int k0 = lane; k0 < nblk; k0 += dfp::kWave * kMergeLoads) {
+        double2 v[kMergeLoads];
+#pragma unroll
+        for (int j = 0; j < kMergeLoads; ++j) {
+            const int k = k0 + j * dfp::kWave;
+            v[j] = k < nblk ? p[k] : make_double2(0.0, 0.0);
         }
-        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < kMergeLoads; ++j) {
+            a += v[j].x;
+            b += v[j].y;
+        }
     }
-    if (tid == 0) out[img] = (float)(snum[0] / sden[0]);
+    a = dfp::wave_sum(a);
+    b = dfp::wave_sum(b);
+    if (lane == 0) out[img] = (float)(a / b);
 }
 
 // Fill z with the draw the fused step uses (same device code).
@@ -405,7 +408,7 @@ dfp_status launch(float *x, const float *g_c, const float *g_u, const NoiseArgs 
         return DFP_ERR_INVALID_ARG;
     const int reduce = out != nullptr;
     if (reduce && (!ws || ws_bytes < workspace_need(n, batch) ||
-                   (reinterpret_cast<uintptr_t>(ws) % 8) != 0))
+                   (reinterpret_cast<uintptr_t>(ws) % 16) != 0))
         return DFP_ERR_INVALID_ARG;
     const int item = nz.kind == kNoisePhilox ? 8 : 4;
     const bool vec = (n % item == 0) && (reinterpret_cast<uintptr_t>(g_c) % 16 == 0) &&
@@ -432,7 +435,7 @@ dfp_status launch(float *x, const float *g_c, const float *g_u, const NoiseArgs 
     }
 #undef DFP_CFG_LAUNCH
     if (reduce)
-        hipLaunchKernelGGL(cfg_merge_kernel, dim3((unsigned)batch), dim3(kThreads), 0, stream,
+        hipLaunchKernelGGL(cfg_merge_kernel, dim3((unsigned)batch), dim3(dfp::kWave), 0, stream,
                            partials, (int)grid.x, out);
     return dfp::launch_status();
 }
