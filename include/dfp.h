@@ -69,7 +69,8 @@ typedef enum {
     DFP_OK = 0,
     DFP_ERR_INVALID_ARG = 1,  /* null pointer, negative or inconsistent size */
     DFP_ERR_UNSUPPORTED = 2,  /* valid request the kernels do not implement  */
-    DFP_ERR_HIP = 3           /* the HIP runtime rejected a launch           */
+    DFP_ERR_HIP = 3,          /* the HIP runtime rejected a launch           */
+    DFP_ERR_TOO_LARGE = 4     /* exceeds the library's static scratch        */
 } dfp_status;
 
 typedef enum {
@@ -288,6 +289,27 @@ dfp_status dfp_philox_normal(float *z, int64_t n_per_image, int batch, uint64_t 
  * blocks == 0 is a no-op.  Errors: INVALID_ARG for blocks < 0 or a null out. */
 dfp_status dfp_philox4x64_10(uint64_t *out, int64_t blocks, uint64_t counter1, uint64_t key0,
                              uint64_t key1, hipStream_t stream);
+
+/* dfp_cfg_step for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments and results as dfp_cfg_step without the workspace: the
+ * rel-MAE partials go to a static device array of
+ * dfp_cfg_static_scratch_bytes() bytes (1 MiB) inside the library, one per
+ * GPU, kept until the process ends.  Nothing in it needs initial contents.
+ * The call allocates nothing (no hipMalloc, no allocating library
+ * routine); its first call on a device looks the array's device address up
+ * once.  Every call on one GPU shares that GPU's array: calls that overlap
+ * in time on one GPU (different streams without ordering, several host
+ * threads) race and may return wrong rel-MAE values.
+ * Errors: those of dfp_cfg_step, and DFP_ERR_TOO_LARGE (nothing enqueued)
+ * when relmae_out is non-NULL and dfp_workspace_bytes(DFP_OP_CFG_STEP,
+ * n_per_image, batch, ...) exceeds dfp_cfg_static_scratch_bytes(). */
+dfp_status dfp_cfg_step_static(float *x, const float *g_c, const float *g_u,
+                               int64_t n_per_image, int batch, float w, double c_x,
+                               double c_e, float *relmae_out, hipStream_t stream);
+
+/* Size in bytes of the static scratch of dfp_cfg_step_static. */
+size_t dfp_cfg_static_scratch_bytes(void);
 
 /* (a7) rel-MAE alone ([HY] 关键设计 2):
  *   out[b] = sum |g_c - g_u| / sum |g_u|  over image b's n_per_image values.

@@ -34,6 +34,7 @@
 // one counter, about 14 ns per workgroup of serialized atomics; the
 // following launch is cheaper than either.)
 #include <cmath>
+#include <mutex>
 
 #include "dfp_common.h"
 #include "dfp_internal.h"
@@ -480,6 +481,53 @@ extern "C" dfp_status dfp_cfg_step_philox(float *x, const float *g_c, const floa
     const NoiseArgs nz{kNoisePhilox, nullptr, (float)c_z, seed, step};
     return launch<true>(x, g_c, g_u, nz, n_per_image, batch, w, (float)c_x, (float)c_e,
                         relmae_out, workspace, ws_bytes, stream);
+}
+
+// ------------------------------------------------------ no-allocation step
+// Scratch of dfp_cfg_step_static: the per-workgroup rel-MAE partials in a
+// file-scope device array, one copy per GPU, held until the process ends.
+// Host code never uses this name as an address: each device's copy is found
+// with hipGetSymbolAddress on the first call on that device.
+constexpr size_t kStaticScratchBytes = size_t(1) << 20;
+static __device__ __align__(256) double scratch[kStaticScratchBytes / sizeof(double)];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's copy of `scratch`, looked up once per device.
+dfp_status static_scratch(void **out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return DFP_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return DFP_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return DFP_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return DFP_OK;
+}
+
+extern "C" size_t dfp_cfg_static_scratch_bytes(void) { return kStaticScratchBytes; }
+
+extern "C" dfp_status dfp_cfg_step_static(float *x, const float *g_c, const float *g_u,
+                                          int64_t n_per_image, int batch, float w, double c_x,
+                                          double c_e, float *relmae_out, hipStream_t stream) {
+    if (!std::isfinite(w) || !std::isfinite(c_x) || !std::isfinite(c_e))
+        return DFP_ERR_INVALID_ARG;
+    if (!x || !g_c || !g_u || n_per_image <= 0 || batch <= 0 || batch > 65535)
+        return DFP_ERR_INVALID_ARG;
+    void *ws = nullptr;
+    if (relmae_out) {
+        if (workspace_need(n_per_image, batch) > kStaticScratchBytes) return DFP_ERR_TOO_LARGE;
+        const dfp_status st = static_scratch(&ws);
+        if (st != DFP_OK) return st;
+    }
+    const NoiseArgs nz{kNoNoise, nullptr, 0.f, 0, 0};
+    return launch<true>(x, g_c, g_u, nz, n_per_image, batch, w, (float)c_x, (float)c_e,
+                        relmae_out, ws, relmae_out ? kStaticScratchBytes : 0, stream);
 }
 
 extern "C" dfp_status dfp_relmae(const float *g_c, const float *g_u, int64_t n_per_image,

@@ -15,6 +15,8 @@ const char *dfp_status_string(dfp_status s) {
     case DFP_ERR_INVALID_ARG: return "DFP_ERR_INVALID_ARG: invalid argument";
     case DFP_ERR_UNSUPPORTED: return "DFP_ERR_UNSUPPORTED: shape or dtype not implemented";
     case DFP_ERR_HIP: return "DFP_ERR_HIP: the HIP runtime rejected a launch";
+    case DFP_ERR_TOO_LARGE:
+        return "DFP_ERR_TOO_LARGE: the request exceeds the library's static scratch buffer";
     }
     return "unknown dfp_status";
 }

@@ -16,7 +16,7 @@ import numpy as np
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libdfp.so")
 
-OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP = 0, 1, 2, 3
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP, ERR_TOO_LARGE = 0, 1, 2, 3, 4
 F32, BF16 = 0, 1
 OP_CFG_STEP, OP_RELMAE, OP_PATCH_ATTENTION = 0, 1, 2
 _M64 = 2**64 - 1
@@ -37,6 +37,8 @@ SIGNATURES = {
                                  _SZ, _P]),
     "dfp_philox_normal": (_I, [_P, _I64, _I, _U64, _U64, _P]),
     "dfp_philox4x64_10": (_I, [_P, _I64, _U64, _U64, _U64, _P]),
+    "dfp_cfg_step_static": (_I, [_P, _P, _P, _I64, _I, _F, _D, _D, _P, _P]),
+    "dfp_cfg_static_scratch_bytes": (_SZ, []),
     "dfp_relmae": (_I, [_P, _P, _I64, _I, _P, _P, _SZ, _P]),
     "dfp_workspace_bytes": (_SZ, [_I, _I64, _I, _I, _I, _I, _I, _I]),
     "dfp_attention_plan": (_I, [_I, _I, _I, _I, _I, _I, _P, _P, _P]),
@@ -378,6 +380,16 @@ def cfg_step(x, g_c, g_u, w: float, c_x: float, c_e: float, relmae_out=None, wor
                             float(c_e), _ptr(relmae_out), _ptr(workspace), _ws_bytes(workspace),
                             _stream(stream))
     _check(st, "dfp_cfg_step")
+
+
+def cfg_step_static(x, g_c, g_u, w: float, c_x: float, c_e: float, relmae_out=None,
+                    stream=None) -> None:
+    """dfp_cfg_step without a workspace: the partials use the library's
+    static scratch (for callers that cannot allocate)."""
+    batch, n = _check_latent(x, g_c, g_u, None, relmae_out, None)
+    st = lib().dfp_cfg_step_static(_ptr(x), _ptr(g_c), _ptr(g_u), n, batch, float(w),
+                                   float(c_x), float(c_e), _ptr(relmae_out), _stream(stream))
+    _check(st, "dfp_cfg_step_static")
 
 
 def cfg_step_noise(x, g_c, g_u, z, w: float, c_x: float, c_e: float, c_z: float,
