@@ -299,6 +299,31 @@ def time_levels(levels, sampler, dfp, torch, reps):
     return kern
 
 
+def time_group_norm(wl, dfp, torch, inputs, reps):
+    """Displaced GroupNorm (the corrected_async_gn mode) on the workload's
+    first U-Net level: 320 channels in 32 groups over the latent grid, one
+    patch's row band, batch 2, with a workspace (the whole-GPU path).  A DiT
+    has no GroupNorm.  8 algorithmic bytes per element (x read, y written);
+    the per-group sums are a few KB."""
+    if not wl.name.startswith("sdxl"):
+        return None
+    _, _, hl, wdl = wl.latent
+    pg = wl.levels[0].P
+    n = (hl // pg) * wdl
+    gi = inputs.group_norm_inputs(2, 320, 32, n, pg, 1, wl.seed + 300)
+    gx = torch.from_numpy(gi.x).cuda()
+    gy = torch.empty_like(gx)
+    gst = torch.from_numpy(gi.stats).cuda()
+    gga, gbe = torch.from_numpy(gi.gamma).cuda(), torch.from_numpy(gi.beta).cuda()
+    gws = dfp.group_norm_workspace(2, 320, 32, n)
+    mean, mn = time_kernel(torch, lambda: dfp.displaced_group_norm(
+        gy, gx, gst, 32, 1, 1e-5, gga, gbe, True, gws), reps)
+    gb = 8 * gx.numel()
+    return {"us_mean": mean, "us_min": mn, "gbps": gb / (mean * 1e-6) / 1e9,
+            "frac_hbm_peak": gb / (mean * 1e-6) / 1e9 / PEAK_HBM_GBPS, "bytes": gb,
+            "shape": f"x [2, 320, {n}] (patch 1 of {pg}), 32 groups"}
+
+
 def cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as fh:
@@ -441,6 +466,9 @@ def main():
 
     # ---- per-kernel durations (HIP events on the launch stream)
     kern = time_levels(levels, sampler, dfp, torch, args.kernel_reps)
+    gn = time_group_norm(wl, dfp, torch, inputs, max(args.kernel_reps, 50))
+    if gn:
+        kern["displaced_group_norm"] = gn
 
     dom = max(levels, key=lambda L: L.level.flops())
     dk = kern[f"attn_{dom.level.name}"]
@@ -485,6 +513,9 @@ def main():
                 L.run(dfp)
             csm.step(dfp, 0)
         ckern = time_levels(clv, csm, dfp, torch, args.kernel_reps)
+        cgn = time_group_norm(cw, dfp, torch, inputs, max(args.kernel_reps, 50))
+        if cgn:
+            ckern["displaced_group_norm"] = cgn
         configs[name] = {"workload": NAMES[name], "kernels": ckern}
         print(f"[bench] {name}: kernels timed", file=sys.stderr, flush=True)
         del clv, csm

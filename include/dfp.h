@@ -47,8 +47,7 @@
  *   - A launch error reported by the HIP runtime returns DFP_ERR_HIP.
  *     Faults inside a kernel surface at the caller's next synchronisation.
  *   - No entry point throws; none keeps state between calls except where a
- *     workspace is documented to (attention split-KV arrival counters,
- *     displaced GroupNorm arrival counters).
+ *     workspace is documented to (the attention split-KV arrival counters).
  *   - bf16 tensors hold raw bfloat16 bit patterns (uint16_t).
  *   - Tensors are dense and row-major in the order their shape is written.
  *   - Calls that share a workspace must not overlap in time.
@@ -339,18 +338,17 @@ dfp_status dfp_relmae(const float *g_c, const float *g_u, int64_t n_per_image,
  *                        p is ignored on input; with land != 0 it receives
  *                        (f1, f2) for the next step.
  *   gamma, beta  [C] fp32, or NULL (1 and 0).
- *   workspace/ws_bytes  optional device scratch (may be NULL/0), 256-byte
- *           aligned.  Groups of up to 64 Ki floats of the patch (C/G * n)
- *           need none.  For longer groups, with at least
- *           dfp_group_norm_workspace_bytes(B, C, G, n) bytes the work is
- *           spread over the whole GPU in two launches; without it one
- *           workgroup per (image, group) does it.  The workspace starts
- *           with one arrival counter per (image, group) that must be zero
- *           before the first call (allocate it zeroed); every call leaves
- *           them zero.  As their extent depends on B and G, zero the
- *           workspace again before it serves calls of other sizes, or keep
- *           one per size.  Calls that share a workspace must not run
- *           concurrently.
+ *   workspace/ws_bytes  optional device scratch (may be NULL/0), 8-byte
+ *           aligned; its initial contents do not matter.  A patch's group
+ *           of up to 64 Ki floats (C/G * n, with n % 4 == 0 and x, y 16-byte
+ *           aligned) needs none: one workgroup per (image, group) holds it
+ *           in registers (one read of x).  Longer groups, with at least
+ *           dfp_group_norm_workspace_bytes(B, C, G, n) bytes, are cut into
+ *           chunks of 4 Ki floats spread over the whole GPU in two launches
+ *           (chunk sums, then statistics and normalization; x is read
+ *           twice, the second time mostly from cache); without it one
+ *           workgroup per (image, group) streams x twice.  Calls that share
+ *           a workspace must not run concurrently.
  * The statistics are bitwise reproducible (fixed-order fp64 sums).
  * Errors: INVALID_ARG for null y/x/stats, non-positive B/C/G/n/P, C not a
  * multiple of G, p outside [0, P), negative or non-finite eps, misaligned

@@ -14,15 +14,19 @@
 // variance S2/N - mean^2, eps inside the square root.
 //
 // The group's C/G channels of the patch are one contiguous run of C/G * n
-// floats.  Runs of up to 64 Ki floats: one workgroup per (image, group)
-// keeps its run in registers between the two uses (one read of x).  Longer
-// runs, given a workspace: two launches over chunks of every run, across
-// the whole GPU -- partial sums published per chunk, the last chunk of each
-// group to arrive forms the statistics (and lands the fresh sums); then
-// every chunk normalizes.  Without a workspace one workgroup streams each
-// run twice.  Sums are fp64 per thread, per wavefront (fixed butterfly) and
-// across wavefronts and chunks in a fixed order, so the statistics are
-// bitwise reproducible.
+// floats.  Runs of up to 64 Ki floats (n % 4 == 0, x and y 16-byte aligned):
+// one workgroup per (image, group) keeps its run in registers between the
+// two uses, so x is read once.  Longer runs, given a workspace: every run is
+// cut into chunks of 4 Ki floats spread over the whole GPU, in two launches
+// -- launch 1 stores each chunk's fp64 sums; launch 2 has every chunk add its
+// group's chunk sums in chunk order (the same order in every chunk, so all
+// agree bit for bit), form the statistics, normalize its floats (which
+// launch 1 just read, so they mostly come back from cache), and the group's
+// first chunk lands the fresh sums.  No atomics and no counters: the launch
+// boundary orders the two.  Otherwise one workgroup streams each run twice.
+// Sums are fp64 per thread, per wavefront (fixed butterfly) and across
+// wavefronts and chunks in a fixed order, so the statistics are bitwise
+// reproducible.
 #include <cmath>
 
 #include "dfp_common.h"
@@ -33,11 +37,11 @@ constexpr int kGnThreads = 1024;
 constexpr int kGnWaves = kGnThreads / dfp::kWave;
 constexpr int kGnVec = 16;   // float4 per thread held in registers
 constexpr int64_t kGnResidentFloats = (int64_t)kGnThreads * kGnVec * 4;
-// Chunked path: 256-thread workgroups over 16 Ki-float chunks (16 floats per
-// thread per pass), at most kGnMaxChunks per run.
+// Chunked path: 256-thread workgroups over 4 Ki-float chunks (16 floats per
+// thread), at most kGnMaxChunks per run (longer chunks beyond).
 constexpr int kGcThreads = 256;
 constexpr int kGcWaves = kGcThreads / dfp::kWave;
-constexpr int64_t kGcChunk = (int64_t)kGcThreads * 16 * 4;
+constexpr int64_t kGcChunk = (int64_t)kGcThreads * 4 * 4;
 constexpr int kGnMaxChunks = 4096;
 
 int64_t run_chunks(int64_t run) {
@@ -51,10 +55,8 @@ __host__ __device__ inline int64_t chunk_span(int64_t run, int nch, bool vec) {
     const int64_t per = (run + nch - 1) / nch;
     return vec ? (per + 3) / 4 * 4 : per;
 }
-size_t gn_counter_bytes(int64_t groups) { return ((size_t)groups * 4 + 255) / 256 * 256; }
 size_t gn_workspace_need(int64_t groups, int64_t chunks) {
-    return gn_counter_bytes(groups) + (size_t)groups * chunks * 2 * sizeof(double) +
-           (size_t)groups * 2 * sizeof(float);
+    return (size_t)groups * chunks * 2 * sizeof(double);
 }
 
 struct GnArgs {
@@ -197,14 +199,10 @@ __global__ __launch_bounds__(kGnThreads) void gn_stream_kernel(GnArgs a) {
 }
 
 // Chunked path, launch 1: chunk blockIdx.x of group (blockIdx.y, blockIdx.z)
-// sums its floats and publishes them; the last chunk of the group to
-// arrive adds the chunks' sums in chunk order, forms the statistics, lands
-// the fresh sums and resets the counter.  VEC: float4 loads (n % 4 == 0,
-// x 16-byte aligned).
+// sums its floats and stores the pair.  VEC: float4 loads (n % 4 == 0, x
+// 16-byte aligned).
 template <bool VEC>
-__global__ __launch_bounds__(kGcThreads) void gn_chunk_sums_kernel(GnArgs a, double *partials,
-                                                                   unsigned *counters,
-                                                                   float *mean_rstd) {
+__global__ __launch_bounds__(kGcThreads) void gn_chunk_sums_kernel(GnArgs a, double *partials) {
     const int chunk = blockIdx.x, nch = gridDim.x, g = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x;
     const int64_t run = (int64_t)(a.C / a.G) * a.n;
@@ -224,32 +222,20 @@ __global__ __launch_bounds__(kGcThreads) void gn_chunk_sums_kernel(GnArgs a, dou
         }
     }
     block_sums<kGcWaves>(s1, s2);
-    __shared__ int is_last;
-    const int64_t grp = (int64_t)b * a.G + g;
     if (tid == 0) {
-        double *pp = partials + (grp * nch + chunk) * 2;
-        dfp::publish(pp, s1);
-        dfp::publish(pp + 1, s2);
-        dfp::published_wait();
-        is_last = dfp::arrive(counters + grp) == (unsigned)nch - 1;
+        double *pp = partials + (((int64_t)b * a.G + g) * nch + chunk) * 2;
+        pp[0] = s1;
+        pp[1] = s2;
     }
-    __syncthreads();
-    if (!is_last || tid != 0) return;
-    double f1 = 0.0, f2 = 0.0;
-    for (int k = 0; k < nch; ++k) {
-        f1 += dfp::fetch_published(partials + (grp * nch + k) * 2);
-        f2 += dfp::fetch_published(partials + (grp * nch + k) * 2 + 1);
-    }
-    const float2 mr = stats_from_sums(a, b, g, f1, f2);
-    mean_rstd[grp * 2] = mr.x;
-    mean_rstd[grp * 2 + 1] = mr.y;
-    dfp::publish(counters + grp, 0u);
 }
 
-// Chunked path, launch 2: every chunk normalizes its floats.
+// Chunked path, launch 2: every chunk adds its group's chunk sums in chunk
+// order (thread t takes chunks t, t + 256, ..., then the fixed block sum),
+// forms (mean, rstd) -- the group's chunk 0 also lands the fresh sums -- and
+// normalizes its floats.
 template <bool VEC, bool AFFINE>
 __global__ __launch_bounds__(kGcThreads) void gn_chunk_norm_kernel(GnArgs a,
-                                                                   const float *mean_rstd) {
+                                                                   const double *partials) {
     const int chunk = blockIdx.x, nch = gridDim.x, g = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x;
     const int cg = a.C / a.G;
@@ -258,12 +244,42 @@ __global__ __launch_bounds__(kGcThreads) void gn_chunk_norm_kernel(GnArgs a,
     const int64_t lo = min(run, (int64_t)chunk * per), hi = min(run, lo + per);
     const int64_t off = ((int64_t)b * a.C + (int64_t)g * cg) * a.n;
     const int64_t grp = (int64_t)b * a.G + g;
-    const float2 mr = make_float2(mean_rstd[grp * 2], mean_rstd[grp * 2 + 1]);
+    // this chunk's floats first: they do not depend on the statistics
+    constexpr int kHeld = 4;   // float4 per thread held across the statistics
+    const int64_t m4 = VEC ? (hi - lo) / 4 : 0;
+    const float4 *x4 = reinterpret_cast<const float4 *>(a.x + off + lo);
+    float4 v[kHeld];
     if (VEC) {
-        const float4 *x4 = reinterpret_cast<const float4 *>(a.x + off + lo);
+#pragma unroll
+        for (int k = 0; k < kHeld; ++k) {
+            const int64_t i = tid + (int64_t)k * kGcThreads;
+            v[k] = i < m4 ? x4[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    }
+    double f1 = 0.0, f2 = 0.0;
+    for (int k = tid; k < nch; k += kGcThreads) {
+        f1 += partials[(grp * nch + k) * 2];
+        f2 += partials[(grp * nch + k) * 2 + 1];
+    }
+    __shared__ float mean_rstd[2];
+    block_sums<kGcWaves>(f1, f2);
+    if (tid == 0) {
+        GnArgs ac = a;
+        ac.land = a.land && chunk == 0;
+        const float2 mr = stats_from_sums(ac, b, g, f1, f2);
+        mean_rstd[0] = mr.x;
+        mean_rstd[1] = mr.y;
+    }
+    __syncthreads();
+    const float2 mr = make_float2(mean_rstd[0], mean_rstd[1]);
+    if (VEC) {
         float4 *y4 = reinterpret_cast<float4 *>(a.y + off + lo);
-        const int64_t m4 = (hi - lo) / 4;
-        for (int64_t i = tid; i < m4; i += kGcThreads)
+#pragma unroll
+        for (int k = 0; k < kHeld; ++k) {
+            const int64_t i = tid + (int64_t)k * kGcThreads;
+            if (i < m4) y4[i] = normalize4<AFFINE>(a, v[k], g * cg + (int)((lo + 4 * i) / a.n), mr);
+        }
+        for (int64_t i = tid + (int64_t)kHeld * kGcThreads; i < m4; i += kGcThreads)
             y4[i] = normalize4<AFFINE>(a, x4[i], g * cg + (int)((lo + 4 * i) / a.n), mr);
     } else {
         for (int64_t i = lo + tid; i < hi; i += kGcThreads) {
@@ -282,7 +298,7 @@ bool aligned(const void *p, uintptr_t to) { return (reinterpret_cast<uintptr_t>(
 extern "C" size_t dfp_group_norm_workspace_bytes(int B, int C, int G, int64_t n) {
     if (B <= 0 || C <= 0 || G <= 0 || C % G != 0 || n <= 0) return 0;
     const int64_t run = (int64_t)(C / G) * n;
-    if (run <= kGnResidentFloats) return 0;
+    if (run <= kGnResidentFloats && n % 4 == 0) return 0;   // the register path needs none
     return gn_workspace_need((int64_t)B * G, run_chunks(run));
 }
 
@@ -308,32 +324,31 @@ extern "C" dfp_status dfp_displaced_group_norm(float *y, const float *x, double 
                           aligned(y, 16);
     const int64_t groups = (int64_t)B * G;
     const int64_t chunks = run_chunks(run);
-    const bool chunked = !resident && run > kGnResidentFloats && G <= 65535 && workspace &&
-                         aligned(workspace, 256) &&
+    const bool chunked = !resident && G <= 65535 && workspace && aligned(workspace, 8) &&
                          ws_bytes >= gn_workspace_need(groups, chunks);
     const dim3 grid((unsigned)G, (unsigned)B), block(kGnThreads);
     if (chunked) {
-        unsigned *counters = static_cast<unsigned *>(workspace);
-        double *partials = reinterpret_cast<double *>(static_cast<char *>(workspace) +
-                                                      gn_counter_bytes(groups));
-        float *mr = reinterpret_cast<float *>(partials + groups * chunks * 2);
+        // y partially overlapping x is refused above; y == x (in place) is
+        // safe: a chunk writes only the floats it read, after reading them
+        double *partials = static_cast<double *>(workspace);
         const bool vec = n % 4 == 0 && aligned(x, 16) && aligned(y, 16);
         const dim3 cgrid((unsigned)chunks, (unsigned)G, (unsigned)B), cblock(kGcThreads);
         if (vec)
-            hipLaunchKernelGGL(gn_chunk_sums_kernel<true>, cgrid, cblock, 0, stream, a, partials,
-                               counters, mr);
+            hipLaunchKernelGGL(gn_chunk_sums_kernel<true>, cgrid, cblock, 0, stream, a, partials);
         else
-            hipLaunchKernelGGL(gn_chunk_sums_kernel<false>, cgrid, cblock, 0, stream, a, partials,
-                               counters, mr);
+            hipLaunchKernelGGL(gn_chunk_sums_kernel<false>, cgrid, cblock, 0, stream, a, partials);
         if (vec && affine)
-            hipLaunchKernelGGL((gn_chunk_norm_kernel<true, true>), cgrid, cblock, 0, stream, a, mr);
+            hipLaunchKernelGGL((gn_chunk_norm_kernel<true, true>), cgrid, cblock, 0, stream, a,
+                               partials);
         else if (vec)
-            hipLaunchKernelGGL((gn_chunk_norm_kernel<true, false>), cgrid, cblock, 0, stream, a, mr);
+            hipLaunchKernelGGL((gn_chunk_norm_kernel<true, false>), cgrid, cblock, 0, stream, a,
+                               partials);
         else if (affine)
-            hipLaunchKernelGGL((gn_chunk_norm_kernel<false, true>), cgrid, cblock, 0, stream, a, mr);
+            hipLaunchKernelGGL((gn_chunk_norm_kernel<false, true>), cgrid, cblock, 0, stream, a,
+                               partials);
         else
             hipLaunchKernelGGL((gn_chunk_norm_kernel<false, false>), cgrid, cblock, 0, stream, a,
-                               mr);
+                               partials);
     } else if (resident) {
         if (affine) hipLaunchKernelGGL(gn_resident_kernel<true>, grid, block, 0, stream, a);
         else hipLaunchKernelGGL(gn_resident_kernel<false>, grid, block, 0, stream, a);

@@ -230,11 +230,12 @@ def test_group_norm_validation(L):
     assert call(eps=float("nan")) == E
     assert call(eps=float("inf")) == E
     assert call(B=65536) == dfp.ERR_UNSUPPORTED
-    # groups of up to 64 Ki floats need no workspace; longer ones one counter
-    # per group (256-byte padded), fp64 sums per 16 Ki-float chunk, (mean, rstd)
+    # groups of up to 64 Ki floats (n % 4 == 0) need none; longer ones one
+    # fp64 pair per 4 Ki-float chunk of every group
     ws = L.dfp_group_norm_workspace_bytes
-    assert ws(2, 320, 32, 4096) == 0               # 40 Ki floats per group
-    assert ws(2, 320, 32, 28800) == 256 + 64 * 18 * 16 + 64 * 8
+    assert ws(2, 320, 32, 4096) == 0                 # 40 Ki floats per group
+    assert ws(2, 320, 32, 4097) == 64 * 11 * 16      # n % 4 != 0: chunked
+    assert ws(2, 320, 32, 28800) == 64 * 71 * 16     # 281.25 Ki floats: 71 chunks
     assert ws(2, 320, 30, 28800) == 0              # C not a multiple of G
     assert ws(0, 320, 32, 28800) == 0
 

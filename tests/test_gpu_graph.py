@@ -85,10 +85,10 @@ def test_graph_replays_match_eager(monkeypatch):
 
 
 def test_group_norm_graph_replays_match_eager():
-    """The chunked displaced GroupNorm (two launches, published chunk sums,
-    last-arrival statistics) captured in a HIP graph: every replay gives the
-    eager call's bits, lands the same sums and leaves the counters at zero,
-    with an eager call on the same workspace between replays."""
+    """The chunked displaced GroupNorm (two launches: chunk sums, then
+    statistics and normalization) captured in a HIP graph: every replay
+    gives the eager call's bits and lands the same sums, with an eager call
+    on the same workspace between replays."""
     G.require_gpu()
     G.announce("graph replay: chunked displaced GroupNorm, 4 replays")
     torch = G.torch_mod()
@@ -126,7 +126,6 @@ def test_group_norm_graph_replays_match_eager():
         torch.cuda.synchronize()
         np.testing.assert_array_equal(G.down(y_g), want_y, err_msg=f"replay {i} output")
         np.testing.assert_array_equal(st_g.cpu().numpy(), want_st, err_msg=f"replay {i} sums")
-        assert int(ws[:B * G_ * 4].sum().item()) == 0
         dfp.displaced_group_norm(other, x, st_e, G_, p, 1e-5, ga, be, True, ws)
         torch.cuda.synchronize()
         np.testing.assert_array_equal(G.down(other), want_y)

@@ -38,10 +38,10 @@ def _run(B, C, G_, n, P, p, seed, affine=True, in_place=False, land=True, offset
     gamma = torch.from_numpy(a.gamma).cuda() if affine else None
     beta = torch.from_numpy(a.beta).cuda() if affine else None
     work = dfp.group_norm_workspace(B, C, G_, n) if ws else None
+    if work is not None:
+        work.fill_(0x7F)   # the chunked path needs no initial workspace contents
     dfp.displaced_group_norm(y, x, st, G_, p, 1e-5, gamma, beta, land, work)
     torch.cuda.synchronize()
-    if work is not None:   # arrival counters, one per (image, group), back at zero
-        assert int(work[:B * G_ * 4].sum().item()) == 0
     got = G.down(y).astype(np.float64)
     err = np.abs(got - want_y)
     rel = np.linalg.norm(got - want_y) / np.linalg.norm(want_y)
