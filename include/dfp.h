@@ -49,7 +49,13 @@
  *   - No entry point throws; none keeps state between calls except where a
  *     workspace is documented to (the attention split-KV arrival counters).
  *   - bf16 tensors hold raw bfloat16 bit patterns (uint16_t).
- *   - Tensors are dense and row-major in the order their shape is written.
+ *   - Tensors are dense and row-major in the order their shape is written;
+ *     no entry point takes element strides (a caller holding K/V rows as
+ *     [B][N][H][d] transposes them to [B][H][N][d] before dfp_kv_scatter).
+ *   - The persistent V buffer is stored TRANSPOSED ([B][H][d][ldv], see the
+ *     layout block below), so the attention's P.V product reads it without a
+ *     transpose; dfp_kv_scatter transposes fresh V rows once when they land,
+ *     and dfp_patch_attention_fresh takes fresh V already channel-major.
  *   - Calls that share a workspace must not overlap in time.
  */
 #ifndef DFP_H
