@@ -49,9 +49,9 @@
  *   - No entry point throws; none keeps state between calls except where a
  *     workspace is documented to (the attention split-KV arrival counters).
  *   - bf16 tensors hold raw bfloat16 bit patterns (uint16_t).
- *   - Tensors are dense and row-major in the order their shape is written;
- *     no entry point takes element strides (a caller holding K/V rows as
- *     [B][N][H][d] transposes them to [B][H][N][d] before dfp_kv_scatter).
+ *   - Tensors are dense and row-major in the order their shape is written,
+ *     except the fresh K/V rows of dfp_kv_scatter_strided, which take
+ *     element strides (so a projection's [B][N][H][d] output lands as is).
  *   - The persistent V buffer is stored TRANSPOSED ([B][H][d][ldv], see the
  *     layout block below), so the attention's P.V product reads it without a
  *     transpose; dfp_kv_scatter transposes fresh V rows once when they land,
@@ -128,6 +128,22 @@ int64_t dfp_v_ld(int64_t N_buf, dfp_dtype dt);
 dfp_status dfp_kv_scatter(void *k_buf, void *v_buf_t, const void *k_new,
                           const void *v_new, int B, int H, int N_buf, int d,
                           int row0, int n, dfp_dtype dt, hipStream_t stream);
+
+/* dfp_kv_scatter for fresh rows in any layout whose rows are contiguous: row
+ * i of (b, h) starts at element b * stride_b + h * stride_h + i * stride_n of
+ * k_new (and of v_new, which shares the strides), and holds d contiguous
+ * elements.  A projection's [B][n][H][d] output passes stride_b = n*H*d,
+ * stride_h = d, stride_n = H*d; dense [B][H][n][d] is stride_b = H*n*d,
+ * stride_h = n*d, stride_n = d (what dfp_kv_scatter passes).  Strides are in
+ * elements, non-negative, multiples of 8 (bf16) or 4 (f32) so every row
+ * starts on a 16-byte boundary, and stride_n >= d; the caller guarantees
+ * every addressed row lies inside its tensors.  Result, buffers, other
+ * arguments and errors as dfp_kv_scatter, plus INVALID_ARG for a stride
+ * outside these rules. */
+dfp_status dfp_kv_scatter_strided(void *k_buf, void *v_buf_t, const void *k_new,
+                                  const void *v_new, int B, int H, int N_buf, int d,
+                                  int row0, int n, int64_t stride_b, int64_t stride_h,
+                                  int64_t stride_n, dfp_dtype dt, hipStream_t stream);
 
 /* (a2-a4) One patch's attention over the displaced buffer.
  * [DF] activation reuse: the buffer holds fresh rows for this patch (and

@@ -9,7 +9,9 @@
 // 64 x 64 element tile through LDS so both its reads (along channels) and its
 // writes (along tokens) stay coalesced.  K and V share one launch (the copy
 // is latency-bound at these sizes, so a second launch would cost as much as
-// the data).
+// the data).  The fresh rows may come in any layout whose rows of d elements
+// are contiguous and 16-byte aligned (element strides per batch, head and
+// row): [B][H][n][d] and a projection's [B][n][H][d] alike.
 #include "dfp_common.h"
 
 namespace {
@@ -22,20 +24,37 @@ struct ScatterArgs {
     int64_t k_dst_off;        // row0 * d / VE
     int64_t k_total;          // BH * k_vec_per_bh
     void *v_dst;              // V^T buffer [BH][d][ldv]
-    const void *v_src;        // [BH][n][d]
-    int n, d, row0;
+    const void *v_src;        // fresh V rows, element strides below
+    int n, d, row0, H;
     int64_t ldv;
+    int64_t sb, sh, sn;       // fresh rows' element strides: batch, head, row
+    int vec_per_row;          // d / VE
+    int dense;                // fresh rows are [B][H][n][d] with no gaps
     int v_tiles_i, v_tiles_c;   // 64-token and 64-channel tiles per (b,h)
     int v_blocks;               // blocks [0, v_blocks) transpose V; the rest copy K
 };
 
-// K: every (b,h) owns one contiguous run of n*d elements in k_new and one in
-// k_buf starting at row0*d; both runs are multiples of 16 bytes.
+// Element offset of fresh row i of (b,h) = bh.
+__device__ __forceinline__ int64_t src_row(const ScatterArgs &a, int64_t bh, int64_t i) {
+    const int64_t b = bh / a.H, h = bh - b * a.H;
+    return b * a.sb + h * a.sh + i * a.sn;
+}
+
+// K: every (b,h) owns rows row0.. of its k_buf run; a dense source is one
+// contiguous run of n*d elements per (b,h), a strided one n rows of d.
+template <int VE>
 __device__ __forceinline__ void k_rows_copy(const ScatterArgs &a, int64_t first, int64_t stride) {
     for (int64_t v = first; v < a.k_total; v += stride) {
         const int64_t bh = v / a.k_vec_per_bh;
         const int64_t r = v - bh * a.k_vec_per_bh;
-        a.k_dst[bh * a.k_dst_bh_stride + a.k_dst_off + r] = a.k_src[v];
+        uint4 q;
+        if (a.dense) {
+            q = a.k_src[v];
+        } else {
+            const int64_t i = r / a.vec_per_row, cv = r - i * a.vec_per_row;
+            q = a.k_src[(src_row(a, bh, i) >> (VE == 8 ? 3 : 2)) + cv];
+        }
+        a.k_dst[bh * a.k_dst_bh_stride + a.k_dst_off + r] = q;
     }
 }
 
@@ -55,7 +74,7 @@ __device__ __forceinline__ void v_tile_transpose(const ScatterArgs &a, int tile)
     const int64_t bh = rest / a.v_tiles_c;
     const int i0 = ti * T, c0 = tc * T;
     const int n = a.n, d = a.d;
-    const E *s = static_cast<const E *>(a.v_src) + bh * (int64_t)n * d;
+    const E *s = static_cast<const E *>(a.v_src) + src_row(a, bh, 0);
     E *o = static_cast<E *>(a.v_dst) + bh * (int64_t)d * a.ldv;
 
     // load: rows i, 16-byte vectors along channels (d is a multiple of VE)
@@ -65,7 +84,7 @@ __device__ __forceinline__ void v_tile_transpose(const ScatterArgs &a, int tile)
         const int gi = i0 + i, gc = c0 + cv * VE;
         E vals[VE];
         if (gi < n && gc < d) {
-            const uint4 q = *reinterpret_cast<const uint4 *>(s + (int64_t)gi * d + gc);
+            const uint4 q = *reinterpret_cast<const uint4 *>(s + (int64_t)gi * a.sn + gc);
             __builtin_memcpy(vals, &q, 16);
         } else {
 #pragma unroll
@@ -105,15 +124,17 @@ __global__ __launch_bounds__(256) void kv_scatter_kernel(ScatterArgs a) {
     } else {
         const int64_t kb = blockIdx.x - a.v_blocks;
         const int64_t k_blocks = gridDim.x - a.v_blocks;
-        k_rows_copy(a, kb * blockDim.x + threadIdx.x, k_blocks * blockDim.x);
+        k_rows_copy<16 / sizeof(E)>(a, kb * blockDim.x + threadIdx.x, k_blocks * blockDim.x);
     }
 }
 
 }  // namespace
 
-extern "C" dfp_status dfp_kv_scatter(void *k_buf, void *v_buf_t, const void *k_new,
-                                     const void *v_new, int B, int H, int N_buf, int d,
-                                     int row0, int n, dfp_dtype dt, hipStream_t stream) {
+extern "C" dfp_status dfp_kv_scatter_strided(void *k_buf, void *v_buf_t, const void *k_new,
+                                             const void *v_new, int B, int H, int N_buf, int d,
+                                             int row0, int n, int64_t stride_b,
+                                             int64_t stride_h, int64_t stride_n, dfp_dtype dt,
+                                             hipStream_t stream) {
     if (B <= 0 || H <= 0 || N_buf <= 0 || d <= 0 || n < 0 || row0 < 0 ||
         (int64_t)row0 + n > N_buf)
         return DFP_ERR_INVALID_ARG;
@@ -128,12 +149,23 @@ extern "C" dfp_status dfp_kv_scatter(void *k_buf, void *v_buf_t, const void *k_n
     const int esize = dt == DFP_BF16 ? 2 : 4;
     const int VE = 16 / esize;
     if (d % VE != 0) return DFP_ERR_UNSUPPORTED;
+    // every fresh row must start on a 16-byte boundary
+    if (stride_b < 0 || stride_h < 0 || stride_n < d || stride_b % VE || stride_h % VE ||
+        stride_n % VE)
+        return DFP_ERR_INVALID_ARG;
     const int64_t BH = (int64_t)B * H;
 
     ScatterArgs a{};
     a.n = n;
     a.d = d;
     a.row0 = row0;
+    a.H = H;
+    a.sb = stride_b;
+    a.sh = stride_h;
+    a.sn = stride_n;
+    a.vec_per_row = d / VE;
+    a.dense = stride_n == d && (H == 1 || stride_h == (int64_t)n * d) &&
+              (B == 1 || stride_b == (int64_t)H * n * d);
     int64_t k_blocks = 0, v_blocks = 0;
     if (k_buf) {
         const int64_t vec_per_row = (int64_t)d / VE;
@@ -162,4 +194,11 @@ extern "C" dfp_status dfp_kv_scatter(void *k_buf, void *v_buf_t, const void *k_n
     else
         hipLaunchKernelGGL(kv_scatter_kernel<uint32_t>, grid, dim3(256), 0, stream, a);
     return dfp::launch_status();
+}
+
+extern "C" dfp_status dfp_kv_scatter(void *k_buf, void *v_buf_t, const void *k_new,
+                                     const void *v_new, int B, int H, int N_buf, int d,
+                                     int row0, int n, dfp_dtype dt, hipStream_t stream) {
+    return dfp_kv_scatter_strided(k_buf, v_buf_t, k_new, v_new, B, H, N_buf, d, row0, n,
+                                  (int64_t)H * n * d, (int64_t)n * d, d, dt, stream);
 }

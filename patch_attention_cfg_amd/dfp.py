@@ -28,6 +28,8 @@ _U64 = ctypes.c_uint64
 SIGNATURES = {
     "dfp_v_ld": (_I64, [_I64, _I]),
     "dfp_kv_scatter": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P]),
+    "dfp_kv_scatter_strided": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I64, _I64, _I64, _I,
+                                    _P]),
     "dfp_patch_attention": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _SZ, _P]),
     "dfp_patch_attention_fresh": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I,
                                        _P, _SZ, _P]),
@@ -259,6 +261,39 @@ def kv_scatter(k_buf, v_buf_t, k_new, v_new, row0: int, stream=None) -> None:
     st = lib().dfp_kv_scatter(_ptr(k_buf), _ptr(v_buf_t), _ptr(k_new), _ptr(v_new), B, H,
                               N_buf, d, int(row0), n, _dtype_code(ref), _stream(stream))
     _check(st, "dfp_kv_scatter")
+
+
+def kv_scatter_strided(k_buf, v_buf_t, k_new, v_new, row0: int, stream=None) -> None:
+    """dfp_kv_scatter_strided: k_new / v_new are [B,H,n,d] views of any layout
+    with contiguous rows (stride 1 along d) and equal strides, e.g.
+    x.permute(0, 2, 1, 3) of a projection's [B,n,H,d] output."""
+    _need(k_new is not None and v_new is not None and k_buf is not None and v_buf_t is not None,
+          "the strided landing takes both K and V")
+    for t in (k_buf, v_buf_t):
+        _need(t.is_cuda and t.is_contiguous(), "the buffers must be contiguous GPU tensors")
+    for t in (k_new, v_new):
+        _need(t.is_cuda and t.dim() == 4 and t.stride(3) == 1,
+              "fresh rows must be [B,H,n,d] GPU views with contiguous rows")
+    _need(len({t.device for t in (k_buf, v_buf_t, k_new, v_new)}) == 1,
+          "tensors live on different devices")
+    _need(tuple(k_new.shape) == tuple(v_new.shape) and k_new.stride() == v_new.stride(),
+          "k_new and v_new must share shape and strides")
+    B, H, n, d = k_new.shape
+    _need(len({t.dtype for t in (k_buf, v_buf_t, k_new, v_new)}) == 1,
+          "buffer and fresh rows must share a dtype")
+    _need(k_buf.dim() == 4 and tuple(k_buf.shape[:2]) == (B, H) and k_buf.shape[3] == d,
+          "k_buf must be [B,H,N_buf,d]")
+    N_buf = k_buf.shape[2]
+    _need(tuple(v_buf_t.shape[:3]) == (B, H, d) and
+          v_buf_t.shape[3] == v_ld(N_buf, _dtype_code(v_buf_t)), "v_buf_t must be [B,H,d,ldv]")
+    sb, sh, sn = k_new.stride(0), k_new.stride(1), k_new.stride(2)
+    # a size-1 dimension's stride is never used
+    sb, sh, sn = (0 if B == 1 else sb), (0 if H == 1 else sh), (d if n == 1 else sn)
+    st = lib().dfp_kv_scatter_strided(_ptr(k_buf), _ptr(v_buf_t),
+                                      ctypes.c_void_p(k_new.data_ptr()),
+                                      ctypes.c_void_p(v_new.data_ptr()), B, H, N_buf, d, int(row0),
+                                      n, sb, sh, sn, _dtype_code(k_buf), _stream(stream))
+    _check(st, "dfp_kv_scatter_strided")
 
 
 def _check_attention(o, q, k_buf, v_buf_t, workspace):

@@ -81,6 +81,22 @@ def test_scatter_validation(L, args, expect):
     assert L.dfp_kv_scatter(*args, S0) == expect
 
 
+@pytest.mark.parametrize("strides,expect", [
+    ((2 * 64 * 16, 64, 2 * 64), dfp.ERR_INVALID_ARG),   # nothing wrong but a NULL v_new below
+    ((4, 64, 128), dfp.ERR_INVALID_ARG),                # batch stride not 16-byte rows (bf16: x8)
+    ((2048, 60, 128), dfp.ERR_INVALID_ARG),             # head stride not a multiple of 8
+    ((2048, 64, 32), dfp.ERR_INVALID_ARG),              # rows overlap (stride_n < d)
+    ((-2048, 64, 128), dfp.ERR_INVALID_ARG),            # negative
+])
+def test_strided_scatter_validation(L, strides, expect):
+    v_new = NULL if strides == (2 * 64 * 16, 64, 2 * 64) else FAKE
+    assert L.dfp_kv_scatter_strided(FAKE, FAKE, FAKE, v_new, 2, 2, 64, 64, 0, 16, *strides,
+                                    dfp.BF16, S0) == expect
+    # empty landings are no-ops whatever the strides
+    assert L.dfp_kv_scatter_strided(NULL, NULL, NULL, NULL, 2, 2, 64, 64, 0, 0, 1, 1, 1,
+                                    dfp.BF16, S0) == dfp.OK
+
+
 @pytest.mark.parametrize("args,expect", [
     ((NULL, FAKE, FAKE, FAKE, 2, 2, 16, 64, 64, 0.125, dfp.BF16), dfp.ERR_INVALID_ARG),
     ((FAKE, FAKE, FAKE, NULL, 2, 2, 16, 64, 64, 0.125, dfp.BF16), dfp.ERR_INVALID_ARG),

@@ -57,3 +57,41 @@ def test_scatter_only_v_or_only_k_and_empty():
     torch.cuda.synchronize()
     np.testing.assert_array_equal(G.down(k_buf), oracle.effective_kv(sk, fk, 40))
     np.testing.assert_array_equal(G.v_buffer_to_rows(v_buf, 96), sv)
+
+
+@pytest.mark.parametrize("kind", ["bf16", "f32"])
+@pytest.mark.parametrize("B,H,N,d,row0,n", [
+    (2, 10, 57600, 64, 7200, 7200),  # an SDXL-3840 patch, from a [B, n, H, d] projection
+    (2, 3, 200, 64, 3, 37),           # unaligned offset, ragged n
+    (1, 2, 130, 128, 64, 66),         # d=128
+    (2, 1, 96, 64, 5, 1),             # one row, one head
+])
+def test_strided_scatter_from_token_major_rows(kind, B, H, N, d, row0, n):
+    """dfp_kv_scatter_strided lands fresh rows held token-major ([B, n, H, d],
+    a projection's natural output, viewed as [B, H, n, d]) and rows of a
+    wider tensor (a slice), bit for bit as dfp_kv_scatter of the dense rows."""
+    G.require_gpu()
+    G.announce(f"strided scatter {kind} B{B} H{H} N{N} d{d} row0={row0} n={n}")
+    torch = G.torch_mod()
+    _, sk, sv = inputs.random_attention_arrays(B, H, 1, N, d, seed=N + 3, dtype=kind)
+    _, fk, fv = inputs.random_attention_arrays(B, H, 1, n, d, seed=N + 4, dtype=kind)
+    dt = G.dtype_of(kind)
+    want_k = oracle.effective_kv(sk, fk, row0).astype(np.float32)
+    want_v = oracle.effective_kv(sv, fv, row0).astype(np.float32)
+    # token-major storage [B, n, H, d], viewed as [B, H, n, d]
+    tk = G.up(np.ascontiguousarray(np.swapaxes(fk, 1, 2)), kind).permute(0, 2, 1, 3)
+    tv = G.up(np.ascontiguousarray(np.swapaxes(fv, 1, 2)), kind).permute(0, 2, 1, 3)
+    # rows 8..8+n of a wider dense tensor
+    wide_k = torch.zeros((B, H, n + 16, d), dtype=dt, device="cuda")
+    wide_v = torch.zeros((B, H, n + 16, d), dtype=dt, device="cuda")
+    wide_k[:, :, 8:8 + n] = G.up(fk, kind)
+    wide_v[:, :, 8:8 + n] = G.up(fv, kind)
+    for src_k, src_v in ((tk, tv), (wide_k[:, :, 8:8 + n], wide_v[:, :, 8:8 + n])):
+        k_buf, v_buf = dfp.alloc_kv_buffer(B, H, N, d, dt)
+        v_buf.fill_(float("nan"))
+        dfp.kv_scatter(k_buf, v_buf, G.up(sk, kind), G.up(sv, kind), 0)
+        dfp.kv_scatter_strided(k_buf, v_buf, src_k, src_v, row0)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(_bits(G.down(k_buf), kind), _bits(want_k, kind))
+        np.testing.assert_array_equal(_bits(G.v_buffer_to_rows(v_buf, N), kind),
+                                      _bits(want_v, kind))
