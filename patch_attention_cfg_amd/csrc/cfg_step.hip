@@ -73,6 +73,7 @@ inline int plan_blocks(int64_t n_per_image, int item_floats, int unroll = kUnrol
 // first) become uniforms u = (h + 1/2) 2^-32, and pair k gives
 //   z[8j+2k] = sqrt(-2 ln u_2k) cos(2 pi u_2k+1),
 //   z[8j+2k+1] = sqrt(-2 ln u_2k) sin(2 pi u_2k+1).
+
 // Full 128-bit product of two 64-bit words from four 32 x 32 -> 64 products.
 __device__ __forceinline__ void mul128(uint64_t a, uint64_t b, uint64_t &lo, uint64_t &hi) {
     const uint32_t a0 = (uint32_t)a, a1 = (uint32_t)(a >> 32);
@@ -167,7 +168,8 @@ __global__ __launch_bounds__(kThreads) void cfg_step_kernel(
     constexpr int F = NOISE == kNoisePhilox ? 2 : 1;   // float4 per item and array
     constexpr int UN = unroll_of<NOISE>();
     float4 cv[UN][F], uv[UN][F], xv[UN][F], zv[UN][F];
-    float zn[UN][NOISE == kNoisePhilox ? 8 : 1];   // drawn noise of the pass's items
+    constexpr int ZN = NOISE == kNoisePhilox ? 8 : 1;
+    float zn[UN][ZN];   // drawn noise of the pass's items
     int64_t last = -1;   // item base of this thread's final vector pass
     const int64_t n_items = n / (4 * F);
     const int64_t stride = (int64_t)nblk * kThreads * UN;
@@ -207,16 +209,12 @@ __global__ __launch_bounds__(kThreads) void cfg_step_kernel(
                 if (i < n_items) zv[k][0] = z4[i];
             }
         }
-        if (NOISE == kNoisePhilox && UPDATE) {
+        if constexpr (NOISE == kNoisePhilox && UPDATE) {
             // independent of the loads: drawn while they are in flight
 #pragma unroll
-            for (int k = 0; k < UN; ++k) {
-                float zb[8];
+            for (int k = 0; k < UN; ++k)
                 philox_normals8((uint64_t)(i0 + (int64_t)k * kThreads), (uint64_t)img, seed,
-                                step, zb);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) zn[k][e % (NOISE == kNoisePhilox ? 8 : 1)] = zb[e];
-            }
+                                step, zn[k]);
         }
     };
     auto accum_pass = [&](int64_t i0) {
@@ -239,10 +237,10 @@ __global__ __launch_bounds__(kThreads) void cfg_step_kernel(
             const int64_t i = i0 + (int64_t)k * kThreads;
             if (i >= n_items) continue;
             float zz[4 * F];
-            if (NOISE == kNoisePhilox) {
+            if constexpr (NOISE == kNoisePhilox) {
 #pragma unroll
-                for (int e = 0; e < 4 * F; ++e) zz[e] = zn[k][e % (NOISE == kNoisePhilox ? 8 : 1)];
-            } else if (NOISE == kNoiseArray) {
+                for (int e = 0; e < 4 * F; ++e) zz[e] = zn[k][e];
+            } else if constexpr (NOISE == kNoiseArray) {
                 zz[0] = zv[k][0].x;
                 zz[1] = zv[k][0].y;
                 zz[2] = zv[k][0].z;

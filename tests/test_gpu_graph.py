@@ -129,3 +129,70 @@ def test_group_norm_graph_replays_match_eager():
         dfp.displaced_group_norm(other, x, st_e, G_, p, 1e-5, ga, be, True, ws)
         torch.cuda.synchronize()
         np.testing.assert_array_equal(G.down(other), want_y)
+
+
+def test_fused_step_entries_in_graph():
+    """The fused step's other entry points under capture: the in-kernel noise
+    draw (dfp_cfg_step_philox) and the no-allocation step
+    (dfp_cfg_step_static, partials in the library's static scratch), two
+    launches each, captured in one graph and replayed four times with eager
+    calls of both entries (other sizes, the same scratch) between the
+    replays; every replay matches the eager sequence bit for bit."""
+    G.require_gpu()
+    G.announce("graph replay: cfg_step_philox + cfg_step_static, 4 replays")
+    torch = G.torch_mod()
+    rng = np.random.Generator(np.random.PCG64(47))
+    n, batch = 4 * 96 * 96, 2
+    x0 = rng.standard_normal((batch, n), dtype=np.float32)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    g_c, g_u = dev(rng.standard_normal((batch, n), dtype=np.float32)), \
+        dev(rng.standard_normal((batch, n), dtype=np.float32))
+    c_x, c_e, c_z = dfp.ddim_eta_coeffs(0.3, 0.5, 0.7)
+    ws = dfp.cfg_workspace(n, batch)
+
+    def step(x, r1, r2):
+        dfp.cfg_step_philox(x, g_c, g_u, 6.0, c_x, c_e, c_z, 2024, 11, r1, ws)
+        dfp.cfg_step_static(x, g_u, g_c, 4.0, 0.99, -0.02, r2)
+
+    x_e = dev(x0.copy())
+    r1_e = torch.empty(batch, device="cuda")
+    r2_e = torch.empty(batch, device="cuda")
+    want = []
+    for _ in range(4):
+        step(x_e, r1_e, r2_e)
+        torch.cuda.synchronize()
+        want.append((x_e.cpu().numpy().copy(), r1_e.cpu().numpy().copy(),
+                     r2_e.cpu().numpy().copy()))
+
+    x_g = dev(x0.copy())
+    r1_g = torch.empty(batch, device="cuda")
+    r2_g = torch.empty(batch, device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):            # warm-up outside capture, then restore x
+        step(x_g, r1_g, r2_g)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    x_g.copy_(dev(x0))
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(x_g, r1_g, r2_g)
+    torch.cuda.synchronize()
+    x_g.copy_(dev(x0))
+    torch.cuda.synchronize()
+
+    small = dev(rng.standard_normal((1, 4 * 32 * 32), dtype=np.float32))
+    r_small = torch.empty(1, device="cuda")
+    for i in range(4):
+        graph.replay()
+        torch.cuda.synchronize()
+        wx, wr1, wr2 = want[i]
+        np.testing.assert_array_equal(x_g.cpu().numpy(), wx, err_msg=f"replay {i} latent")
+        np.testing.assert_array_equal(r1_g.cpu().numpy(), wr1, err_msg=f"replay {i} rel-MAE 1")
+        np.testing.assert_array_equal(r2_g.cpu().numpy(), wr2, err_msg=f"replay {i} rel-MAE 2")
+        # eager calls of both entries between replays, on other sizes
+        xs = small.clone()
+        dfp.cfg_step_static(xs, small, small * 0.5, 2.0, 1.0, -0.1, r_small)
+        dfp.cfg_step_philox(xs, small, small, 1.0, 1.0, 0.0, 0.1, 5, i, r_small,
+                            dfp.cfg_workspace(small.numel(), 1))
+        torch.cuda.synchronize()
