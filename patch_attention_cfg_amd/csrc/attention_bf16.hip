@@ -637,41 +637,13 @@ __device__ __forceinline__ void raise_reference(
             }
 }
 
-// Split-KV merge, phase 2: each thread owns G 16-byte groups of the query
-// tile and folds NS splits per pass, with all G x NS coherent loads of a
-// pass in flight together (at most 24, to bound registers).
-template <int D, int KS>
-struct MergeCfg {
-    static constexpr int G = Cfg<D, KS>::BLOCK_M * D / 4 / Cfg<D, KS>::THREADS;
-    static constexpr int NS = 24 / G < 1 ? 1 : (24 / G > 4 ? 4 : 24 / G);
-    static_assert(G * Cfg<D, KS>::THREADS * 4 == Cfg<D, KS>::BLOCK_M * D, "groups tile the query tile");
+// Split-KV merge: the other splits' partials a merging lane loads in one
+// batch of coherent loads (all in flight together), bounded by registers:
+// 4 splits at d=64, one at d=128.
+template <int D>
+struct MergeBatch {
+    static constexpr int N = D == 64 ? 4 : 1;
 };
-
-template <int D, int KS, int N>
-__device__ __forceinline__ void merge_pass(f32x4_t (&acc)[(MergeCfg<D, KS>::G)], const float *part0,
-                                           const float *wts, int s0, int tid) {
-    using C = Cfg<D, KS>;
-    constexpr int G = MergeCfg<D, KS>::G;
-    f32x4_t v[N][G];
-#pragma unroll
-    for (int j = 0; j < N; ++j) {
-        const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<float *>(part0) + (int64_t)(s0 + j) * C::BLOCK_M * D, 0,
-            C::BLOCK_M * D * 4, 0x00020000);
-#pragma unroll
-        for (int k = 0; k < G; ++k)
-            v[j][k] = __builtin_bit_cast(
-                f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ro, (tid + k * C::THREADS) * 16, 0,
-                                                               kCoherent));
-    }
-#pragma unroll
-    for (int j = 0; j < N; ++j)
-#pragma unroll
-        for (int k = 0; k < G; ++k) {
-            const int rr = (tid + k * C::THREADS) * 4 / D;
-            acc[k] += wts[rr * kMaxSplits + s0 + j] * v[j][k];
-        }
-}
 
 template <int D, int KS>
 struct Smem {
@@ -1144,124 +1116,158 @@ __global__ __launch_bounds__((Cfg<D, KS>::THREADS), (Cfg<D, KS>::WG_PER_CU)) voi
     // split-KV: publish this range's partial, the last arrival merges.
     // Partials travel through coherent 16-byte stores and loads (cache
     // policy sc1: they bypass the non-coherent part of the cache hierarchy
-    // for device scope), see dfp::publish.
-    const int row = wave * 32 + ql;
-    const int64_t slot = (int64_t)qtile_id * p.splits + split;
-    {
-        const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
-            p.part_o + slot * C::BLOCK_M * D, 0, C::BLOCK_M * D * 4, 0x00020000);
+    // for device scope), see dfp::publish.  The planner splits one-group
+    // launches only.
+    if constexpr (KS == 1) {
+        // Each wavefront restages its 32 rows through LDS, one 32-channel
+        // block at a time, so that a store covers eight rows' 128-byte runs
+        // instead of 32 rows' 32-byte pieces; a lane keeps what it stored
+        // (own[db][i]: row (lane + 64 i) / 8 of the wavefront, channels
+        // db*32 + ((lane + 64 i) % 8) * 4 + 0..3), and a merging lane loads
+        // the other splits' partials from the same addresses.
+        constexpr int LDW = 36;                      // staged row: 32 floats + 4 pad
+        float *wst = reinterpret_cast<float *>(&sm_all[0]) + wave * (32 * LDW);
+        float *wts = reinterpret_cast<float *>(&sm_all[0]) + C::NW * 32 * LDW;
+        static_assert((C::NW * 32 * LDW + C::BLOCK_M * kMaxSplits) * 4 <= (int)sizeof(Smem<D, KS>),
+                      "staging and row weights fit the ring");
+        const int row = wave * 32 + ql;
+        const int64_t slot = (int64_t)qtile_id * p.splits + split;
+        const int64_t base = (int64_t)qtile_id * p.splits;
+        __syncthreads();   // every wavefront is done with the ring
+        f32x4_t own[C::DB][4];
+        {
+            const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+                p.part_o + slot * C::BLOCK_M * D, 0, C::BLOCK_M * D * 4, 0x00020000);
+#pragma unroll
+            for (int db = 0; db < C::DB; ++db) {
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr)
+                    *reinterpret_cast<f32x4_t *>(wst + ql * LDW + rr * 8 + g * 4) =
+                        f32x4_t{st.oacc[db][rr * 4], st.oacc[db][rr * 4 + 1],
+                                st.oacc[db][rr * 4 + 2], st.oacc[db][rr * 4 + 3]};
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the block is staged
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int c = lane + 64 * i;
+                    own[db][i] = *reinterpret_cast<const f32x4_t *>(wst + (c >> 3) * LDW +
+                                                                     (c & 7) * 4);
+                }
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // read before reuse
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int c = lane + 64 * i;
+                    __builtin_amdgcn_raw_buffer_store_b128(
+                        __builtin_bit_cast(int32x4_t, own[db][i]), ro,
+                        ((wave * 32 + (c >> 3)) * D + db * 32 + (c & 7) * 4) * 4, 0, kCoherent);
+                }
+            }
+        }
+        if (g == 0) {
+            float *pml = p.part_ml + (slot * C::BLOCK_M + row) * 2;
+            dfp::publish(pml, st.m_run);
+            dfp::publish(pml + 1, l_tot);
+        }
+        dfp::published_wait();
+        __syncthreads();
+        if (tid == 0) s_last = (dfp::arrive(p.counters + qtile_id) == (unsigned)p.splits - 1);
+        __syncthreads();
+        if (!s_last) return;
+
+        // merge: O = sum_s w_s O_s with w_s = 2^(m_s - m*) / sum_s' 2^(m_s' - m*) l_s',
+        // in split order, every lane over the elements it holds; this split's
+        // partial comes from registers, the others' in batches of loads that
+        // are in flight together.  The arithmetic does not depend on which
+        // split arrives last.
+        constexpr int NB = MergeBatch<D>::N;
+        f32x4_t acc[C::DB][4];
 #pragma unroll
         for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                const f32x4_t v = {st.oacc[db][rr * 4], st.oacc[db][rr * 4 + 1],
-                                   st.oacc[db][rr * 4 + 2], st.oacc[db][rr * 4 + 3]};
-                __builtin_amdgcn_raw_buffer_store_b128(
-                    __builtin_bit_cast(int32x4_t, v), ro,
-                    (row * D + db * 32 + rr * 8 + g * 4) * 4, 0, kCoherent);
-            }
-    }
-    if (g == 0) {
-        float *pml = p.part_ml + (slot * C::BLOCK_M + row) * 2;
-        dfp::publish(pml, st.m_run);
-        dfp::publish(pml + 1, l_tot);
-    }
-    dfp::published_wait();
-    __syncthreads();
-    if (tid == 0) s_last = (dfp::arrive(p.counters + qtile_id) == (unsigned)p.splits - 1);
-    __syncthreads();
-    if (!s_last) return;
-
-    // merge: O = sum_s w_s O_s with w_s = 2^(m_s - m*) / sum_s' 2^(m_s' - m*) l_s',
-    // in split order.  Row weights into LDS (reusing the K ring); every
-    // thread streams its 16-byte groups, one batch of loads per split in
-    // flight together.
-    const int64_t base = (int64_t)qtile_id * p.splits;
-    constexpr int G = MergeCfg<D, KS>::G;
-    constexpr int NS = MergeCfg<D, KS>::NS;
-    const float *part0 = p.part_o + base * C::BLOCK_M * D;
-    // With at most NS splits every partial's loads go out before the row
-    // weights' loads, so the two round trips overlap (same arithmetic).
-    // d=64 only: at d=128 the registers are needed elsewhere.
-    const bool early = D == 64 && p.splits <= NS;
-    f32x4_t pre[NS][G];
-    if (early) {
+            for (int i = 0; i < 4; ++i) acc[db][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int s0 = 0; s0 < p.splits; s0 += NB) {
+            f32x4_t v[NB][C::DB][4];
 #pragma unroll
-        for (int j = 0; j < NS; ++j)
-            if (j < p.splits) {
-                const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
-                    const_cast<float *>(part0) + (int64_t)j * C::BLOCK_M * D, 0,
-                    C::BLOCK_M * D * 4, 0x00020000);
+            for (int j = 0; j < NB; ++j) {
+                const int sj = s0 + j;
+                if (sj < p.splits && sj != split) {
+                    const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+                        p.part_o + (base + sj) * C::BLOCK_M * D, 0, C::BLOCK_M * D * 4,
+                        0x00020000);
 #pragma unroll
-                for (int k = 0; k < G; ++k)
-                    pre[j][k] = __builtin_bit_cast(
-                        f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                                     ro, (tid + k * C::THREADS) * 16, 0, kCoherent));
-            }
-    }
-    float *wts = reinterpret_cast<float *>(sm.k[0]);   // [BLOCK_M][kMaxSplits]
-    static_assert(C::BLOCK_M * kMaxSplits * 4 <= C::K_TILE, "row weights fit one K stage");
-    if (tid < C::BLOCK_M) {
-        float ms[kMaxSplits], ls[kMaxSplits];
+                    for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-        for (int s = 0; s < kMaxSplits; ++s) {
-            if (s < p.splits) {
-                const float *ml = p.part_ml + ((base + s) * C::BLOCK_M + tid) * 2;
-                ms[s] = dfp::fetch_published(ml);
-                ls[s] = dfp::fetch_published(ml + 1);
-            }
-        }
-        float mstar = -INFINITY;
-#pragma unroll
-        for (int s = 0; s < kMaxSplits; ++s)
-            if (s < p.splits) mstar = fmaxf(mstar, ms[s]);
-        float den = 0.f;
-#pragma unroll
-        for (int s = 0; s < kMaxSplits; ++s)
-            if (s < p.splits) {
-                ms[s] = __builtin_amdgcn_exp2f(ms[s] - mstar);
-                den = fmaf(ms[s], ls[s], den);
-            }
-        const float inv = 1.0f / den;
-#pragma unroll
-        for (int s = 0; s < kMaxSplits; ++s)
-            if (s < p.splits) wts[tid * kMaxSplits + s] = ms[s] * inv;
-    }
-    __syncthreads();
-    f32x4_t acc[G];
-#pragma unroll
-    for (int k = 0; k < G; ++k) acc[k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    if (early) {
-#pragma unroll
-        for (int j = 0; j < NS; ++j)
-            if (j < p.splits)
-#pragma unroll
-                for (int k = 0; k < G; ++k) {
-                    const int rr = (tid + k * C::THREADS) * 4 / D;
-                    acc[k] += wts[rr * kMaxSplits + j] * pre[j][k];
+                        for (int i = 0; i < 4; ++i) {
+                            const int c = lane + 64 * i;
+                            v[j][db][i] = __builtin_bit_cast(
+                                f32x4_t,
+                                __builtin_amdgcn_raw_buffer_load_b128(
+                                    ro, ((wave * 32 + (c >> 3)) * D + db * 32 + (c & 7) * 4) * 4,
+                                    0, kCoherent));
+                        }
                 }
-    }
-    for (int s0 = early ? p.splits : 0; s0 < p.splits; s0 += NS) {
-        switch (min(NS, p.splits - s0)) {
-            case 1: merge_pass<D, KS, 1>(acc, part0, wts, s0, tid); break;
-            case 2: merge_pass<D, KS, (NS >= 2 ? 2 : 1)>(acc, part0, wts, s0, tid); break;
-            case 3: merge_pass<D, KS, (NS >= 3 ? 3 : 1)>(acc, part0, wts, s0, tid); break;
-            default: merge_pass<D, KS, NS>(acc, part0, wts, s0, tid); break;
-        }
-    }
+            }
+            if (s0 == 0) {   // row weights into LDS while the first batch is in flight
+                if (tid < C::BLOCK_M) {
+                    float ms[kMaxSplits], ls[kMaxSplits];
 #pragma unroll
-    for (int k = 0; k < G; ++k) {
-        const int e = tid + k * C::THREADS;
-        const int rr = e * 4 / D, d0 = e * 4 % D;
-        const int qr = qt * C::BLOCK_M + rr;
-        if (qr >= n_q) continue;
-        __bf16 vals[4] = {(__bf16)acc[k][0], (__bf16)acc[k][1], (__bf16)acc[k][2],
-                          (__bf16)acc[k][3]};
-        uint2 pk;
-        __builtin_memcpy(&pk, vals, 8);
-        *reinterpret_cast<uint2 *>(p.O + ((int64_t)bh * n_q + qr) * D + d0) = pk;
+                    for (int s = 0; s < kMaxSplits; ++s)
+                        if (s < p.splits) {
+                            const float *ml = p.part_ml + ((base + s) * C::BLOCK_M + tid) * 2;
+                            ms[s] = dfp::fetch_published(ml);
+                            ls[s] = dfp::fetch_published(ml + 1);
+                        }
+                    float mstar = -INFINITY;
+#pragma unroll
+                    for (int s = 0; s < kMaxSplits; ++s)
+                        if (s < p.splits) mstar = fmaxf(mstar, ms[s]);
+                    float den = 0.f;
+#pragma unroll
+                    for (int s = 0; s < kMaxSplits; ++s)
+                        if (s < p.splits) {
+                            ms[s] = __builtin_amdgcn_exp2f(ms[s] - mstar);
+                            den = fmaf(ms[s], ls[s], den);
+                        }
+                    const float inv = 1.0f / den;
+#pragma unroll
+                    for (int s = 0; s < kMaxSplits; ++s)
+                        if (s < p.splits) wts[tid * kMaxSplits + s] = ms[s] * inv;
+                }
+                __syncthreads();
+            }
+#pragma unroll
+            for (int j = 0; j < NB; ++j) {
+                const int sj = s0 + j;
+                if (sj >= p.splits) continue;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float w = wts[(wave * 32 + ((lane + 64 * i) >> 3)) * kMaxSplits + sj];
+#pragma unroll
+                    for (int db = 0; db < C::DB; ++db) {
+                        const f32x4_t o_s = sj == split ? own[db][i] : v[j][db][i];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) acc[db][i][e] = fmaf(w, o_s[e], acc[db][i][e]);
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int c = lane + 64 * i;
+            const int qr = qt * C::BLOCK_M + wave * 32 + (c >> 3);
+            if (qr >= n_q) continue;
+            uint16_t *orow = p.O + ((int64_t)bh * n_q + qr) * D + (c & 7) * 4;
+#pragma unroll
+            for (int db = 0; db < C::DB; ++db) {
+                __bf16 vals[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) vals[e] = (__bf16)acc[db][i][e];
+                uint2 pk;
+                __builtin_memcpy(&pk, vals, 8);
+                *reinterpret_cast<uint2 *>(orow + db * 32) = pk;
+            }
+        }
+        if (tid == 0) dfp::publish(p.counters + qtile_id, 0u);
     }
-    if (tid == 0) dfp::publish(p.counters + qtile_id, 0u);
 }
 
 // ---------------------------------------------------------------- planning
@@ -1298,7 +1304,7 @@ Plan make_plan(int BH, int n_q, int N_kv, int d, bool can_split) {
     // publish, arrive and row weights, then one memory round trip per batch
     // of partials the merge loads together (measured: 3 splits ~3.5 us,
     // 8 splits ~6.5 us at d=64)
-    const int merge_batch = d == 64 ? MergeCfg<64, 1>::NS : MergeCfg<128, 1>::NS;
+    const int merge_batch = d == 64 ? MergeBatch<64>::N : MergeBatch<128>::N;
     const double merge_bw = 5e12;                        // partial bytes/s, written and read
     const double base = (double)BH * pl.q_tiles;
     double best = 1e300;
