@@ -16,7 +16,8 @@
 // The group's C/G channels of the patch are one contiguous run of C/G * n
 // floats.  Runs of up to 64 Ki floats (n % 4 == 0, x and y 16-byte aligned):
 // one workgroup per (image, group) keeps its run in registers between the
-// two uses, so x is read once.  Longer runs, given a workspace: every run is
+// two uses, so x is read once, and stages the group's gamma and beta in LDS
+// alongside, so nothing but the statistics stands between the two.  Longer runs, given a workspace: every run is
 // cut into chunks of 4 Ki floats spread over the whole GPU, in two launches
 // -- launch 1 stores each chunk's fp64 sums; launch 2 has every chunk add its
 // group's chunk sums in chunk order (the same order in every chunk, so all
@@ -137,14 +138,42 @@ __device__ __forceinline__ void accum4(double &s1, double &s2, float4 v) {
     s2 = fma((double)v.w, (double)v.w, s2);
 }
 
+__device__ __forceinline__ float4 affine4(float4 v, float mean, float sc, float be) {
+    return make_float4((v.x - mean) * sc + be, (v.y - mean) * sc + be, (v.z - mean) * sc + be,
+                       (v.w - mean) * sc + be);
+}
+
 template <bool AFFINE>
 __device__ __forceinline__ float4 normalize4(const GnArgs &a, float4 v, int c, float2 mr) {
     const float ga = AFFINE && a.gamma ? a.gamma[c] : 1.f;
     const float be = AFFINE && a.beta ? a.beta[c] : 0.f;
-    const float sc = mr.y * ga;
-    return make_float4((v.x - mr.x) * sc + be, (v.y - mr.x) * sc + be, (v.z - mr.x) * sc + be,
-                       (v.w - mr.x) * sc + be);
+    return affine4(v, mr.x, mr.y * ga, be);
 }
+
+// gamma and beta of a group's channels [c0, c0 + cnt) staged in LDS by the
+// register-resident path: the first cnt threads load them before the x
+// loads (so they share that round trip), store them after, and the
+// statistics' barrier publishes them; the normalization then reads no
+// memory after the statistics.  Groups of more channels read them from
+// memory.
+constexpr int kGbLds = 256;
+struct GammaBeta {
+    float ga = 1.f, be = 0.f;
+    template <bool AFFINE>
+    __device__ __forceinline__ void load(const GnArgs &a, int c0, int cnt) {
+        if (AFFINE && cnt <= kGbLds && (int)threadIdx.x < cnt) {
+            if (a.gamma) ga = a.gamma[c0 + threadIdx.x];
+            if (a.beta) be = a.beta[c0 + threadIdx.x];
+        }
+    }
+    template <bool AFFINE>
+    __device__ __forceinline__ void stage(float *s_ga, float *s_be, int cnt) const {
+        if (AFFINE && cnt <= kGbLds && (int)threadIdx.x < cnt) {
+            s_ga[threadIdx.x] = ga;
+            s_be[threadIdx.x] = be;
+        }
+    }
+};
 
 // The group's run in registers: n % 4 == 0 (a float4 never crosses a
 // channel), x and y 16-byte aligned, C/G * n <= kGnResidentFloats.
@@ -156,12 +185,17 @@ __global__ __launch_bounds__(kGnThreads) void gn_resident_kernel(GnArgs a) {
     const int len4 = cg * n4;
     const int64_t off = ((int64_t)b * a.C + (int64_t)g * cg) * a.n;
     const float4 *xg = reinterpret_cast<const float4 *>(a.x + off);
+    __shared__ float s_ga[kGbLds], s_be[kGbLds];
+    const bool gb_lds = AFFINE && cg <= kGbLds;
+    GammaBeta gb;
+    gb.load<AFFINE>(a, g * cg, cg);
     float4 v[kGnVec];
 #pragma unroll
     for (int k = 0; k < kGnVec; ++k) {
         const int i = tid + k * kGnThreads;
         v[k] = i < len4 ? xg[i] : make_float4(0.f, 0.f, 0.f, 0.f);
     }
+    gb.stage<AFFINE>(s_ga, s_be, cg);
     double s1 = 0.0, s2 = 0.0;
 #pragma unroll
     for (int k = 0; k < kGnVec; ++k) accum4(s1, s2, v[k]);
@@ -170,7 +204,13 @@ __global__ __launch_bounds__(kGnThreads) void gn_resident_kernel(GnArgs a) {
 #pragma unroll
     for (int k = 0; k < kGnVec; ++k) {
         const int i = tid + k * kGnThreads;
-        if (i < len4) yg[i] = normalize4<AFFINE>(a, v[k], g * cg + i / n4, mr);
+        if (i >= len4) continue;
+        if (gb_lds) {
+            const int lc = i / n4;
+            yg[i] = affine4(v[k], mr.x, mr.y * s_ga[lc], s_be[lc]);
+        } else {
+            yg[i] = normalize4<AFFINE>(a, v[k], g * cg + i / n4, mr);
+        }
     }
 }
 

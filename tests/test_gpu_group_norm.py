@@ -67,6 +67,8 @@ def _run(B, C, G_, n, P, p, seed, affine=True, in_place=False, land=True, offset
     (3, 12, 3, 1001, 5, 4),       # n not a multiple of 4: scalar path
     (3, 12, 3, 30001, 5, 4),      # ... with groups of 117 Ki floats
     (1, 8, 8, 4, 1, 0),           # one channel per group, one patch
+    (1, 512, 1, 64, 2, 0),        # in registers, 512 channels: gamma/beta read from memory
+    (1, 32768, 1, 4, 1, 0),       # chunks spanning 1024 channels each
 ])
 @pytest.mark.parametrize("ws", [True, False])
 def test_every_element(B, C, G_, n, P, p, ws):
