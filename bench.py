@@ -265,6 +265,19 @@ def attn_reps(flops: float, reps: int) -> int:
     return max(3, min(reps, int(0.05 / max(per, 1e-9))))
 
 
+def attention_bytes(level, landing: bool) -> float:
+    """Algorithmic HBM bytes of one patch's attention launch (bf16): Q read
+    and O written once, every K and V row read once (the patch's own rows
+    from this step's tensors), and, when the launch lands the fresh rows
+    (the patch's and a DiT's text rows), their write into the buffer."""
+    e = 2
+    bytes_ = 2 * level.B * level.H * level.n * level.d * e          # Q, O
+    bytes_ += 2 * level.B * level.H * level.N_kv * level.d * e      # K, V
+    if landing:
+        bytes_ += 2 * level.B * level.H * (level.n + level.n_text) * level.d * e
+    return float(bytes_)
+
+
 def time_levels(levels, sampler, dfp, torch, reps):
     kern = {}
     for L in levels:
@@ -272,9 +285,16 @@ def time_levels(levels, sampler, dfp, torch, reps):
         fn = (lambda L=L: L.attend_fresh(dfp)) if L.fused else (lambda L=L: L.attend(dfp))
         mean, mn = time_kernel(torch, fn, attn_reps(L.level.flops(), reps))
         tf = L.level.flops() / (mean * 1e-6) / 1e12
+        # roofline of this launch: min(dense bf16 peak, arithmetic intensity x HBM)
+        nbytes = attention_bytes(L.level, L.fused)
+        ai = L.level.flops() / nbytes
+        attain = min(PEAK_BF16_TFLOPS, ai * PEAK_HBM_GBPS / 1e3)
         kern[f"attn_{L.level.name}"] = {
             "us_mean": mean, "us_min": mn, "tflops": tf,
             "frac_bf16_peak": tf / PEAK_BF16_TFLOPS, "flop": L.level.flops(),
+            "algorithmic_bytes": nbytes, "flop_per_byte": ai,
+            "bound": "mfma" if attain >= PEAK_BF16_TFLOPS else "hbm",
+            "attainable_tflops": attain, "frac_attainable": tf / attain,
             "kernel": L.kernel_name(),
             "plan": {"key_groups": L.plan[0], "splits": L.plan[1], "workgroups": L.plan[2]},
             "launch": "dfp_patch_attention_fresh (attention + landing of the fresh K/V)"
