@@ -32,6 +32,7 @@ import argparse
 import hashlib
 import json
 import os
+import subprocess
 import sys
 import time
 
@@ -319,6 +320,62 @@ def time_levels(levels, sampler, dfp, torch, reps):
     return kern
 
 
+def time_sampler_graph(sampler, dfp, torch, replays=5):
+    """The whole sampler trajectory -- every step's fused CFG step (both
+    launches), in order -- captured as one HIP graph and replayed: per-step
+    time with launch gaps as small as the runtime makes them, to set beside
+    the per-launch figure.  x drifts over the replays; only time is read."""
+    S = sampler.wl.steps
+    try:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for i in range(S):
+                sampler.step(dfp, i)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(S):
+                sampler.step(dfp, i)
+        g.replay()
+        torch.cuda.synchronize()
+    except Exception as e:  # capture refused: report nothing
+        print(f"[bench] sampler graph unavailable ({e})", file=sys.stderr)
+        return None
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(replays):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / replays
+    del g
+    return {"steps": S, "us_per_trajectory": us, "us_per_step": us / S,
+            "gbps": sampler.bytes / (us / S * 1e-6) / 1e9,
+            "launch": "one HIP graph of the whole trajectory"}
+
+
+def rocminfo_max_clock_ghz():
+    """The gfx950 agent's maximum engine clock as rocminfo reports it, or None."""
+    try:
+        out = subprocess.run(["rocminfo"], capture_output=True, text=True, timeout=60).stdout
+    except (OSError, subprocess.SubprocessError):
+        return None
+    found = False
+    for line in out.splitlines():
+        t = line.strip()
+        if t.startswith("Name:") and "gfx950" in t:
+            found = True
+        elif found and t.startswith("Max Clock Freq. (MHz):"):
+            try:
+                return float(t.split(":", 1)[1]) / 1e3
+            except ValueError:
+                return None
+    return None
+
+
 def time_group_norm(wl, dfp, torch, inputs, reps):
     """Displaced GroupNorm (the corrected_async_gn mode) on the workload's
     first U-Net level: 320 channels in 32 groups over the latent grid, one
@@ -486,6 +543,7 @@ def main():
 
     # ---- per-kernel durations (HIP events on the launch stream)
     kern = time_levels(levels, sampler, dfp, torch, args.kernel_reps)
+    kern["cfg_step"]["trajectory_graph"] = time_sampler_graph(sampler, dfp, torch)
     gn = time_group_norm(wl, dfp, torch, inputs, max(args.kernel_reps, 50))
     if gn:
         kern["displaced_group_norm"] = gn
@@ -506,6 +564,7 @@ def main():
         pc = PEAK_BF16_TFLOPS * clock / PEAK_CLOCK_GHZ
         roofline.update({"clock_ghz_measured": clock, "peak_at_measured_clock": pc,
                          "frac_at_measured_clock": dk["tflops"] / pc})
+    roofline["clock_ghz_rocminfo_max"] = rocminfo_max_clock_ghz()
     ck = kern["cfg_step"]
     cfg_src = "patch_attention_cfg_amd/csrc/cfg_step.hip"
     cfg_prof = os.path.join(prof, f"cfg_step_{wl.name}_hbm_traffic.txt")
@@ -533,6 +592,7 @@ def main():
                 L.run(dfp)
             csm.step(dfp, 0)
         ckern = time_levels(clv, csm, dfp, torch, args.kernel_reps)
+        ckern["cfg_step"]["trajectory_graph"] = time_sampler_graph(csm, dfp, torch)
         cgn = time_group_norm(cw, dfp, torch, inputs, max(args.kernel_reps, 50))
         if cgn:
             ckern["displaced_group_norm"] = cgn
