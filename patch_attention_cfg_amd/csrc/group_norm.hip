@@ -69,6 +69,7 @@ struct GnArgs {
     int64_t n;
     float eps;
     int land;
+    int reverse;     // chunked path: launch 2 walks the chunks last first
 };
 
 // Sum of every thread's pair across a workgroup of WAVES wavefronts, in
@@ -276,7 +277,21 @@ __global__ __launch_bounds__(kGcThreads) void gn_chunk_sums_kernel(GnArgs a, dou
 template <bool VEC, bool AFFINE>
 __global__ __launch_bounds__(kGcThreads) void gn_chunk_norm_kernel(GnArgs a,
                                                                    const double *partials) {
-    const int chunk = blockIdx.x, nch = gridDim.x, g = blockIdx.y, b = blockIdx.z;
+    // With `reverse` the chunks go last first, each on the XCD that read it
+    // in launch 1 (workgroup i runs on XCD i % 8, and the permutation keeps
+    // i % 8): the chunks launch 1 read last are the ones its L2s still
+    // hold.  Any order gives the same results.
+    const int nch = gridDim.x;
+    int chunk = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    if (a.reverse) {   // set only for grids of fewer than 2^31 workgroups
+        const uint32_t wg = blockIdx.x + (uint32_t)nch * (blockIdx.y + gridDim.y * blockIdx.z);
+        const uint32_t all = (uint32_t)nch * gridDim.y * gridDim.z;
+        const uint32_t lin = (all / 8 - 1 - wg / 8) * 8 + wg % 8;
+        const uint32_t rest = lin / (uint32_t)nch;
+        chunk = (int)(lin - rest * (uint32_t)nch);
+        g = (int)(rest % gridDim.y);
+        b = (int)(rest / gridDim.y);
+    }
     const int tid = threadIdx.x;
     const int cg = a.C / a.G;
     const int64_t run = (int64_t)cg * a.n;
@@ -358,7 +373,7 @@ extern "C" dfp_status dfp_displaced_group_norm(float *y, const float *x, double 
     if (y != x && (const float *)y < x + total && x < (const float *)y + total)
         return DFP_ERR_INVALID_ARG;
     const bool affine = gamma || beta;
-    GnArgs a{y, x, stats, gamma, beta, C, G, P, p, n, eps, land ? 1 : 0};
+    GnArgs a{y, x, stats, gamma, beta, C, G, P, p, n, eps, land ? 1 : 0, 0};
     const int64_t run = (int64_t)(C / G) * n;
     const bool resident = n % 4 == 0 && run <= kGnResidentFloats && aligned(x, 16) &&
                           aligned(y, 16);
@@ -373,6 +388,11 @@ extern "C" dfp_status dfp_displaced_group_norm(float *y, const float *x, double 
         double *partials = static_cast<double *>(workspace);
         const bool vec = n % 4 == 0 && aligned(x, 16) && aligned(y, 16);
         const dim3 cgrid((unsigned)chunks, (unsigned)G, (unsigned)B), cblock(kGcThreads);
+        // x larger than the eight XCDs' L2s together (8 x 4 MiB): launch 2
+        // starts from the chunks they still hold.  A smaller x stays in
+        // them whole, and the original order measured faster there.
+        a.reverse = total * 4 > (int64_t(32) << 20) && (chunks * groups) % 8 == 0 &&
+                    chunks * groups < (int64_t(1) << 31);
         if (vec)
             hipLaunchKernelGGL(gn_chunk_sums_kernel<true>, cgrid, cblock, 0, stream, a, partials);
         else

@@ -69,6 +69,7 @@ def _run(B, C, G_, n, P, p, seed, affine=True, in_place=False, land=True, offset
     (1, 8, 8, 4, 1, 0),           # one channel per group, one patch
     (1, 512, 1, 64, 2, 0),        # in registers, 512 channels: gamma/beta read from memory
     (1, 32768, 1, 4, 1, 0),       # chunks spanning 1024 channels each
+    (1, 16, 1, 600001, 2, 1),     # x over 32 MiB, n odd: scalar chunks, launch 2 last chunk first
 ])
 @pytest.mark.parametrize("ws", [True, False])
 def test_every_element(B, C, G_, n, P, p, ws):
