@@ -279,8 +279,8 @@ __global__ __launch_bounds__(kGcThreads) void gn_chunk_norm_kernel(GnArgs a,
                                                                    const double *partials) {
     // With `reverse` the chunks go last first, each on the XCD that read it
     // in launch 1 (workgroup i runs on XCD i % 8, and the permutation keeps
-    // i % 8): the chunks launch 1 read last are the ones its L2s still
-    // hold.  Any order gives the same results.
+    // i % 8), so the most recently read chunks come first.  Any order gives
+    // the same results.
     const int nch = gridDim.x;
     int chunk = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
     if (a.reverse) {   // set only for grids of fewer than 2^31 workgroups
@@ -389,8 +389,9 @@ extern "C" dfp_status dfp_displaced_group_norm(float *y, const float *x, double 
         const bool vec = n % 4 == 0 && aligned(x, 16) && aligned(y, 16);
         const dim3 cgrid((unsigned)chunks, (unsigned)G, (unsigned)B), cblock(kGcThreads);
         // x larger than the eight XCDs' L2s together (8 x 4 MiB): launch 2
-        // starts from the chunks they still hold.  A smaller x stays in
-        // them whole, and the original order measured faster there.
+        // starts from the chunks launch 1 read last, measured faster there
+        // (the L2 miss counts stay the same: the misses are served faster).
+        // For a smaller x the original order measured faster.
         a.reverse = total * 4 > (int64_t(32) << 20) && (chunks * groups) % 8 == 0 &&
                     chunks * groups < (int64_t(1) << 31);
         if (vec)
