@@ -368,8 +368,8 @@ dfp_status dfp_relmae(const float *g_c, const float *g_u, int64_t n_per_image,
  *           dfp_group_norm_workspace_bytes(B, C, G, n) bytes, are cut into
  *           chunks of 4 Ki floats spread over the whole GPU in two launches
  *           (chunk sums, then statistics and normalization; x is read
- *           twice, the second time mostly from cache); without it one
- *           workgroup per (image, group) streams x twice.  Calls that share
+ *           twice); without it one workgroup per (image, group) streams x
+ *           twice.  Calls that share
  *           a workspace must not run concurrently.
  * The statistics are bitwise reproducible (fixed-order fp64 sums).
  * Errors: INVALID_ARG for null y/x/stats, non-positive B/C/G/n/P, C not a
