@@ -17,13 +17,13 @@
 // floats.  Runs of up to 64 Ki floats (n % 4 == 0, x and y 16-byte aligned):
 // one workgroup per (image, group) keeps its run in registers between the
 // two uses, so x is read once, and stages the group's gamma and beta in LDS
-// alongside, so nothing but the statistics stands between the two.  Longer runs, given a workspace: every run is
-// cut into chunks of 4 Ki floats spread over the whole GPU, in two launches
-// -- launch 1 stores each chunk's fp64 sums; launch 2 has every chunk add its
-// group's chunk sums in chunk order (the same order in every chunk, so all
-// agree bit for bit), form the statistics, normalize its floats (which
-// launch 1 just read, so they mostly come back from cache), and the group's
-// first chunk lands the fresh sums.  No atomics and no counters: the launch
+// alongside, so nothing but the statistics stands between the two.  Longer
+// runs, given a workspace: every run is cut into chunks of 4 Ki floats
+// spread over the whole GPU, in two launches -- launch 1 stores each chunk's
+// fp64 sums; launch 2 has every chunk add its group's chunk sums in chunk
+// order (the same order in every chunk, so all agree bit for bit), form the
+// statistics, read and normalize its floats again, and the group's first
+// chunk lands the fresh sums.  No atomics and no counters: the launch
 // boundary orders the two.  Otherwise one workgroup streams each run twice.
 // Sums are fp64 per thread, per wavefront (fixed butterfly) and across
 // wavefronts and chunks in a fixed order, so the statistics are bitwise
