@@ -64,6 +64,29 @@ def build_library(verbose: bool = False) -> str:
     return LIB
 
 
+C_CALLER_SRC = os.path.join(ROOT, "tests", "c", "step_from_c.c")
+C_CALLER = os.path.join(ROOT, "tests", "c", "step_from_c")
+
+
+def build_c_caller(verbose: bool = False) -> str:
+    """The plain-C caller the tests run (host code only: gcc, the HIP runtime
+    and libdfp.so)."""
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    tmp = C_CALLER + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-std=c11", "-O2", "-Wall", "-Werror", "-D__HIP_PLATFORM_AMD__",
+           "-I", INCLUDE, "-I", os.path.join(rocm, "include"), C_CALLER_SRC, "-o", tmp,
+           "-L", PKG, "-l:libdfp.so", "-Wl,-rpath,$ORIGIN/../../patch_attention_cfg_amd",
+           "-L", os.path.join(rocm, "lib"), "-lamdhip64", "-Wl,-rpath," + os.path.join(rocm, "lib")]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"gcc failed for {C_CALLER_SRC}:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, C_CALLER)
+    if verbose:
+        print("built", C_CALLER)
+    return C_CALLER
+
+
 if __name__ == "__main__":
     build_library(verbose=True)
+    build_c_caller(verbose=True)
     sys.exit(0)
