@@ -76,7 +76,8 @@ def build_c_caller(verbose: bool = False) -> str:
     cmd = ["gcc", "-std=c11", "-O2", "-Wall", "-Werror", "-D__HIP_PLATFORM_AMD__",
            "-I", INCLUDE, "-I", os.path.join(rocm, "include"), C_CALLER_SRC, "-o", tmp,
            "-L", PKG, "-l:libdfp.so", "-Wl,-rpath,$ORIGIN/../../patch_attention_cfg_amd",
-           "-L", os.path.join(rocm, "lib"), "-lamdhip64", "-Wl,-rpath," + os.path.join(rocm, "lib")]
+           "-L", os.path.join(rocm, "lib"), "-lamdhip64", "-Wl,-rpath," + os.path.join(rocm, "lib"),
+           "-lm"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"gcc failed for {C_CALLER_SRC}:\n{r.stdout}\n{r.stderr}")
