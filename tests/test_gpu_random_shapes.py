@@ -3,8 +3,9 @@ head size 64/128, one or two key groups, split key ranges, zero to two
 fresh ranges with and without landing, ragged queries and keys.  Every
 element against the oracle over the effective K/V (bf16 bars), the fused
 call bitwise equal to scatter + attention, the landed buffer exact, and the
-workspace counters back at zero.  The draws are fixed by the seed, so the
-cases are the same on every run."""
+workspace counters back at zero.  A second set forces every split count
+from 2 to 8 at both head sizes over key ranges up to 5000 rows.  The draws
+are fixed by the seed, so the cases are the same on every run."""
 import numpy as np
 import pytest
 
@@ -24,24 +25,52 @@ def _case(i):
     B, H = int(rng.integers(1, 3)), int(rng.integers(1, 4))
     n_q = int(rng.integers(1, 400))
     N = int(rng.integers(64, 2200))
-    ntiles_whole = N // 64
-    ranges = []
-    for _ in range(int(rng.integers(0, 3))):   # fresh ranges of whole tiles, disjoint
-        if ntiles_whole < 1:
-            break
-        t0 = int(rng.integers(0, ntiles_whole))
-        nt = int(rng.integers(1, min(8, ntiles_whole - t0) + 1))
-        if all(t0 + nt <= a // 64 or t0 >= (a + n) // 64 for a, n in ranges):
-            ranges.append((t0 * 64, nt * 64))
+    ranges = _fresh_ranges(rng, N)
     ks = str(rng.choice(["auto", "1", "2"])) if d == 64 else "auto"
     splits = int(rng.choice([0, 0, 2, 3, 5]))
     land = bool(rng.integers(0, 2))
     return B, H, n_q, N, d, ranges, ks, splits, land
 
 
+def _fresh_ranges(rng, N):
+    """Zero to two disjoint fresh ranges of whole 64-row tiles."""
+    ntiles_whole = N // 64
+    ranges = []
+    for _ in range(int(rng.integers(0, 3))):
+        if ntiles_whole < 1:
+            break
+        t0 = int(rng.integers(0, ntiles_whole))
+        nt = int(rng.integers(1, min(8, ntiles_whole - t0) + 1))
+        if all(t0 + nt <= a // 64 or t0 >= (a + n) // 64 for a, n in ranges):
+            ranges.append((t0 * 64, nt * 64))
+    return ranges
+
+
+def _split_case(i):
+    """Every split count from 2 to 8 at both head sizes, longer key ranges."""
+    rng = np.random.Generator(np.random.PCG64(31000 + i))
+    d = int(rng.choice([64, 128]))
+    B, H = int(rng.integers(1, 3)), int(rng.integers(1, 3))
+    n_q = int(rng.integers(1, 700))
+    N = int(rng.integers(64, 5000))
+    ranges = _fresh_ranges(rng, N)
+    splits = int(rng.integers(2, 9))
+    land = bool(rng.integers(0, 2))
+    return B, H, n_q, N, d, ranges, "auto", splits, land
+
+
 @pytest.mark.parametrize("i", range(64))
 def test_random_shape(monkeypatch, i):
-    B, H, n_q, N, d, ranges, ks, splits, land = _case(i)
+    _run_case(monkeypatch, i, _case(i))
+
+
+@pytest.mark.parametrize("i", range(96))
+def test_random_split(monkeypatch, i):
+    _run_case(monkeypatch, i, _split_case(i))
+
+
+def _run_case(monkeypatch, i, case):
+    B, H, n_q, N, d, ranges, ks, splits, land = case
     G.require_gpu()
     G.announce(f"random attention case {i}: B{B} H{H} nq{n_q} N{N} d{d} ranges={ranges} "
                f"ks={ks} splits={splits} land={land}")
