@@ -70,6 +70,9 @@ def _run(B, C, G_, n, P, p, seed, affine=True, in_place=False, land=True, offset
     (1, 512, 1, 64, 2, 0),        # in registers, 512 channels: gamma/beta read from memory
     (1, 32768, 1, 4, 1, 0),       # chunks spanning 1024 channels each
     (1, 16, 1, 600001, 2, 1),     # x over 32 MiB, n odd: scalar chunks, launch 2 last chunk first
+    (2, 64, 8, 256, 64, 63),      # 64 patches: every stale sum staged in LDS
+    (2, 64, 8, 256, 65, 0),       # 65 patches: stale sums read after the reduction
+    (1, 64, 2, 4096, 100, 57),    # chunked, 100 patches
 ])
 @pytest.mark.parametrize("ws", [True, False])
 def test_every_element(B, C, G_, n, P, p, ws):
