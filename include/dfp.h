@@ -369,8 +369,8 @@ dfp_status dfp_relmae(const float *g_c, const float *g_u, int64_t n_per_image,
  *           chunks of 4 Ki floats spread over the whole GPU in two launches
  *           (chunk sums, then statistics and normalization; x is read
  *           twice); without it one workgroup per (image, group) streams x
- *           twice.  Calls that share
- *           a workspace must not run concurrently.
+ *           twice.  Calls that share a workspace must not run
+ *           concurrently.
  * The statistics are bitwise reproducible (fixed-order fp64 sums).
  * Errors: INVALID_ARG for null y/x/stats, non-positive B/C/G/n/P, C not a
  * multiple of G, p outside [0, P), negative or non-finite eps, misaligned
