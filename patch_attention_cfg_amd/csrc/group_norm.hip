@@ -221,9 +221,12 @@ __global__ __launch_bounds__(kGnThreads) void gn_resident_kernel(GnArgs a) {
         v[k] = i < len4 ? xg[i] : make_float4(0.f, 0.f, 0.f, 0.f);
     }
     gb.stage<AFFINE>(s_ga, s_be, cg);
+    // only the slots that hold the run: the fp64 sums are the costly part of
+    // this kernel, and adding the padding's zeros would not change them
     double s1 = 0.0, s2 = 0.0;
 #pragma unroll
-    for (int k = 0; k < kGnVec; ++k) accum4(s1, s2, v[k]);
+    for (int k = 0; k < kGnVec; ++k)
+        if (tid + k * kGnThreads < len4) accum4(s1, s2, v[k]);
     const float2 mr = group_stats(a, b, g, s1, s2, nullptr);
     float4 *yg = reinterpret_cast<float4 *>(a.y + off);
 #pragma unroll
