@@ -116,6 +116,37 @@ def test_attention_validation(L, args, expect):
     assert L.dfp_patch_attention(*args, NULL, 0, S0) == expect
 
 
+# Sizes past the 32-bit offsets and grid sizes the kernels use are refused
+# before anything is enqueued (so these run without a GPU).
+@pytest.mark.parametrize("dt", [dfp.BF16, dfp.F32])
+@pytest.mark.parametrize("B,H,n_q,N_kv,d,bf16_only", [
+    (1, 1, 64, 1 << 24, 64, True),          # one head's K is 2 GiB of bf16
+    (1, 1, 64, 1 << 23, 128, True),
+    (1 << 16, 1 << 15, 64, 64, 64, False),  # 2^31 (batch, head) pairs
+    (1 << 15, 1 << 15, 256, 64, 64, False),  # 2^31 workgroups
+])
+def test_attention_refuses_sizes_past_its_limits(L, dt, B, H, n_q, N_kv, d, bf16_only):
+    if bf16_only and dt != dfp.BF16:
+        pytest.skip("the fp32 path addresses K and V with 64-bit offsets")
+    assert L.dfp_patch_attention(FAKE, FAKE, FAKE, FAKE, B, H, n_q, N_kv, d, 0.125, dt,
+                                 NULL, 0, S0) == dfp.ERR_UNSUPPORTED
+
+
+def test_fresh_attention_refuses_sizes_past_its_limits(L):
+    big = dfp.FreshRows(FAKE, FAKE, 0, 64)
+    arr = (dfp.FreshRows * 1)(big)
+    assert L.dfp_patch_attention_fresh(FAKE, FAKE, FAKE, FAKE, arr, 1, 1, 1, 64, 1 << 24, 64, 1,
+                                       0.125, dfp.BF16, NULL, 0, S0) == dfp.ERR_UNSUPPORTED
+    assert L.dfp_patch_attention_fresh(FAKE, FAKE, FAKE, FAKE, arr, 1, 1 << 16, 1 << 15, 64, 64,
+                                       64, 1, 0.125, dfp.BF16, NULL, 0, S0) == dfp.ERR_UNSUPPORTED
+
+
+def test_scatter_refuses_grids_past_its_limits(L):
+    # 2^30 (batch, head) pairs of two 64-row V^T tiles: 2^31 workgroups
+    assert L.dfp_kv_scatter(FAKE, FAKE, FAKE, FAKE, 1 << 15, 1 << 15, 128, 64, 0, 128, dfp.BF16,
+                            S0) == dfp.ERR_UNSUPPORTED
+
+
 MIS = ctypes.c_void_p(0x100008)   # 8-byte aligned only
 
 
